@@ -1,0 +1,475 @@
+"""Pins of the float64 oracle to things other than itself.
+
+Each test ties an oracle function to a value the pages print (fixtures under
+tests/golden/, each citing its passage), a closed form, an invariant the pages
+state, a library routine (torch SDPA, torch's fp8/bf16 conversions, logsumexp)
+or brute force on tiny inputs.  CPU only.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# --------------------------------------------------------------------------- layer split
+
+
+def test_layer_split_worked_example():
+    rows = _rows("layer_split_78_over_8.txt")
+    assert len(rows) == 8
+    for r, a, b in rows:
+        assert O.layer_range(78, 8, int(r)) == (int(a), int(b))
+    # section 6.5: first 6 ranks 10 layers, last 2 get 9
+    sizes = [b - a for a, b in (O.layer_range(78, 8, r) for r in range(8))]
+    assert sizes == [10] * 6 + [9] * 2
+
+
+@pytest.mark.parametrize("L", [1, 4, 7, 64, 78, 100])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 12])
+def test_layer_split_partition(L, n):
+    if n > L:
+        return
+    ranges = [O.layer_range(L, n, r) for r in range(n)]
+    # contiguous cover of [0, L)
+    assert ranges[0][0] == 0 and ranges[-1][1] == L
+    for (a0, b0), (a1, b1) in zip(ranges, ranges[1:]):
+        assert b0 == a1
+    sizes = [b - a for a, b in ranges]
+    assert all(s in (L // n, L // n + 1) for s in sizes)
+    assert sizes == sorted(sizes, reverse=True)
+    assert sum(s == L // n + 1 for s in sizes) == (L % n if L % n else 0) or L % n == 0
+    for layer in range(L):
+        r = O.layer_owner(L, n, layer)
+        a, b = ranges[r]
+        assert a <= layer < b
+    assert O.local_layer_count(L, n, 0) == sizes[0] + 1
+
+
+def test_layer_split_64_over_4():
+    assert [O.layer_range(64, 4, r) for r in range(4)] == [(0, 16), (16, 32), (32, 48), (48, 64)]
+    assert O.local_layer_count(64, 4, 2) == 17
+
+
+# --------------------------------------------------------------------------- round robin, filter
+
+
+def test_round_robin_animation():
+    for p, d, s in _rows("round_robin_16_over_4.txt"):
+        assert O.dcp_owner(int(p), 4) == int(d)
+        assert O.dcp_local_slot(int(p), 4) == int(s)
+
+
+@pytest.mark.parametrize("n,m", [(1, 5), (2, 7), (4, 16), (8, 9)])
+def test_owner_slot_bijection(n, m):
+    seen = set()
+    for p in range(n * m):
+        d, s = O.dcp_owner(p, n), O.dcp_local_slot(p, n)
+        assert 0 <= d < n and 0 <= s < m
+        assert s * n + d == p
+        seen.add((d, s))
+    assert len(seen) == n * m
+
+
+def test_filter_log_line_256_to_64():
+    t = {k: v for k, v in _rows("transfer_volume.txt")}
+    full = int(t["log_pages_full"])
+    pages = list(range(full))
+    for d in range(4):
+        kept = O.filter_kv_indices_for_dcp_rank(pages, 4, d)
+        assert len(kept) == int(t["log_pages_per_rank"])
+        assert kept == list(range(64))
+    # N <= 1 passes the list unchanged
+    assert O.filter_kv_indices_for_dcp_rank([5, 3, 9], 1, 0) == [5, 3, 9]
+
+
+def test_filter_reconstructs_full_set():
+    rng = np.random.default_rng(0)
+    idx = rng.permutation(200)[:77].tolist()
+    back = set()
+    for d in range(8):
+        for s in O.filter_kv_indices_for_dcp_rank(idx, 8, d):
+            back.add(s * 8 + d)
+    assert back == set(idx)
+
+
+def test_ownership_by_value_not_position():
+    # destination values whose residues mod N differ from their list positions:
+    # the filter and the plan must follow the VALUE (section 6.3; reading R6)
+    dst = [7, 2, 4, 13, 0, 9]
+    src = [100, 101, 102, 103, 104, 105]
+    plan = O.reshard_plan(1, 1, 4, src, dst, 0)
+    got = {(d, s): sp for (_, _, sp, d, _, s) in plan}
+    assert got == {(3, 1): 100, (2, 0): 101, (0, 1): 102, (1, 3): 103, (0, 0): 104, (1, 2): 105}
+    for d in range(4):
+        assert sorted(O.filter_kv_indices_for_dcp_rank(dst, 4, d)) == sorted(s for (dd, s) in got if dd == d)
+
+
+# --------------------------------------------------------------------------- volumes
+
+
+def test_transfer_volume_bytes():
+    t = {k: v for k, v in _rows("transfer_volume.txt")}
+    L, B, T = int(t["layers"]), int(t["bytes_per_token_per_layer"]), int(t["tokens_32k"])
+    page = 64
+    pages = T // page
+    n = 4
+    pm = O.PageMap(n, page, pages)
+    g = pm.alloc(T)
+    plan = O.reshard_plan(L, 8, n, list(range(pages)), g, 0)
+    page_bytes = page * B
+    per_dst = [0] * n
+    paths = set()
+    for (r, _, _, d, _, _) in plan:
+        per_dst[d] += page_bytes
+        paths.add((r, d))
+    total = sum(per_dst)
+    assert total == L * B * T == 1_472_200_704
+    assert abs(total / 1e9 - float(t["total_kv_bytes_approx_gb"])) < 0.005
+    assert all(x == total // n for x in per_dst)
+    assert abs(per_dst[0] / 1e6 - float(t["per_rank_bytes_approx_mb"])) < 0.5
+    naive = n * total  # every rank receives the whole sequence (section 6.1)
+    assert abs(naive / 1e9 - float(t["naive_total_approx_gb"])) < 0.01
+    assert abs((naive - total) / 1e9 - float(t["naive_discarded_approx_gb"])) < 0.01
+    assert (naive - total) / naive == float(t["naive_discarded_frac"])
+    assert len(paths) == int(t["paths"])
+    assert abs(-(-int(t["tokens_500k"]) // page) / 1000 - float(t["pages_500k_approx_k"])) < 0.05
+
+
+def test_reshard_paths_cover_2d_target():
+    # section 2: each path (r, d) carries exactly L_r x P_d
+    L, ncp, n, pages = 11, 3, 4, 23
+    rng = np.random.default_rng(1)
+    pm = O.PageMap(n, 16, 40, rng.permutation(40))
+    g = pm.alloc(pages * 16)
+    src = rng.permutation(60)[:pages]
+    plan = O.reshard_plan(L, ncp, n, src, g, 0)
+    for r in range(ncp):
+        a, b = O.layer_range(L, ncp, r)
+        for d in range(n):
+            got = {(ls + a, sp) for (rr, ls, sp, dd, _, _) in plan if rr == r and dd == d}
+            want = {(layer, int(src[i])) for layer in range(a, b) for i in range(pages) if g[i] % n == d}
+            assert got == want
+
+
+# --------------------------------------------------------------------------- reshard brute force
+
+
+def _tagged_sources(L, ncp, S, page_bytes):
+    pools = []
+    for r in range(ncp):
+        n_slots = O.local_layer_count(L, ncp, r)
+        p = np.zeros((n_slots, S, page_bytes), dtype=np.uint8)
+        for ls in range(n_slots):
+            for sp in range(S):
+                tag = np.frombuffer(np.array([r, ls, sp, 0xC0FFEE], dtype=np.int32).tobytes(), dtype=np.uint8)
+                p[ls, sp] = np.resize(tag, page_bytes)
+        p[-1] = 0xEE  # transient slot: must never appear in a destination
+        pools.append(p)
+    return pools
+
+
+@pytest.mark.parametrize("n,cached,dst_filter", [(1, 0, -1), (2, 0, -1), (4, 3, -1), (3, 5, -1), (4, 2, 1)])
+def test_reshard_bruteforce_tags(n, cached, dst_filter):
+    L, ncp, S, M, psz, page_bytes = 7, 3, 30, 20, 16, 32
+    rng = np.random.default_rng(7 + n)
+    pm = O.PageMap(n, psz, M, rng.permutation(M))
+    T = 19 * psz - 5
+    g = pm.alloc(T)
+    P = len(g)
+    src = rng.permutation(S)[:P]
+    srcp = _tagged_sources(L, ncp, S, page_bytes)
+    dst = [np.full((L, M, page_bytes), 0xA5, dtype=np.uint8) for _ in range(n)]
+    sent = O.reshard(srcp, dst, L, n, src, g, cached, dst_filter)
+    # pull view: for every destination page decide independently what must be there
+    where = {int(gg): i for i, gg in enumerate(g)}
+    for d in range(n):
+        for layer in range(L):
+            owner = next(r for r in range(ncp) if O.layer_range(L, ncp, r)[0] <= layer < O.layer_range(L, ncp, r)[1])
+            for s in range(M):
+                gg = s * n + d
+                i = where.get(gg)
+                page = dst[d][layer, s]
+                if i is None or i < cached or (dst_filter >= 0 and d != dst_filter):
+                    assert (page == 0xA5).all()
+                else:
+                    tag = page[:16].view(np.int32)
+                    assert tag.tolist() == [owner, layer - O.layer_range(L, ncp, owner)[0], int(src[i]), 0xC0FFEE]
+                assert not (page == 0xEE).all()
+    for d in range(n):
+        want = sum(1 for i in range(cached, P) if g[i] % n == d) if (dst_filter < 0 or dst_filter == d) else 0
+        assert sent[d] == want
+
+
+def test_reshard_moves_scales():
+    L, n, M, S = 2, 2, 4, 6
+    src = [np.arange(3 * S * 8, dtype=np.uint8).reshape(3, S, 8)]
+    ssc = [np.arange(3 * S, dtype=np.uint16).reshape(3, S) + 1000]
+    dst = [np.zeros((L, M, 8), np.uint8) for _ in range(n)]
+    dsc = [np.zeros((L, M), np.uint16) for _ in range(n)]
+    g = [4, 1, 2, 7]
+    sp = [5, 0, 3, 2]
+    O.reshard(src, dst, L, n, sp, g, 0, src_scales=ssc, dst_scales=dsc)
+    for i, gg in enumerate(g):
+        for layer in range(L):
+            assert dsc[gg % n][layer, gg // n] == ssc[0][layer, sp[i]]
+            assert (dst[gg % n][layer, gg // n] == src[0][layer, sp[i]]).all()
+
+
+# --------------------------------------------------------------------------- page map
+
+
+def test_pagemap_canonical_and_log_line():
+    n, page = 4, 64
+    pm = O.PageMap(n, page, 100, np.random.default_rng(3).permutation(100))
+    g = pm.alloc(16384)  # 16K tokens -> 256 pages, 64 per rank (section 6.3 log line)
+    assert len(g) == 256 and len(set(g)) == 256
+    for i, gg in enumerate(g):
+        assert gg % n == i % n  # page p lands on rank p mod N
+        assert 0 <= gg // n < 100
+    assert sum(1 for gg in g if gg % n == 2) == 64
+    # one virtual page = N physical pages, one per rank, same local slot (section 6.4)
+    for v in range(64):
+        assert len({g[v * n + k] // n for k in range(n)}) == 1
+
+
+def test_pagemap_partial_last_virtual_page_and_exhaustion():
+    pm = O.PageMap(4, 16, 3, [2, 0, 1])
+    g = pm.alloc(16 * 5 + 1)  # 6 pages -> 2 virtual pages
+    assert g == [8, 9, 10, 11, 0, 1]
+    with pytest.raises(MemoryError):
+        pm.alloc(16 * 4 * 2)
+    pm.release(g)
+    assert list(pm.free) == [1, 2, 0]  # FIFO reuse (reading R12)
+    with pytest.raises(ValueError):
+        pm.release(g)
+    with pytest.raises(ValueError):
+        pm.alloc(0)
+
+
+# --------------------------------------------------------------------------- number formats
+
+
+def test_e4m3fn_table_vs_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            assert math.isnan(O.E4M3FN_TABLE[c]) and math.isnan(ref[c])
+        else:
+            assert O.E4M3FN_TABLE[c] == ref[c], c
+    assert O.e4m3fn_value(0x7E) == 448.0
+    assert O.e4m3fn_value(0x01) == 2.0 ** -9
+    assert O.e4m3fn_value(0x08) == 2.0 ** -6
+    assert O.e4m3fn_value(0x38) == 1.0
+    assert math.copysign(1.0, O.e4m3fn_value(0x80)) == -1.0
+
+
+def test_bf16_decode_vs_torch():
+    bits = torch.randint(-32768, 32767, (4096,), dtype=torch.int16, generator=torch.Generator().manual_seed(0))
+    ref = bits.view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_bits_to_f64(bits.numpy())
+    ok = ~np.isnan(ref)
+    assert (got[ok] == ref[ok]).all() and np.isnan(got[~ok]).all()
+
+
+def test_fp8_times_bf16_scale_exact_in_f32():
+    # dequant in float32 (code * scale) equals the float64 product: 4 x 8 significant bits
+    rng = np.random.default_rng(5)
+    scales = rng.integers(0x3000, 0x4400, size=64).astype(np.uint16)
+    sv = O.bf16_bits_to_f64(scales)
+    for c in range(256):
+        if c in (0x7F, 0xFF):
+            continue
+        x64 = O.E4M3FN_TABLE[c] * sv
+        x32 = (np.float32(O.E4M3FN_TABLE[c]) * sv.astype(np.float32)).astype(np.float64)
+        assert (x32 == x64).all()
+
+
+def test_decode_pages_vs_torch():
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 256, size=(16, 576), dtype=np.uint8)
+    codes[codes == 0x7F] = 0
+    codes[codes == 0xFF] = 0
+    sbits = int(torch.tensor([0.0123], dtype=torch.bfloat16).view(torch.int16).item()) & 0xFFFF
+    got = O.decode_mla_page(codes, sbits, 16)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64) * float(
+        torch.tensor([sbits], dtype=torch.int32).to(torch.int16).view(torch.bfloat16).item())
+    assert np.array_equal(got, ref.numpy())
+    x = torch.randn(2, 3, 4, 8, dtype=torch.float32)
+    k, v = O.decode_split_page(x.numpy().view(np.uint8).reshape(-1), "f32", 3, 4, 8)
+    assert np.array_equal(k, x[0].double().numpy()) and np.array_equal(v, x[1].double().numpy())
+    xb = x.to(torch.bfloat16)
+    k, v = O.decode_split_page(xb.view(torch.int16).numpy().view(np.uint8).reshape(-1), "bf16", 3, 4, 8)
+    assert np.array_equal(k, xb[0].double().numpy()) and np.array_equal(v, xb[1].double().numpy())
+
+
+# --------------------------------------------------------------------------- attention
+
+
+def _rand_req(rng, T, q_len, hq, hkv, dqk, dv):
+    q = rng.standard_normal((q_len, hq, dqk))
+    k = rng.standard_normal((hkv, T, dqk))
+    v = rng.standard_normal((hkv, T, dv))
+    return q, k, v
+
+
+@pytest.mark.parametrize("T,q_len,hq,hkv", [(37, 1, 4, 1), (50, 3, 8, 2), (9, 4, 6, 3)])
+def test_attention_vs_torch_sdpa(T, q_len, hq, hkv):
+    rng = np.random.default_rng(T)
+    dqk, dv = 12, 10
+    q, k, v = _rand_req(rng, T, q_len, hq, hkv, dqk, dv)
+    scale = 1 / math.sqrt(dqk)
+    out, lse = O.request_attention(q, k, v, T, scale)
+    qt = torch.from_numpy(q).permute(1, 0, 2)  # [Hq][q_len][D]
+    grp = hq // hkv
+    kt = torch.from_numpy(k).repeat_interleave(grp, dim=0)  # head h reads kv head h // grp
+    vt = torch.from_numpy(v).repeat_interleave(grp, dim=0)
+    pos = torch.tensor([T - q_len + t for t in range(q_len)])
+    mask = torch.arange(T)[None, :] <= pos[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+    assert np.allclose(out, ref.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+    s = scale * (qt @ kt.transpose(-1, -2))
+    ref_lse = torch.logsumexp(s.masked_fill(~mask, float("-inf")), dim=-1)
+    assert np.allclose(lse, ref_lse.T.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_head_mapping_is_contiguous_groups():
+    # kv head 0 all zeros, kv head 1 all ones: heads 0..1 must see zeros, heads 2..3 ones
+    T = 5
+    q = np.ones((1, 4, 3))
+    k = np.zeros((2, T, 3))
+    v = np.stack([np.zeros((T, 2)), np.ones((T, 2))])
+    out, _ = O.request_attention(q, k, v, T, 1.0)
+    assert (out[0, :2] == 0).all() and (out[0, 2:] == 1).all()
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(11)
+    q, k, v = _rand_req(rng, 1, 1, 2, 1, 6, 5)
+    out, lse = O.request_attention(q, k, v, 1, 0.5)
+    assert np.allclose(out[0, 0], v[0, 0]) and np.isclose(lse[0, 0], 0.5 * q[0, 0] @ k[0, 0])
+    # equal scores: O = mean of visible v, LSE = log(n)
+    T = 13
+    q = np.zeros((2, 1, 4))
+    _, k, v = _rand_req(rng, T, 2, 1, 1, 4, 3)
+    out, lse = O.request_attention(q, k, v, T, 1.0)
+    assert np.allclose(out[0, 0], v[0, :T - 1].mean(0)) and np.isclose(lse[0, 0], math.log(T - 1))
+    assert np.allclose(out[1, 0], v[0, :T].mean(0)) and np.isclose(lse[1, 0], math.log(T))
+    # a constant added to every score shifts LSE by it and leaves O unchanged
+    q, k, v = _rand_req(rng, 20, 1, 1, 1, 4, 3)
+    o1, l1 = O.request_attention(q, k, v, 20, 1.0)
+    c = 2.75
+    q2 = np.concatenate([q, np.full((1, 1, 1), c)], axis=2)
+    k2 = np.concatenate([k, np.ones((1, 20, 1))], axis=2)
+    o2, l2 = O.request_attention(q2, k2, v, 20, 1.0)
+    assert np.allclose(o1, o2, rtol=1e-13) and np.isclose(l2[0, 0], l1[0, 0] + c, rtol=1e-13)
+
+
+def test_attention_bruteforce_fsum():
+    rng = np.random.default_rng(12)
+    T, dqk, dv = 7, 3, 2
+    q, k, v = _rand_req(rng, T, 2, 2, 1, dqk, dv)
+    out, lse = O.request_attention(q, k, v, T, 0.7)
+    for t in range(2):
+        pos = T - 2 + t
+        for h in range(2):
+            s = [0.7 * math.fsum(q[t, h, i] * k[0, j, i] for i in range(dqk)) for j in range(pos + 1)]
+            z = math.fsum(math.exp(x) for x in s)
+            assert math.isclose(lse[t, h], math.log(z), rel_tol=1e-13)
+            for c in range(dv):
+                want = math.fsum(math.exp(s[j]) / z * v[0, j, c] for j in range(pos + 1))
+                assert math.isclose(out[t, h, c], want, rel_tol=1e-12, abs_tol=1e-14)
+
+
+# --------------------------------------------------------------------------- partials + merge
+
+
+def _sharded_case(seed, n, T=301, page=16, q_len=2, hq=4, hkv=2, d=8):
+    rng = np.random.default_rng(seed)
+    q, k, v = _rand_req(rng, T, q_len, hq, hkv, d, d)
+    pm = O.PageMap(n, page, 64, rng.permutation(64))
+    g = pm.alloc(T)
+    return q, k, v, g, T, page
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
+def test_merge_equals_unsharded(n):
+    q, k, v, g, T, page = _sharded_case(n, n)
+    ref_o, ref_l = O.request_attention(q, k, v, T, 0.3)
+    po, pl = O.request_partials(q, k, v, T, 0.3, g, page, n)
+    mo, ml = O.lse_merge(po, pl)
+    assert np.allclose(mo, ref_o, rtol=1e-12, atol=1e-13)
+    assert np.allclose(ml, ref_l, rtol=1e-12, atol=1e-13)
+    if n == 1:
+        assert np.allclose(po[0], ref_o, rtol=0, atol=0) and np.allclose(pl[0], ref_l, rtol=0, atol=0)
+
+
+def test_merge_order_independent_and_associative():
+    q, k, v, g, T, page = _sharded_case(21, 4)
+    po, pl = O.request_partials(q, k, v, T, 0.3, g, page, 4)
+    a = O.lse_merge(po, pl)
+    perm = [2, 0, 3, 1]
+    b = O.lse_merge(po[perm], pl[perm])
+    assert np.allclose(a[0], b[0], rtol=1e-13) and np.allclose(a[1], b[1], rtol=1e-13)
+    # merge pairs first, then merge the two results
+    m01 = O.lse_merge(po[:2], pl[:2])
+    m23 = O.lse_merge(po[2:], pl[2:])
+    c = O.lse_merge(np.stack([m01[0], m23[0]]), np.stack([m01[1], m23[1]]))
+    assert np.allclose(a[0], c[0], rtol=1e-13) and np.allclose(a[1], c[1], rtol=1e-13)
+
+
+def test_merge_split_shard_further():
+    # splitting a shard's tokens in two and merging gives that shard's partial
+    q, k, v, g, T, page = _sharded_case(22, 2)
+    mask = O.shard_token_mask(g, page, T, 2, 1)
+    idx = np.nonzero(mask)[0]
+    half = np.zeros(T, bool)
+    half[idx[: len(idx) // 2]] = True
+    o_full, l_full = O.request_attention(q, k, v, T, 0.3, mask)
+    o_a, l_a = O.request_attention(q, k, v, T, 0.3, mask & half)
+    o_b, l_b = O.request_attention(q, k, v, T, 0.3, mask & ~half)
+    mo, ml = O.lse_merge(np.stack([o_a, o_b]), np.stack([l_a, l_b]))
+    assert np.allclose(mo, o_full, rtol=1e-12, atol=1e-13) and np.allclose(ml, l_full, rtol=1e-12)
+
+
+def test_merge_empty_shard_and_all_empty():
+    o = np.random.default_rng(0).standard_normal((3, 5, 4))
+    l = np.array([[0.5, -1.0, 2.0, 0.1, 3.0], [-np.inf] * 5, [1.0, 1.0, 1.0, 1.0, 1.0]])
+    mo, ml = O.lse_merge(o, l)
+    mo2, ml2 = O.lse_merge(o[[0, 2]], l[[0, 2]])
+    assert np.allclose(mo, mo2) and np.allclose(ml, ml2)
+    mo3, ml3 = O.lse_merge(o, np.full((3, 5), -np.inf))
+    assert (mo3 == 0).all() and np.isneginf(ml3).all()
+    # a shard that holds nothing visible yields (0, -inf)
+    q, k, v = _rand_req(np.random.default_rng(1), 10, 1, 2, 1, 4, 4)
+    oo, ll = O.request_attention(q, k, v, 10, 1.0, np.zeros(10, bool))
+    assert (oo == 0).all() and np.isneginf(ll).all()
+
+
+def test_logical_kv_gather_from_pools():
+    # pages placed by the page map's owner/slot are read back in sequence order
+    n, page, hkv, dd, M = 2, 4, 1, 3, 6
+    rng = np.random.default_rng(4)
+    pm = O.PageMap(n, page, M, rng.permutation(M))
+    T = 17
+    g = pm.alloc(T)
+    k = rng.standard_normal((hkv, len(g) * page, dd)).astype(np.float32)
+    v = rng.standard_normal((hkv, len(g) * page, dd)).astype(np.float32)
+    pools = np.zeros((n, M, 2, hkv, page, dd), np.float32)
+    for i, gg in enumerate(g):
+        pools[gg % n, gg // n, 0] = k[:, i * page:(i + 1) * page]
+        pools[gg % n, gg // n, 1] = v[:, i * page:(i + 1) * page]
+    kk, vv = O.logical_kv_split(lambda d, s: pools[d, s].reshape(-1).view(np.uint8), g, n, "f32", hkv, page, dd, T)
+    assert np.array_equal(kk, k[:, :T].astype(np.float64)) and np.array_equal(vv, v[:, :T].astype(np.float64))
