@@ -1,0 +1,280 @@
+"""ctypes binding of libdcpkv.so: argument marshalling only.
+
+Every function keeps the C name of the entry point it wraps (include/dcpkv.h)
+and only turns tensors into device pointers, Python lists into host arrays
+and status codes into exceptions.  All arithmetic runs in the library's HIP
+kernels; there is no other path.  If the library is missing, importing this
+module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdcpkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m context_paged_kv_amd.build` "
+        "(this package has no fallback path)")
+
+# One HIP runtime per process: torch ships its own libamdhip64 (same SONAME as
+# ROCm's).  Importing torch first makes the loader bind this library to the
+# runtime torch already uses; loading ours first would bring up a second HIP/HSA
+# runtime that sees no device.
+import torch  # noqa: E402,F401
+
+_lib = C.CDLL(LIB_PATH)
+
+DCPKV_OK = 0
+DCPKV_EDEVICE = -5
+DCPKV_ENOMEM = -12
+DCPKV_EINVAL = -22
+DCPKV_ENOSPC = -28
+DCPKV_ENOTSUP = -95
+KV_F32, KV_BF16, KV_FP8E4M3 = 0, 1, 2
+LAYOUT_SPLIT, LAYOUT_MLA = 0, 1
+Q_F32, Q_BF16 = 0, 1
+
+EXPORTED = (
+    "dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
+    "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
+    "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
+    "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge",
+)
+
+
+class DcpkvError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class kv_reshard_desc(C.Structure):
+    _fields_ = [("num_sources", C.c_int32), ("num_layers", C.c_int32), ("dcp_size", C.c_int32),
+                ("dst_filter", C.c_int32), ("page_bytes", C.c_int64), ("src_pages", C.c_int64),
+                ("dst_pages", C.c_int64)]
+
+
+class dcp_attn_desc(C.Structure):
+    _fields_ = [("kv_dtype", C.c_int32), ("kv_layout", C.c_int32), ("q_dtype", C.c_int32),
+                ("num_q_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim_qk", C.c_int32), ("head_dim_v", C.c_int32), ("page_size", C.c_int32),
+                ("dcp_size", C.c_int32), ("batch", C.c_int32), ("q_len", C.c_int32),
+                ("max_local_pages", C.c_int32), ("layer", C.c_int32), ("num_layers", C.c_int32),
+                ("pages_per_layer", C.c_int64), ("softmax_scale", C.c_float), ("pad2_", C.c_float)]
+
+
+_P = C.c_void_p
+_I32P = C.POINTER(C.c_int32)
+_I64P = C.POINTER(C.c_int64)
+
+_lib.dcpkv_last_error.restype = C.c_char_p
+_lib.dcpkv_last_error.argtypes = []
+_lib.dcpkv_abi_version.restype = C.c_int
+_lib.cp_layersplit_layer_range.argtypes = [C.c_int32, C.c_int32, C.c_int32, _I32P, _I32P]
+_lib.dcp_filter_kv_indices.argtypes = [_I64P, C.c_int64, C.c_int32, C.c_int32, _I64P, _I64P]
+_lib.dcp_pagemap_create.argtypes = [C.c_int32, C.c_int32, C.c_int64, _I64P, C.POINTER(_P)]
+_lib.dcp_pagemap_destroy.argtypes = [_P]
+_lib.dcp_pagemap_destroy.restype = None
+_lib.dcp_pagemap_num_free.argtypes = [_P]
+_lib.dcp_pagemap_num_free.restype = C.c_int64
+_lib.dcp_pagemap_alloc.argtypes = [_P, C.c_int64, _I64P, C.c_int64]
+_lib.dcp_pagemap_release.argtypes = [_P, _I64P, C.c_int64]
+_lib.dcp_build_block_tables.argtypes = [C.c_int32, C.c_int32, _I64P, _I64P, C.c_int32, _I32P, _I32P]
+_lib.kv_reshard_pages.argtypes = [C.POINTER(kv_reshard_desc), C.POINTER(_P), C.POINTER(_P),
+                                  C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, C.c_int64, _P, _P]
+_lib.dcp_decode_partial_workspace.argtypes = [C.POINTER(dcp_attn_desc), C.c_int64]
+_lib.dcp_decode_partial_workspace.restype = C.c_size_t
+_lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P,
+                                    _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P]
+_lib.dcp_lse_merge.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P]
+for _f in ("cp_layersplit_layer_range", "dcp_filter_kv_indices", "dcp_pagemap_create",
+           "dcp_pagemap_alloc", "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
+           "dcp_decode_partial", "dcp_lse_merge"):
+    getattr(_lib, _f).restype = C.c_int
+
+
+def _check(rc: int) -> None:
+    if rc != DCPKV_OK:
+        raise DcpkvError(rc, _lib.dcpkv_last_error().decode(errors="replace"))
+
+
+def _i64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+
+
+def _ptr64(a: np.ndarray):
+    return a.ctypes.data_as(_I64P)
+
+
+def _ptr32(a: np.ndarray):
+    return a.ctypes.data_as(_I32P)
+
+
+def _dptr(t) -> Optional[int]:
+    """Device pointer of a tensor (None passes NULL)."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise ValueError("expected a tensor in GPU memory")
+    return t.data_ptr()
+
+
+def _ptr_array(ts):
+    if ts is None:
+        return None
+    arr = (_P * len(ts))(*[_dptr(t) for t in ts])
+    return arr
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return int(stream)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dcpkv_last_error() -> str:
+    return _lib.dcpkv_last_error().decode(errors="replace")
+
+
+def dcpkv_abi_version() -> int:
+    return _lib.dcpkv_abi_version()
+
+
+def cp_layersplit_layer_range(num_layers: int, num_sources: int, r: int):
+    b, e = C.c_int32(), C.c_int32()
+    _check(_lib.cp_layersplit_layer_range(num_layers, num_sources, r, C.byref(b), C.byref(e)))
+    return b.value, e.value
+
+
+def dcp_filter_kv_indices(kv_indices: Sequence[int], dcp_size: int, dcp_rank: int) -> np.ndarray:
+    idx = _i64(kv_indices)
+    out = np.empty(max(1, idx.size), dtype=np.int64)
+    cnt = C.c_int64()
+    _check(_lib.dcp_filter_kv_indices(_ptr64(idx), idx.size, dcp_size, dcp_rank, _ptr64(out), C.byref(cnt)))
+    return out[: cnt.value].copy()
+
+
+def dcp_pagemap_create(dcp_size: int, page_size: int, num_virtual_pages: int, free_order=None) -> int:
+    h = _P()
+    fo = None if free_order is None else _i64(free_order)
+    _check(_lib.dcp_pagemap_create(dcp_size, page_size, num_virtual_pages,
+                                   None if fo is None else _ptr64(fo), C.byref(h)))
+    return h.value
+
+
+def dcp_pagemap_destroy(handle: int) -> None:
+    _lib.dcp_pagemap_destroy(handle)
+
+
+def dcp_pagemap_num_free(handle: int) -> int:
+    return _lib.dcp_pagemap_num_free(handle)
+
+
+def dcp_pagemap_alloc(handle: int, num_tokens: int, page_size: int) -> np.ndarray:
+    cap = max(1, -(-num_tokens // page_size))
+    out = np.empty(cap, dtype=np.int64)
+    _check(_lib.dcp_pagemap_alloc(handle, num_tokens, _ptr64(out), cap))
+    return out
+
+
+def dcp_pagemap_release(handle: int, global_pages: Sequence[int]) -> None:
+    g = _i64(global_pages)
+    _check(_lib.dcp_pagemap_release(handle, _ptr64(g) if g.size else None, g.size))
+
+
+class PageMap:
+    """Owning handle around dcp_pagemap_* (frees the host object on close)."""
+
+    def __init__(self, dcp_size: int, page_size: int, num_virtual_pages: int, free_order=None):
+        self.dcp_size, self.page_size = dcp_size, page_size
+        self.handle = dcp_pagemap_create(dcp_size, page_size, num_virtual_pages, free_order)
+
+    def alloc(self, num_tokens: int) -> np.ndarray:
+        return dcp_pagemap_alloc(self.handle, num_tokens, self.page_size)
+
+    def release(self, global_pages) -> None:
+        dcp_pagemap_release(self.handle, global_pages)
+
+    def num_free(self) -> int:
+        return dcp_pagemap_num_free(self.handle)
+
+    def close(self) -> None:
+        if self.handle:
+            dcp_pagemap_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def dcp_build_block_tables(dcp_size: int, pages_per_request: Sequence[Sequence[int]], max_local_pages: int):
+    """Returns (tables int32 [N][B][max_local_pages], counts int32 [N][B])."""
+    batch = len(pages_per_request)
+    offs = np.zeros(batch + 1, dtype=np.int64)
+    for b, pg in enumerate(pages_per_request):
+        offs[b + 1] = offs[b] + len(pg)
+    flat = _i64(np.concatenate([np.asarray(p, dtype=np.int64) for p in pages_per_request])
+                if batch else np.zeros(0, np.int64))
+    tables = np.empty((dcp_size, batch, max_local_pages), dtype=np.int32)
+    counts = np.empty((dcp_size, batch), dtype=np.int32)
+    _check(_lib.dcp_build_block_tables(dcp_size, batch, _ptr64(flat) if flat.size else None, _ptr64(offs),
+                                       max_local_pages, _ptr32(tables), _ptr32(counts)))
+    return tables, counts
+
+
+def kv_reshard_pages(*, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int, dst_pages: int,
+                     src_pools, dst_pools, src_page_ids, dst_global_pages, first_uncached: int = 0,
+                     dst_filter: int = -1, src_scales=None, dst_scales=None, bad_entries=None,
+                     num_pages: Optional[int] = None, stream=None) -> None:
+    """Enqueue the page-level 2D reshard (see include/dcpkv.h)."""
+    desc = kv_reshard_desc(len(src_pools), num_layers, dcp_size, dst_filter, page_bytes, src_pages, dst_pages)
+    n = src_page_ids.numel() if num_pages is None else num_pages
+    _check(_lib.kv_reshard_pages(C.byref(desc), _ptr_array(src_pools), _ptr_array(dst_pools),
+                                 _ptr_array(src_scales), _ptr_array(dst_scales), _dptr(src_page_ids),
+                                 _dptr(dst_global_pages), n, first_uncached, _dptr(bad_entries),
+                                 _stream(stream)))
+
+
+def make_attn_desc(*, kv_dtype: int, kv_layout: int, q_dtype: int, num_q_heads: int, num_kv_heads: int,
+                   head_dim_qk: int, head_dim_v: int, page_size: int, dcp_size: int, batch: int,
+                   q_len: int, max_local_pages: int, layer: int, num_layers: int, pages_per_layer: int,
+                   softmax_scale: float) -> dcp_attn_desc:
+    return dcp_attn_desc(kv_dtype, kv_layout, q_dtype, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
+                         page_size, dcp_size, batch, q_len, max_local_pages, layer, num_layers, pages_per_layer,
+                         softmax_scale, 0.0)
+
+
+def dcp_decode_partial_workspace(desc: dcp_attn_desc, total_tokens: int) -> int:
+    n = _lib.dcp_decode_partial_workspace(C.byref(desc), total_tokens)
+    if n == 0:
+        raise DcpkvError(DCPKV_EINVAL, "bad attention descriptor")
+    return n
+
+
+def dcp_decode_partial(desc: dcp_attn_desc, *, q, kv_pools, kv_scales, block_tables, seq_lens,
+                       total_tokens: int, partial_out, partial_lse, workspace, shard_begin: int = 0,
+                       shard_count: Optional[int] = None, stream=None) -> None:
+    """Enqueue per-shard partial attention (see include/dcpkv.h)."""
+    sc = desc.dcp_size - shard_begin if shard_count is None else shard_count
+    _check(_lib.dcp_decode_partial(C.byref(desc), _dptr(q), _ptr_array(kv_pools), _ptr_array(kv_scales),
+                                   _dptr(block_tables), _dptr(seq_lens), total_tokens, shard_begin, sc,
+                                   _dptr(partial_out), _dptr(partial_lse), _dptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dcp_lse_merge(dcp_size: int, rows: int, head_dim_v: int, partial_out, partial_lse, out, out_lse=None,
+                  stream=None) -> None:
+    """Enqueue the exact LSE merge of dcp_size partials (see include/dcpkv.h)."""
+    _check(_lib.dcp_lse_merge(dcp_size, rows, head_dim_v, _dptr(partial_out), _dptr(partial_lse), _dptr(out),
+                              _dptr(out_lse), _stream(stream)))

@@ -1,0 +1,591 @@
+// Per-shard partial decode attention and the exact LSE merge.
+//
+// [2DR] = "Serving Macaron-V1 at Scale: Page-Level 2D KV Resharding"
+//         (section 5.2: DCP attention, LSE merge; section 8: verify under DCP
+//         with several draft tokens per request);
+// [SGL] = "SGLang's path" (serving-k3, module 05): each rank produces a
+//         partial (weighted sum + log-sum-exp) and the recombination is exact.
+//
+// This file holds the launch planning shared by every partial kernel, the
+// generic VALU kernel (every dtype and layout; the reference path for odd
+// shapes), the chunk reduction and dcp_lse_merge.  The MFMA kernels for the
+// bf16 GQA and fp8 MLA shapes live in their own files and plug in through
+// launch_fast_partial().
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+
+#include "attn_common.h"
+#include "attn_kernels.h"
+
+namespace dcpkv {
+
+// ---------------------------------------------------------------------------
+// Plan: chunks per (shard, request) pair and workspace slots (one workgroup)
+// ---------------------------------------------------------------------------
+
+constexpr int kPlanThreads = 256;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
+  __shared__ int32_t s_k[kPlanThreads];
+  __shared__ int32_t s_w[kPlanThreads];
+  __shared__ unsigned long long s_need;
+  __shared__ int32_t s_carry_k, s_carry_w;
+  const int tid = threadIdx.x;
+  const int num_pairs = p.shard_count * p.batch;
+  const int C = p.chunk_pages;
+  if (tid == 0) {
+    s_need = 0;
+    s_carry_k = 0;
+    s_carry_w = 0;
+  }
+  __syncthreads();
+  unsigned long long mine = 0;
+  for (int i = tid; i < num_pairs; i += kPlanThreads) {
+    const int d = p.shard_begin + i / p.batch, b = i % p.batch;
+    const int nl = local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
+    const int k = nl > C ? (nl + C - 1) / C : 1;
+    if (k >= 2) mine += k;
+  }
+  atomicAdd(&s_need, mine);
+  __syncthreads();
+  const int fallback = s_need > (unsigned long long)p.ws_cap ? 1 : 0;
+  for (int base = 0; base < num_pairs; base += kPlanThreads) {
+    const int i = base + tid;
+    int k = 0, kw = 0, nl = 0;
+    if (i < num_pairs) {
+      const int d = p.shard_begin + i / p.batch, b = i % p.batch;
+      nl = local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
+      k = (!fallback && nl > C) ? (nl + C - 1) / C : 1;
+      kw = k >= 2 ? k : 0;
+    }
+    s_k[tid] = k;
+    s_w[tid] = kw;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan
+      const int a = tid >= off ? s_k[tid - off] : 0;
+      const int w = tid >= off ? s_w[tid - off] : 0;
+      __syncthreads();
+      s_k[tid] += a;
+      s_w[tid] += w;
+      __syncthreads();
+    }
+    if (i < num_pairs) {
+      PairPlan pp;
+      pp.chunk_begin = s_carry_k + s_k[tid] - k;
+      pp.ws_begin = kw ? s_carry_w + s_w[tid] - kw : -1;
+      pp.k = k;
+      pp.n_local = nl;
+      p.pairs[i] = pp;
+    }
+    __syncthreads();
+    if (tid == kPlanThreads - 1) {
+      s_carry_k += s_k[tid];
+      s_carry_w += s_w[tid];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.hdr->total_chunks = s_carry_k;
+    p.hdr->ws_chunks = s_carry_w;
+    p.hdr->fallback = fallback;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic VALU partial kernel
+// ---------------------------------------------------------------------------
+
+constexpr int kGenThreads = 256;
+constexpr int kGenTT = 16;  // tokens per tile
+
+template <int KIND>
+struct GenCfg;
+template <>
+struct GenCfg<0> {  // split f32
+  static constexpr int RB = 16;
+};
+template <>
+struct GenCfg<1> {  // split bf16
+  static constexpr int RB = 16;
+};
+template <>
+struct GenCfg<2> {  // mla fp8
+  static constexpr int RB = 8;
+};
+
+size_t generic_lds_bytes(int kind, int dqk, int dv) {
+  const int RB = kind == 2 ? 8 : 16;
+  size_t f = (size_t)RB * (dqk + 1) + (size_t)kGenTT * (dqk + 1);
+  if (kind != 2) f += (size_t)kGenTT * (dv + 1);
+  f += (size_t)RB * kGenTT + 3 * RB;
+  return f * sizeof(float);
+}
+
+template <typename QT>
+__device__ __forceinline__ float load_q(const QT* q, int64_t i);
+template <>
+__device__ __forceinline__ float load_q<float>(const float* q, int64_t i) {
+  return q[i];
+}
+template <>
+__device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q, int64_t i) {
+  return bf16_to_float(q[i]);
+}
+
+// Decode item w into its pair, chunk and head block.
+__device__ __forceinline__ void decode_item(const AttnParams& p, int w, int& pair, int& chunk,
+                                            int& hb) {
+  const int gc = w / p.hb_count;
+  hb = w - gc * p.hb_count;
+  int lo = 0, hi = p.shard_count * p.batch - 1;
+  while (lo < hi) {  // last pair with chunk_begin <= gc
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.pairs[mid].chunk_begin <= gc)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  pair = lo;
+  chunk = gc - p.pairs[lo].chunk_begin;
+}
+
+template <int KIND, typename QT>
+__global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams p) {
+  constexpr int RB = GenCfg<KIND>::RB;
+  constexpr int TT = kGenTT;
+  constexpr int KMAX = RB * 512 / kGenThreads;
+  extern __shared__ float smem[];
+  const int DQ = p.dqk, DV = p.dv;
+  float* sQ = smem;
+  float* sK = sQ + RB * (DQ + 1);
+  float* sV = KIND == 2 ? sK : sK + TT * (DQ + 1);
+  const int vstride = KIND == 2 ? DQ + 1 : DV + 1;
+  float* sP = KIND == 2 ? sK + TT * (DQ + 1) : sV + TT * (DV + 1);
+  float* sM = sP + RB * TT;
+  float* sL = sM + RB;
+  float* sA = sL + RB;
+  const int tid = threadIdx.x;
+  const QT* q = static_cast<const QT*>(p.q);
+  const int total = p.hdr->total_chunks * p.hb_count;
+  const int rg_rows = p.group * p.q_len;  // rows sharing one KV head
+
+  for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    int pair, chunk, hb;
+    decode_item(p, w, pair, chunk, hb);
+    const PairPlan pp = p.pairs[pair];
+    const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
+    const int hk = hb / p.rb_per_head;
+    const int r0 = (hb % p.rb_per_head) * RB;
+    const int nrows = min(RB, rg_rows - r0);
+    const int T = p.seq_lens[b];
+    __syncthreads();  // previous item done with shared memory
+    for (int e = tid; e < RB * DQ; e += kGenThreads) {
+      const int r = e / DQ, k = e - r * DQ;
+      float v = 0.f;
+      if (r < nrows) {
+        const int rr = r0 + r, t = rr / p.group, h = hk * p.group + (rr % p.group);
+        v = load_q<QT>(q, (((int64_t)b * p.q_len + t) * p.hq + h) * DQ + k);
+      }
+      sQ[r * (DQ + 1) + k] = v;
+    }
+    if (tid < RB) {
+      sM[tid] = kNegInf;
+      sL[tid] = 0.f;
+    }
+    float acc[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) acc[k] = 0.f;
+
+    const int j_begin = chunk * p.chunk_pages;
+    const int j_end = min(pp.n_local, j_begin + p.chunk_pages);
+    const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
+    for (int jj = j_begin; jj < j_end; ++jj) {
+      const int32_t slot = bt[jj];
+      if (slot < 0 || slot >= p.pages_per_layer) continue;
+      const uint8_t* page =
+          p.pools[d] + ((int64_t)p.layer * p.pages_per_layer + slot) * p.page_bytes;
+      float pscale = 1.f;
+      if (KIND == 2) pscale = bf16_to_float(p.scales[d][(int64_t)p.layer * p.pages_per_layer + slot]);
+      const int64_t seq_page = (int64_t)jj * p.n + d;
+      for (int off = 0; off < p.page_size; off += TT) {
+        const int64_t pos0 = seq_page * p.page_size + off;
+        const int ntok = min(TT, p.page_size - off);
+        __syncthreads();  // previous tile consumed
+        for (int e = tid; e < TT * DQ; e += kGenThreads) {
+          const int j = e / DQ, k = e - j * DQ;
+          float kv = 0.f;
+          if (j < ntok && pos0 + j < T) {
+            const int tok = off + j;
+            if (KIND == 2) {
+              kv = e4m3fn_to_float(page[(int64_t)tok * 576 + k]) * pscale;
+            } else if (KIND == 1) {
+              const uint16_t* kp = reinterpret_cast<const uint16_t*>(page);
+              kv = bf16_to_float(kp[((int64_t)hk * p.page_size + tok) * DQ + k]);
+            } else {
+              const float* kp = reinterpret_cast<const float*>(page);
+              kv = kp[((int64_t)hk * p.page_size + tok) * DQ + k];
+            }
+          }
+          sK[j * (DQ + 1) + k] = kv;
+        }
+        if (KIND != 2) {
+          for (int e = tid; e < TT * DV; e += kGenThreads) {
+            const int j = e / DV, c = e - j * DV;
+            float vv = 0.f;
+            if (j < ntok && pos0 + j < T) {
+              const int tok = off + j;
+              const int64_t vi = (((int64_t)p.hkv + hk) * p.page_size + tok) * DV + c;
+              if (KIND == 1)
+                vv = bf16_to_float(reinterpret_cast<const uint16_t*>(page)[vi]);
+              else
+                vv = reinterpret_cast<const float*>(page)[vi];
+            }
+            sV[j * (DV + 1) + c] = vv;
+          }
+        }
+        __syncthreads();
+        // scores and online-softmax bookkeeping: thread (row r, token j)
+        {
+          const int r = tid / TT, j = tid % TT;
+          float s = kNegInf;
+          if (r < RB) {
+            const int rr = r0 + r;
+            const int t = rr / p.group;
+            const int64_t pos = pos0 + j;
+            if (r < nrows && j < ntok && pos < T && pos <= (int64_t)T - p.q_len + t) {
+              float dot = 0.f;
+              const float* qr = sQ + r * (DQ + 1);
+              const float* kr = sK + j * (DQ + 1);
+              for (int k = 0; k < DQ; ++k) dot += qr[k] * kr[k];
+              s = dot * p.scale;
+            }
+          }
+          float mx = s;
+#pragma unroll
+          for (int o = TT / 2; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, TT));
+          float m_old = r < RB ? sM[r] : kNegInf;
+          const float m_new = fmaxf(m_old, mx);
+          const float pj = (s == kNegInf) ? 0.f : expf(s - m_new);
+          float ps = pj;
+#pragma unroll
+          for (int o = TT / 2; o > 0; o >>= 1) ps += __shfl_xor(ps, o, TT);
+          if (r < RB) {
+            sP[r * TT + j] = pj;
+            if (j == 0) {
+              const float alpha = (m_old == kNegInf) ? 0.f : expf(m_old - m_new);
+              sA[r] = alpha;
+              sL[r] = sL[r] * alpha + ps;
+              sM[r] = m_new;
+            }
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int idx = tid + k * kGenThreads;
+          if (idx < nrows * DV) {
+            const int r = idx / DV, c = idx - r * DV;
+            float a = acc[k] * sA[r];
+            const float* pr = sP + r * TT;
+            for (int j = 0; j < TT; ++j) a += pr[j] * sV[j * vstride + c];
+            acc[k] = a;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // write the (chunk) partial
+    const bool direct = pp.k == 1;
+    const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
+    const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      const int idx = tid + k * kGenThreads;
+      if (idx < nrows * DV) {
+        const int r = idx / DV, c = idx - r * DV;
+        const int rr = r0 + r, t = rr / p.group, h = hk * p.group + (rr % p.group);
+        const int row = t * p.hq + h;
+        const float l = sL[r];
+        const float o = l > 0.f ? acc[k] / l : 0.f;
+        if (direct)
+          p.partial_out[(pair_row0 + row) * DV + c] = o;
+        else
+          p.ws_o[(ws_row0 + row) * DV + c] = o;
+      }
+    }
+    if (tid < nrows) {
+      const int rr = r0 + tid, t = rr / p.group, h = hk * p.group + (rr % p.group);
+      const int row = t * p.hq + h;
+      const float l = sL[tid];
+      const float lse = l > 0.f ? sM[tid] + logf(l) : kNegInf;
+      if (direct)
+        p.partial_lse[pair_row0 + row] = lse;
+      else
+        p.ws_lse[ws_row0 + row] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Chunk reduction: pairs split into k >= 2 chunks
+// ---------------------------------------------------------------------------
+
+constexpr int kRowsPerMergeBlock = 4;
+
+__global__ __launch_bounds__(256) void chunk_reduce_kernel(AttnParams p) {
+  const int pair = blockIdx.x;
+  const PairPlan pp = p.pairs[pair];
+  if (pp.k < 2) return;
+  const int row = blockIdx.y * kRowsPerMergeBlock + (threadIdx.x >> 6);
+  if (row >= p.rows) return;
+  const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
+  const int64_t out_row = ((int64_t)d * p.batch + b) * p.rows + row;
+  const int64_t ws_row = (int64_t)pp.ws_begin * p.rows + row;
+  wave_merge_row(pp.k, p.ws_lse + ws_row, p.rows, p.ws_o + ws_row * p.dv, (int64_t)p.rows * p.dv,
+                 p.dv, p.partial_out + out_row * p.dv, p.partial_lse + out_row);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-shard merge (dcp_lse_merge)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void lse_merge_kernel(int n, int64_t rows, int dv,
+                                                         const float* __restrict__ po,
+                                                         const float* __restrict__ pl,
+                                                         float* __restrict__ out,
+                                                         float* __restrict__ out_lse) {
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerMergeBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  wave_merge_row(n, pl + row, rows, po + row * dv, rows * dv, dv, out + row * dv,
+                 out_lse ? out_lse + row : nullptr);
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+static int device_cus() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> g(mu);
+  if (!cache[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+static int validate(const dcp_attn_desc& D) {
+  const bool split = D.kv_layout == DCPKV_LAYOUT_SPLIT, mla = D.kv_layout == DCPKV_LAYOUT_MLA;
+  if (!split && !mla) return set_error(DCPKV_EINVAL, "attn: unknown kv_layout %d", D.kv_layout);
+  if (split && D.kv_dtype != DCPKV_KV_F32 && D.kv_dtype != DCPKV_KV_BF16)
+    return set_error(DCPKV_EINVAL, "attn: split layout needs f32 or bf16 KV");
+  if (mla && D.kv_dtype != DCPKV_KV_FP8E4M3)
+    return set_error(DCPKV_EINVAL, "attn: MLA layout needs fp8 e4m3 KV");
+  if (D.q_dtype != DCPKV_Q_F32 && D.q_dtype != DCPKV_Q_BF16)
+    return set_error(DCPKV_EINVAL, "attn: unknown q_dtype %d", D.q_dtype);
+  if (D.num_q_heads < 1 || D.num_kv_heads < 1 || D.num_q_heads % D.num_kv_heads)
+    return set_error(DCPKV_EINVAL, "attn: Hq=%d must be a positive multiple of Hkv=%d",
+                     D.num_q_heads, D.num_kv_heads);
+  if (split && (D.head_dim_qk != D.head_dim_v || D.head_dim_qk < 1 || D.head_dim_qk > 256))
+    return set_error(DCPKV_EINVAL, "attn: split layout needs head_dim_qk == head_dim_v in [1, 256]");
+  if (mla && (D.head_dim_qk != 576 || D.head_dim_v != 512 || D.num_kv_heads != 1))
+    return set_error(DCPKV_EINVAL, "attn: MLA layout needs Dqk=576, Dv=512, one KV head");
+  if (D.page_size < 1 || D.dcp_size < 1 || D.dcp_size > kMaxShards || D.batch < 1 ||
+      D.q_len < 1 || D.max_local_pages < 1 || D.layer < 0 || D.layer >= D.num_layers ||
+      D.pages_per_layer < 1 || !(D.softmax_scale == D.softmax_scale))
+    return set_error(DCPKV_EINVAL, "attn: bad geometry");
+  if ((int64_t)D.q_len * D.num_q_heads > (1 << 20) || (int64_t)D.batch * D.dcp_size > (1 << 24))
+    return set_error(DCPKV_EINVAL, "attn: batch too large");
+  return DCPKV_OK;
+}
+
+static int64_t page_bytes_of(const dcp_attn_desc& D) {
+  if (D.kv_layout == DCPKV_LAYOUT_MLA) return (int64_t)D.page_size * 576;
+  const int64_t elem = D.kv_dtype == DCPKV_KV_F32 ? 4 : 2;
+  return 2 * (int64_t)D.num_kv_heads * D.page_size * D.head_dim_qk * elem;
+}
+
+struct Geometry {
+  int kind;          // KernelKind
+  int rb_rows, rb_per_head, hb_count, rows, chunk_pages;
+  int64_t ws_cap;
+  size_t hdr_off, pairs_off, o_off, lse_off, bytes;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus, Geometry& g) {
+  g.kind = choose_kernel(D);
+  g.rb_rows = kernel_rows_per_block(g.kind, D);
+  const int rg_rows = (D.num_q_heads / D.num_kv_heads) * D.q_len;
+  g.rb_per_head = (rg_rows + g.rb_rows - 1) / g.rb_rows;
+  g.hb_count = D.num_kv_heads * g.rb_per_head;
+  g.rows = D.q_len * D.num_q_heads;
+  const int64_t tot = std::max<int64_t>(total_tokens, 0);
+  const int64_t est_pages = tot / D.page_size + D.batch;  // >= sum of ceil(T_b / page)
+  const int64_t target_items = (int64_t)cus * kernel_items_per_cu(g.kind);
+  int64_t c = (est_pages * g.hb_count + target_items - 1) / std::max<int64_t>(target_items, 1);
+  c = std::max<int64_t>(c, kernel_min_chunk_pages(g.kind, D));
+  c = std::min<int64_t>(c, 1 << 20);
+  g.chunk_pages = (int)c;
+  // pairs with k >= 2 chunks hold at most 2 * (their local pages) / C chunks
+  g.ws_cap = 2 * est_pages / c + 1;
+  const int64_t pairs = (int64_t)D.dcp_size * D.batch;
+  g.hdr_off = 0;
+  g.pairs_off = align256(sizeof(PlanHeader));
+  g.o_off = align256(g.pairs_off + (size_t)pairs * sizeof(PairPlan));
+  g.lse_off = align256(g.o_off + (size_t)g.ws_cap * g.rows * D.head_dim_v * sizeof(float));
+  g.bytes = align256(g.lse_off + (size_t)g.ws_cap * g.rows * sizeof(float));
+}
+
+}  // namespace dcpkv
+
+using namespace dcpkv;
+
+extern "C" size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t total_tokens) {
+  if (!desc || validate(*desc) != DCPKV_OK) return 0;
+  Geometry g;
+  plan_geometry(*desc, total_tokens, device_cus(), g);
+  return g.bytes;
+}
+
+extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
+                                  const void* const* kv_pools, const void* const* kv_scales,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  int64_t total_tokens, int32_t shard_begin, int32_t shard_count,
+                                  float* partial_out, float* partial_lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!desc) return set_error(DCPKV_EINVAL, "attn: NULL descriptor");
+  const dcp_attn_desc& D = *desc;
+  int rc = validate(D);
+  if (rc) return rc;
+  if (shard_begin < 0 || shard_count < 1 || shard_begin + shard_count > D.dcp_size)
+    return set_error(DCPKV_EINVAL, "attn: shard range [%d, %d) outside [0, %d)", shard_begin,
+                     shard_begin + shard_count, D.dcp_size);
+  if (!q || !kv_pools || !block_tables || !seq_lens || !partial_out || !partial_lse || !workspace)
+    return set_error(DCPKV_EINVAL, "attn: NULL pointer argument");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return set_error(DCPKV_EINVAL, "attn: workspace must be 256-byte aligned");
+  if (D.kv_layout == DCPKV_LAYOUT_MLA && !kv_scales)
+    return set_error(DCPKV_EINVAL, "attn: MLA fp8 needs per-page scales");
+  Geometry g;
+  plan_geometry(D, total_tokens, device_cus(), g);
+  if (workspace_bytes < g.bytes)
+    return set_error(DCPKV_EINVAL, "attn: workspace %zu bytes < %zu needed", workspace_bytes,
+                     g.bytes);
+  AttnParams p = {};
+  p.q = q;
+  for (int d = shard_begin; d < shard_begin + shard_count; ++d) {
+    if (!kv_pools[d]) return set_error(DCPKV_EINVAL, "attn: pool %d is NULL", d);
+    p.pools[d] = static_cast<const uint8_t*>(kv_pools[d]);
+    if (D.kv_layout == DCPKV_LAYOUT_MLA) {
+      if (!kv_scales[d]) return set_error(DCPKV_EINVAL, "attn: scale array %d is NULL", d);
+      p.scales[d] = static_cast<const uint16_t*>(kv_scales[d]);
+    }
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.partial_out = partial_out;
+  p.partial_lse = partial_lse;
+  p.hdr = reinterpret_cast<PlanHeader*>(ws + g.hdr_off);
+  p.pairs = reinterpret_cast<PairPlan*>(ws + g.pairs_off);
+  p.ws_o = reinterpret_cast<float*>(ws + g.o_off);
+  p.ws_lse = reinterpret_cast<float*>(ws + g.lse_off);
+  p.ws_cap = g.ws_cap;
+  p.pages_per_layer = D.pages_per_layer;
+  p.page_bytes = page_bytes_of(D);
+  p.kv_dtype = D.kv_dtype;
+  p.layout = D.kv_layout;
+  p.q_dtype = D.q_dtype;
+  p.hq = D.num_q_heads;
+  p.hkv = D.num_kv_heads;
+  p.dqk = D.head_dim_qk;
+  p.dv = D.head_dim_v;
+  p.page_size = D.page_size;
+  p.n = D.dcp_size;
+  p.batch = D.batch;
+  p.q_len = D.q_len;
+  p.max_local = D.max_local_pages;
+  p.layer = D.layer;
+  p.shard_begin = shard_begin;
+  p.shard_count = shard_count;
+  p.chunk_pages = g.chunk_pages;
+  p.group = D.num_q_heads / D.num_kv_heads;
+  p.rows = g.rows;
+  p.hb_count = g.hb_count;
+  p.rb_rows = g.rb_rows;
+  p.rb_per_head = g.rb_per_head;
+  p.scale = D.softmax_scale;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int cus = device_cus();
+
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: plan launch: %s", hipGetErrorString(e));
+
+  // items: at most (pairs + local pages / C) chunks per head block
+  const int64_t pairs = (int64_t)shard_count * D.batch;
+  const int64_t est_pages = std::max<int64_t>(total_tokens, 0) / D.page_size + D.batch;
+  const int64_t item_bound = (pairs + est_pages / g.chunk_pages + 1) * g.hb_count;
+  rc = launch_partial(g.kind, p, D, cus, item_bound, st);
+  if (rc) return rc;
+
+  hipLaunchKernelGGL(chunk_reduce_kernel,
+                     dim3((unsigned)pairs, (unsigned)((g.rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock)),
+                     dim3(256), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: reduce launch: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}
+
+// Launch the generic kernel for this call (also the path for shapes the fast
+// kernels do not take).
+int dcpkv::launch_generic(const AttnParams& p, const dcp_attn_desc& D, int cus, int64_t item_bound,
+                          hipStream_t st) {
+  const int kind = D.kv_layout == DCPKV_LAYOUT_MLA ? 2 : (D.kv_dtype == DCPKV_KV_BF16 ? 1 : 0);
+  const size_t lds = generic_lds_bytes(kind, D.head_dim_qk, D.head_dim_v);
+  const int64_t grid = std::max<int64_t>(1, std::min<int64_t>(item_bound, (int64_t)cus * 2));
+  const bool qbf = D.q_dtype == DCPKV_Q_BF16;
+#define DCPKV_GEN(K, QT)                                                                        \
+  hipLaunchKernelGGL((partial_generic_kernel<K, QT>), dim3((unsigned)grid), dim3(kGenThreads), \
+                     lds, st, p)
+  if (kind == 0) {
+    if (qbf) DCPKV_GEN(0, uint16_t); else DCPKV_GEN(0, float);
+  } else if (kind == 1) {
+    if (qbf) DCPKV_GEN(1, uint16_t); else DCPKV_GEN(1, float);
+  } else {
+    if (qbf) DCPKV_GEN(2, uint16_t); else DCPKV_GEN(2, float);
+  }
+#undef DCPKV_GEN
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return set_error(DCPKV_EDEVICE, "attn: generic launch: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}
+
+extern "C" int dcp_lse_merge(int32_t dcp_size, int64_t rows, int32_t head_dim_v,
+                             const float* partial_out, const float* partial_lse, float* out,
+                             float* out_lse, void* stream) {
+  if (dcp_size < 1 || rows < 0 || head_dim_v < 1 || (rows > 0 && (!partial_out || !partial_lse || !out)))
+    return set_error(DCPKV_EINVAL, "merge: bad arguments (N=%d rows=%lld Dv=%d)", dcp_size,
+                     (long long)rows, head_dim_v);
+  if (rows == 0) return DCPKV_OK;
+  const int64_t blocks = (rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock;
+  if (blocks > INT32_MAX / 256) return set_error(DCPKV_EINVAL, "merge: too many rows");
+  hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), dcp_size, rows, head_dim_v, partial_out,
+                     partial_lse, out, out_lse);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "merge: launch failed: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}

@@ -1,0 +1,151 @@
+// Device-side pieces shared by the partial-attention kernels, the chunk
+// reduction and the cross-shard LSE merge.
+//
+// [2DR] = "Serving Macaron-V1 at Scale: Page-Level 2D KV Resharding";
+// [SGL] = "SGLang's path" (serving-k3, module 05).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "common.h"
+
+namespace dcpkv {
+
+constexpr float kNegInf = -INFINITY;
+
+// Work decomposition of one dcp_decode_partial call.
+//   pair  = (shard d, request b); its local pages are split into k chunks of
+//           at most chunk_pages pages (k = 1 when it fits or for empty pairs);
+//   item  = (pair, chunk, head block); a head block is a set of query rows
+//           that read the same KV head.
+// Pairs with k == 1 write their partial straight to partial_out; pairs with
+// k >= 2 write chunk partials to the workspace and a reduction kernel merges
+// them with the same LSE algebra as the cross-shard merge ([SGL]: the
+// combination is exact across tiles as across ranks).
+struct PairPlan {
+  int32_t chunk_begin;  // exclusive prefix sum of k over pairs
+  int32_t ws_begin;     // first workspace chunk slot (k >= 2), else -1
+  int32_t k;            // chunks of this pair
+  int32_t n_local;      // local pages of this pair
+};
+
+struct PlanHeader {
+  int32_t total_chunks;
+  int32_t ws_chunks;
+  int32_t fallback;  // 1 when the workspace could not hold the split and k = 1 was used
+  int32_t pad[13];
+};
+
+struct AttnParams {
+  const void* q;
+  const uint8_t* pools[kMaxShards];
+  const uint16_t* scales[kMaxShards];
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  float* partial_out;
+  float* partial_lse;
+  PlanHeader* hdr;
+  PairPlan* pairs;
+  float* ws_o;
+  float* ws_lse;
+  int64_t ws_cap;           // chunk partial slots in the workspace
+  int64_t pages_per_layer;  // M
+  int64_t page_bytes;
+  int32_t kv_dtype, layout, q_dtype;
+  int32_t hq, hkv, dqk, dv, page_size, n, batch, q_len, max_local, layer;
+  int32_t shard_begin, shard_count;
+  int32_t chunk_pages;  // C
+  int32_t group;        // Hq / Hkv
+  int32_t rows;         // q_len * Hq: query rows per pair
+  int32_t hb_count;     // head blocks per chunk
+  int32_t rb_rows;      // rows per head block
+  int32_t rb_per_head;  // head blocks per KV head
+  float scale;
+};
+
+__device__ __forceinline__ int32_t local_pages_of(int32_t seq_len, int32_t page_size, int32_t n,
+                                                  int32_t d, int32_t max_local) {
+  const int32_t pages = (seq_len + page_size - 1) / page_size;
+  const int32_t nl = pages > d ? (pages - 1 - d) / n + 1 : 0;
+  return nl < max_local ? nl : max_local;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One wavefront merges `count` partials of one row:
+//   m = max_i L_i, LSE = m + log sum_i exp(L_i - m), out = sum_i exp(L_i - LSE) O_i
+// ([2DR] section 5.2 for LSE; the O rule is the exact recombination of [SGL]).
+// Partial i's LSE is at lse[i * lse_stride], its output at o + i * o_stride.
+__device__ inline void wave_merge_row(int count, const float* __restrict__ lse, int64_t lse_stride,
+                                      const float* __restrict__ o, int64_t o_stride, int dv,
+                                      float* __restrict__ out, float* __restrict__ out_lse) {
+  const int lane = threadIdx.x & 63;
+  float m = kNegInf;
+  for (int i = lane; i < count; i += 64) m = fmaxf(m, lse[i * lse_stride]);
+  m = wave_max(m);
+  if (m == kNegInf) {
+    for (int c = lane; c < dv; c += 64) out[c] = 0.f;
+    if (lane == 0 && out_lse) *out_lse = kNegInf;
+    return;
+  }
+  float s = 0.f;
+  for (int i = lane; i < count; i += 64) {
+    const float l = lse[i * lse_stride];
+    s += (l == kNegInf) ? 0.f : expf(l - m);
+  }
+  s = wave_sum(s);
+  const float tot = m + logf(s);
+  if (lane == 0 && out_lse) *out_lse = tot;
+  if ((dv & 3) == 0 && (o_stride & 3) == 0) {
+    for (int c = lane * 4; c < dv; c += 256) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int i = 0; i < count; ++i) {
+        const float l = lse[i * lse_stride];
+        if (l == kNegInf) continue;
+        const float w = expf(l - tot);
+        const float4 x = *reinterpret_cast<const float4*>(o + i * o_stride + c);
+        acc.x += w * x.x;
+        acc.y += w * x.y;
+        acc.z += w * x.z;
+        acc.w += w * x.w;
+      }
+      *reinterpret_cast<float4*>(out + c) = acc;
+    }
+  } else {
+    for (int c = lane; c < dv; c += 64) {
+      float acc = 0.f;
+      for (int i = 0; i < count; ++i) {
+        const float l = lse[i * lse_stride];
+        if (l == kNegInf) continue;
+        acc += expf(l - tot) * o[i * o_stride + c];
+      }
+      out[c] = acc;
+    }
+  }
+}
+
+// Value of an OCP e4m3fn code (bias 7) computed exactly: the code's exponent
+// and mantissa bits placed in an IEEE half (bias 15) give the value / 2^8 for
+// normal and subnormal codes alike.  The NaN codes 0x7F/0xFF decode to +-480.
+__device__ __forceinline__ float e4m3fn_to_float(uint32_t b) {
+  const uint16_t h = (uint16_t)(((b & 0x80u) << 8) | ((b & 0x7Fu) << 7));
+  return (float)__builtin_bit_cast(_Float16, h) * 256.0f;
+}
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+}  // namespace dcpkv

@@ -1,0 +1,51 @@
+// Kernel choice for dcp_decode_partial.
+#include <cstdlib>
+
+#include "attn_kernels.h"
+
+namespace dcpkv {
+
+// DCPKV_FORCE_GENERIC=1 routes every call to the generic kernel (a debugging
+// aid for comparing kernels; it is still this library's own GPU code).
+static bool force_generic() {
+  const char* e = std::getenv("DCPKV_FORCE_GENERIC");
+  return e && e[0] == '1';
+}
+
+int choose_kernel(const dcp_attn_desc& D) {
+  (void)D;
+  if (force_generic()) return KK_GENERIC;
+  return KK_GENERIC;
+}
+
+int kernel_rows_per_block(int kind, const dcp_attn_desc& D) {
+  switch (kind) {
+    default:
+      return D.kv_layout == DCPKV_LAYOUT_MLA ? 8 : 16;
+  }
+}
+
+int kernel_items_per_cu(int kind) {
+  switch (kind) {
+    default:
+      return 4;
+  }
+}
+
+int kernel_min_chunk_pages(int kind, const dcp_attn_desc& D) {
+  (void)D;
+  switch (kind) {
+    default:
+      return 4;
+  }
+}
+
+int launch_partial(int kind, const AttnParams& p, const dcp_attn_desc& D, int cus,
+                   int64_t item_bound, hipStream_t st) {
+  switch (kind) {
+    default:
+      return launch_generic(p, D, cus, item_bound, st);
+  }
+}
+
+}  // namespace dcpkv

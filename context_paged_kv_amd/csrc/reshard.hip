@@ -1,0 +1,172 @@
+// Page-level 2D reshard ([2DR] = "Serving Macaron-V1 at Scale: Page-Level
+// 2D KV Resharding", sections 2, 4.1, 6.2-6.6).
+//
+// One launch moves one request's uncached pages over every (layer-split
+// source r, DCP destination d) path.  The grid is (entry, layer): each
+// workgroup copies one (layer, page) of page_bytes bytes.  The source-side
+// filter of section 6.2 is fused: the destination global page VALUE g picks
+// the shard (g mod N) and the local slot (g div N), pairing with the source
+// page id at the same list position (section 6.3).  Pages are streamed with
+// 16-byte lane loads, all of a thread's loads issued before its stores, and
+// non-temporal hints (the data is touched exactly once).
+
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace dcpkv {
+
+struct ReshardArgs {
+  const uint8_t* src[kMaxSources];
+  uint8_t* dst[kMaxShards];
+  const uint16_t* src_scale[kMaxSources];
+  uint16_t* dst_scale[kMaxShards];
+  const int32_t* src_ids;
+  const int64_t* dst_ids;
+  int32_t* bad;
+  int64_t page_bytes;
+  int64_t src_pages;   // S
+  int64_t dst_pages;   // M
+  int64_t first;       // first uncached entry
+  int32_t num_layers;
+  int32_t num_sources;
+  int32_t n;           // DCP size
+  int32_t dst_filter;
+  int32_t has_scales;
+};
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kReshardThreads = 256;
+constexpr int kReshardUnroll = 9;  // 256 x 9 x 16 B = one 36 KB fp8 latent page per round
+
+// Owner of `layer` under the section 4.1 split, and the first layer it owns.
+__device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_sources, int& r,
+                                            int& begin) {
+  const int base = num_layers / num_sources, extra = num_layers % num_sources;
+  const int big = extra * (base + 1);  // layers held by the sources with one extra layer
+  if (layer < big) {
+    r = layer / (base + 1);
+    begin = r * (base + 1);
+  } else {
+    r = extra + (layer - big) / base;
+    begin = r * base + extra;
+  }
+}
+
+__global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a) {
+  const int64_t i = a.first + blockIdx.x;
+  const int layer = blockIdx.y;
+  const int64_t g = a.dst_ids[i];
+  const int32_t sp = a.src_ids[i];
+  int d;
+  int64_t s;
+  if (a.n > 1) {
+    d = (int)(g % a.n);
+    s = g / a.n;
+  } else {
+    d = 0;
+    s = g;
+  }
+  const bool ok = g >= 0 && s < a.dst_pages && sp >= 0 && sp < a.src_pages;
+  if (!ok) {
+    if (threadIdx.x == 0 && a.bad) atomicAdd(a.bad, 1);
+    return;
+  }
+  if (a.dst_filter >= 0 && d != a.dst_filter) return;
+  int r, begin;
+  layer_owner(layer, a.num_layers, a.num_sources, r, begin);
+  const int64_t src_off = ((int64_t)(layer - begin) * a.src_pages + sp) * a.page_bytes;
+  const int64_t dst_off = ((int64_t)layer * a.dst_pages + s) * a.page_bytes;
+  const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(a.src[r] + src_off);
+  u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.dst[d] + dst_off);
+  const int64_t chunks = a.page_bytes >> 4;
+  for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kReshardThreads * kReshardUnroll) {
+    u32x4 v[kReshardUnroll];
+#pragma unroll
+    for (int u = 0; u < kReshardUnroll; ++u) {
+      const int64_t c = c0 + u * kReshardThreads + threadIdx.x;
+      if (c < chunks) v[u] = __builtin_nontemporal_load(src + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kReshardUnroll; ++u) {
+      const int64_t c = c0 + u * kReshardThreads + threadIdx.x;
+      if (c < chunks) __builtin_nontemporal_store(v[u], dst + c);
+    }
+  }
+  if (a.has_scales && threadIdx.x == 0) {
+    a.dst_scale[d][(int64_t)layer * a.dst_pages + s] =
+        a.src_scale[r][(int64_t)(layer - begin) * a.src_pages + sp];
+  }
+}
+
+}  // namespace dcpkv
+
+using namespace dcpkv;
+
+extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* src_pools,
+                                void* const* dst_pools, const void* const* src_scales,
+                                void* const* dst_scales, const int32_t* src_page_ids,
+                                const int64_t* dst_global_pages, int64_t num_pages,
+                                int64_t first_uncached, int32_t* bad_entries, void* stream) {
+  if (!desc || !src_pools || !dst_pools) return set_error(DCPKV_EINVAL, "reshard: NULL argument");
+  const kv_reshard_desc& D = *desc;
+  if (D.num_sources < 1 || D.num_sources > kMaxSources || D.num_layers < D.num_sources ||
+      D.num_layers > kMaxLayers || D.dcp_size < 1 || D.dcp_size > kMaxShards ||
+      D.dst_filter < -1 || D.dst_filter >= D.dcp_size || D.page_bytes <= 0 ||
+      D.page_bytes % 16 != 0 || D.src_pages < 1 || D.dst_pages < 1)
+    return set_error(DCPKV_EINVAL,
+                     "reshard: bad descriptor (N_cp=%d L=%d N=%d filter=%d page_bytes=%lld S=%lld "
+                     "M=%lld)",
+                     D.num_sources, D.num_layers, D.dcp_size, D.dst_filter,
+                     (long long)D.page_bytes, (long long)D.src_pages, (long long)D.dst_pages);
+  if (num_pages < 0 || first_uncached < 0 || first_uncached > num_pages)
+    return set_error(DCPKV_EINVAL, "reshard: first_uncached %lld outside [0, %lld]",
+                     (long long)first_uncached, (long long)num_pages);
+  if ((src_scales == nullptr) != (dst_scales == nullptr))
+    return set_error(DCPKV_EINVAL, "reshard: src_scales and dst_scales must both be set or NULL");
+  const int64_t work = num_pages - first_uncached;
+  if (work == 0) return DCPKV_OK;
+  if (!src_page_ids || !dst_global_pages)
+    return set_error(DCPKV_EINVAL, "reshard: NULL page id arrays");
+  // a dispatch dimension counts work-items in 32 bits: entries * 256 threads
+  if (work > (int64_t)(UINT32_MAX / kReshardThreads))
+    return set_error(DCPKV_EINVAL, "reshard: %lld pages exceed one call's limit", (long long)work);
+  ReshardArgs a = {};
+  for (int r = 0; r < D.num_sources; ++r) {
+    if (!src_pools[r] || !aligned16(src_pools[r]))
+      return set_error(DCPKV_EINVAL, "reshard: source pool %d is NULL or not 16-byte aligned", r);
+    a.src[r] = static_cast<const uint8_t*>(src_pools[r]);
+    if (src_scales) {
+      if (!src_scales[r]) return set_error(DCPKV_EINVAL, "reshard: source scale %d is NULL", r);
+      a.src_scale[r] = static_cast<const uint16_t*>(src_scales[r]);
+    }
+  }
+  for (int d = 0; d < D.dcp_size; ++d) {
+    if (!dst_pools[d] || !aligned16(dst_pools[d]))
+      return set_error(DCPKV_EINVAL, "reshard: destination pool %d is NULL or not 16-byte aligned",
+                       d);
+    a.dst[d] = static_cast<uint8_t*>(dst_pools[d]);
+    if (dst_scales) {
+      if (!dst_scales[d]) return set_error(DCPKV_EINVAL, "reshard: destination scale %d is NULL", d);
+      a.dst_scale[d] = static_cast<uint16_t*>(dst_scales[d]);
+    }
+  }
+  a.src_ids = src_page_ids;
+  a.dst_ids = dst_global_pages;
+  a.bad = bad_entries;
+  a.page_bytes = D.page_bytes;
+  a.src_pages = D.src_pages;
+  a.dst_pages = D.dst_pages;
+  a.first = first_uncached;
+  a.num_layers = D.num_layers;
+  a.num_sources = D.num_sources;
+  a.n = D.dcp_size;
+  a.dst_filter = D.dst_filter;
+  a.has_scales = src_scales != nullptr;
+  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)work, (unsigned)D.num_layers),
+                     dim3(kReshardThreads), 0, static_cast<hipStream_t>(stream), a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "reshard: launch failed: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}

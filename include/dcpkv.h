@@ -1,0 +1,259 @@
+/*
+ * dcpkv.h -- C ABI of the Decode Context Parallelism (DCP) paged-KV library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (cited by short name):
+ *   [2DR]  "Serving Macaron-V1 at Scale: Page-Level 2D KV Resharding"
+ *   [SGL]  "SGLang's path" (serving-k3, module 05, the DCP paragraph)
+ *
+ * Conventions shared by every entry point
+ *   - Status: 0 (DCPKV_OK) on success, a negative errno-style code on error.
+ *     Argument errors are detected on the host before anything is enqueued;
+ *     dcpkv_last_error() then returns a thread-local description.
+ *   - Device calls enqueue work on the caller's stream (a hipStream_t passed as
+ *     void*, NULL = the default stream) and return without waiting.  A failed
+ *     launch returns DCPKV_EDEVICE.  Faults surface at the caller's next
+ *     synchronisation.
+ *   - Memory: the caller owns every buffer (device pointers unless marked
+ *     "host").  Device calls never allocate; scratch space is the caller's
+ *     workspace.  The library owns only dcp_pagemap objects.
+ *   - Page contents are opaque bytes to the reshard.  Attention reads pages in
+ *     one of two layouts, both contiguous per (layer, page):
+ *       SPLIT: [2 (K, V)][num_kv_heads][page_size][head_dim], f32 or bf16
+ *       MLA:   [page_size][576] fp8 e4m3fn (512 latent + 64 rope), with one
+ *              bf16 scale per (layer, page) in a separate array.
+ *   - A DCP pool is [num_layers][pages_per_layer][page_bytes]; local slot s of
+ *     layer l lives at byte offset (l * pages_per_layer + s) * page_bytes.
+ *   - Not thread-safe per object; distinct objects/streams may be used from
+ *     distinct threads.
+ */
+#ifndef DCPKV_H
+#define DCPKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define DCPKV_API __attribute__((visibility("default")))
+#else
+#define DCPKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DCPKV_OK = 0,
+  DCPKV_EDEVICE = -5,   /* a HIP call or kernel launch failed */
+  DCPKV_ENOMEM = -12,   /* host allocation failed */
+  DCPKV_EINVAL = -22,   /* bad argument */
+  DCPKV_ENOSPC = -28,   /* page map exhausted */
+  DCPKV_ENOTSUP = -95   /* valid request this build does not implement */
+};
+
+enum { DCPKV_KV_F32 = 0, DCPKV_KV_BF16 = 1, DCPKV_KV_FP8E4M3 = 2 };
+enum { DCPKV_LAYOUT_SPLIT = 0, DCPKV_LAYOUT_MLA = 1 };
+enum { DCPKV_Q_F32 = 0, DCPKV_Q_BF16 = 1 };
+
+/* Thread-local text describing the last non-OK status returned on this thread. */
+DCPKV_API const char* dcpkv_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+DCPKV_API int dcpkv_abi_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Host-side geometry helpers                                                *
+ * ------------------------------------------------------------------------ */
+
+/* [2DR] section 4.1, layer-assignment equation.  Half-open range
+ * [*begin, *end) of layers owned by layer-split source r out of num_sources:
+ * floor(L / N_cp) layers each, the first (L mod N_cp) sources one more.
+ * EINVAL if num_layers < num_sources, num_sources < 1 or r out of range. */
+DCPKV_API int cp_layersplit_layer_range(int32_t num_layers, int32_t num_sources, int32_t r,
+                              int32_t* begin, int32_t* end);
+
+/* [2DR] section 6.2, page index filter.  Writes to out_local (host, capacity
+ * n) the local slots floor(p / N) of the pages p in kv_indices (host, n) with
+ * p mod N == dcp_rank, in input order, and their count to *out_count.  With
+ * dcp_size <= 1 the list is copied unchanged.  EINVAL on a negative index, a
+ * rank outside [0, N) or NULL pointers. */
+DCPKV_API int dcp_filter_kv_indices(const int64_t* kv_indices, int64_t n, int32_t dcp_size,
+                          int32_t dcp_rank, int64_t* out_local, int64_t* out_count);
+
+/* ------------------------------------------------------------------------ *
+ * Page map: free list and allocator ([2DR] sections 5.1 and 6.4)           *
+ * ------------------------------------------------------------------------ */
+
+typedef struct dcp_pagemap dcp_pagemap;
+
+/* An allocator of num_virtual_pages virtual pages (M), each covering
+ * page_size * dcp_size tokens: virtual page v is global pages v*N .. v*N+N-1,
+ * i.e. local slot v on every DCP rank (owner(p) = p mod N, slot = p div N).
+ * free_order (host, nullable): a permutation of [0, M) giving the initial
+ * free-list order (NULL = ascending).  The free list is FIFO: allocation
+ * takes from the front, release appends to the back.
+ * EINVAL on bad geometry or a free_order that is not a permutation;
+ * ENOMEM if the host object cannot be allocated. */
+DCPKV_API int dcp_pagemap_create(int32_t dcp_size, int32_t page_size, int64_t num_virtual_pages,
+                       const int64_t* free_order, dcp_pagemap** out);
+DCPKV_API void dcp_pagemap_destroy(dcp_pagemap* pm);
+
+/* Virtual pages currently on the free list (-1 if pm is NULL). */
+DCPKV_API int64_t dcp_pagemap_num_free(const dcp_pagemap* pm);
+
+/* Allocate a request of num_tokens (>= 1) tokens: P = ceil(T / page_size)
+ * pages from ceil(P / N) virtual pages v_0, v_1, ...; sequence page i gets
+ * global page v_{i div N} * N + (i mod N), so it lands on rank i mod N.
+ * Writes P ids to out_global_pages (host, capacity >= P).
+ * ENOSPC (and nothing allocated) if the free list is too short. */
+DCPKV_API int dcp_pagemap_alloc(dcp_pagemap* pm, int64_t num_tokens, int64_t* out_global_pages,
+                      int64_t capacity);
+
+/* Return the virtual pages behind a request's global pages (host, n) to the
+ * back of the free list.  EINVAL (nothing released) on an id out of range or
+ * a virtual page that is not allocated (double free). */
+DCPKV_API int dcp_pagemap_release(dcp_pagemap* pm, const int64_t* global_pages, int64_t n);
+
+/* Per-shard block tables for a batch ([2DR] section 5.1).  Request b's
+ * global pages are global_pages[page_offsets[b] .. page_offsets[b+1]) (host).
+ * out_tables (host, int32 [N][batch][max_local_pages]) receives, for shard d
+ * and request b, the local slots of the pages d owns in sequence order; unused
+ * entries are -1.  out_counts (host, int32 [N][batch], nullable) receives the
+ * number of pages per (d, b).  Requires the allocator's canonical placement:
+ * sequence page i must be owned by rank i mod N (EINVAL otherwise), which is
+ * what the attention kernels assume when they turn a local page index j of
+ * shard d back into sequence page j*N + d.  EINVAL if a count exceeds
+ * max_local_pages. */
+DCPKV_API int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int64_t* global_pages,
+                           const int64_t* page_offsets, int32_t max_local_pages,
+                           int32_t* out_tables, int32_t* out_counts);
+
+/* ------------------------------------------------------------------------ *
+ * (1) Page-level 2D reshard ([2DR] sections 2, 4.1, 6.2-6.6)               *
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t num_sources;  /* N_cp layer-split sources, >= 1 */
+  int32_t num_layers;   /* L, >= num_sources */
+  int32_t dcp_size;     /* N destination pools, >= 1 */
+  int32_t dst_filter;   /* -1: every destination; d: only pages owned by d */
+  int64_t page_bytes;   /* bytes per (layer, page); a multiple of 16 */
+  int64_t src_pages;    /* S: page slots per layer slot in each source pool */
+  int64_t dst_pages;    /* M: local page slots per layer in each destination */
+} kv_reshard_desc;
+
+/* One transfer of one request's pages over every (source r, destination d)
+ * path at once.  Source r holds the contiguous layer range of
+ * cp_layersplit_layer_range (section 4.1) in a pool of (|L_r| + 1) layer slots
+ * x S pages x page_bytes; the extra slot is the transient broadcast slot and is
+ * never read.  Destination d is a DCP pool [L][M][page_bytes].
+ *
+ * The i-th entry pairs source page src_page_ids[i] with destination global page
+ * dst_global_pages[i] (pairing by position).  Ownership is decided by the
+ * destination VALUE: d = g mod N, slot s = g div N (section 6.3); with N == 1
+ * the slot is g.  For every layer l (from its owner r) and every
+ * i in [first_uncached, num_pages):
+ *     dst[d][l][s] = src[r][l - begin_r][src_page_ids[i]]     (page_bytes bytes)
+ * Entries before first_uncached are prefix-cached: neither read nor written.
+ * No CP-side filtering happens under layer split (section 6.6).
+ *
+ * src_pools (host array [N_cp] of device pointers), dst_pools (host array [N]).
+ * src_scales / dst_scales (both NULL or both set): host arrays of device
+ * pointers to bf16 per-page scales, [|L_r|+1][S] and [L][M]; each scale moves
+ * with its page.  src_page_ids: device int32 [num_pages]; dst_global_pages:
+ * device int64 [num_pages].  Destination global pages must be unique within a
+ * call (each (layer, page) then has one writer).
+ * bad_entries (device int32 [1], nullable): incremented by one for each
+ * (layer, entry) whose ids fall outside [0, S) or [0, M*N); such entries are
+ * skipped, never written.  Pointers must be 16-byte aligned.
+ * EINVAL on a bad descriptor, NULL pool pointers, page_bytes % 16 != 0,
+ * first_uncached outside [0, num_pages] or misaligned pointers. */
+DCPKV_API int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* src_pools,
+                     void* const* dst_pools, const void* const* src_scales,
+                     void* const* dst_scales, const int32_t* src_page_ids,
+                     const int64_t* dst_global_pages, int64_t num_pages,
+                     int64_t first_uncached, int32_t* bad_entries, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * (2) Per-shard partial decode attention ([2DR] sections 5.2, 8; [SGL])    *
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t kv_dtype;        /* DCPKV_KV_* */
+  int32_t kv_layout;       /* DCPKV_LAYOUT_* (MLA requires FP8E4M3) */
+  int32_t q_dtype;         /* DCPKV_Q_* */
+  int32_t num_q_heads;     /* Hq */
+  int32_t num_kv_heads;    /* Hkv (MLA: 1); Hq % Hkv == 0 */
+  int32_t head_dim_qk;     /* SPLIT: D (== head_dim_v, <= 256); MLA: 576 */
+  int32_t head_dim_v;      /* SPLIT: D; MLA: 512 */
+  int32_t page_size;       /* tokens per page */
+  int32_t dcp_size;        /* N shards */
+  int32_t batch;           /* B requests */
+  int32_t q_len;           /* queries per request (1 = decode, >1 = draft verify) */
+  int32_t max_local_pages; /* row length of each block table */
+  int32_t layer;           /* layer to read from the pools, < num_layers */
+  int32_t num_layers;      /* L: layers in each pool */
+  int64_t pages_per_layer; /* M: local slots per layer in each pool */
+  float softmax_scale;     /* scores are softmax_scale * q . k */
+  float pad2_;
+} dcp_attn_desc;
+
+/* Workspace bytes dcp_decode_partial needs for this batch.  total_tokens is
+ * the sum of the batch's sequence lengths (a host-side figure that sizes the
+ * split of long sequences into chunks).  Returns 0 on a bad descriptor. */
+DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t total_tokens);
+
+/* For shards d in [shard_begin, shard_begin + shard_count), every request b,
+ * query t < q_len and head h:
+ *     pos_t = T_b - q_len + t  (T_b counts the q_len draft tokens, whose KV
+ *                               is already in the pools)
+ *     J     = { j <= pos_t : the page of token j is owned by shard d }
+ *     s_j   = softmax_scale * q[b][t][h] . k_j   (k, v of KV head h / (Hq/Hkv))
+ *     LSE_d = log sum_{j in J} exp(s_j)
+ *     O_d   = sum_{j in J} exp(s_j - LSE_d) v_j
+ * i.e. the shard's output normalised by its own denominator plus the
+ * log-sum-exp of its scores; exp(LSE_d) * O_d is the unnormalised weighted
+ * sum of [SGL].  An empty J gives O_d = 0, LSE_d = -inf.  MLA: k_j is the
+ * whole dequantised 576-d latent (code x page scale), v_j its first 512.
+ *
+ * q: [B][q_len][Hq][head_dim_qk] (f32 or bf16).  kv_pools: host array [N] of
+ * device pointers to DCP pools; kv_scales: host array [N] of device pointers
+ * to bf16 [L][M] page scales (MLA), else NULL.  block_tables: device int32
+ * [N][B][max_local_pages] as built by dcp_build_block_tables: entry j of
+ * (d, b) is the local slot of sequence page j*N + d.  seq_lens: device int32
+ * [B], each T_b >= q_len.  Out: partial_out fp32 [N][B][q_len][Hq][head_dim_v],
+ * partial_lse fp32 [N][B][q_len][Hq] (natural log); only the requested shards'
+ * slices are written.  workspace: device, >= dcp_decode_partial_workspace()
+ * bytes, 256-byte aligned; its contents need not be initialised.
+ * A table entry outside [0, M) is treated as a page of no tokens.
+ * EINVAL on a bad descriptor/pointer or too small a workspace; ENOTSUP for
+ * shapes no kernel here handles. */
+DCPKV_API int dcp_decode_partial(const dcp_attn_desc* desc, const void* q, const void* const* kv_pools,
+                       const void* const* kv_scales, const int32_t* block_tables,
+                       const int32_t* seq_lens, int64_t total_tokens, int32_t shard_begin,
+                       int32_t shard_count, float* partial_out, float* partial_lse,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * (3) Exact LSE merge over N partials ([2DR] section 5.2; [SGL])           *
+ * ------------------------------------------------------------------------ */
+
+/* For each of rows rows (rows = B * q_len * Hq when fed by
+ * dcp_decode_partial):
+ *     m   = max_d LSE_d
+ *     LSE = m + log sum_d exp(LSE_d - m)
+ *     out = sum_d exp(LSE_d - LSE) * O_d
+ * partial_out fp32 [N][rows][head_dim_v], partial_lse fp32 [N][rows];
+ * out fp32 [rows][head_dim_v]; out_lse fp32 [rows], nullable.  Rows whose
+ * every LSE_d is -inf give out = 0, LSE = -inf.  The result does not depend on
+ * the order of the shards beyond rounding.  out may not alias the inputs.
+ * EINVAL on bad sizes or NULL pointers. */
+DCPKV_API int dcp_lse_merge(int32_t dcp_size, int64_t rows, int32_t head_dim_v, const float* partial_out,
+                  const float* partial_lse, float* out, float* out_lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DCPKV_H */

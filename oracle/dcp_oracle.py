@@ -308,11 +308,12 @@ def query_positions(seq_len: int, q_len: int) -> List[int]:
 
 
 def request_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_len: int, scale: float,
-                      token_mask: Optional[np.ndarray] = None):
-    """Attention of one request, all heads and queries.
+                      token_mask: Optional[np.ndarray] = None, heads: Optional[Sequence[int]] = None):
+    """Attention of one request, all queries, all heads (or the listed ones).
 
     q: [q_len][Hq][Dqk]; k: [Hkv][T][Dqk]; v: [Hkv][T][Dv] (logical token order).
     token_mask: optional bool [T]: tokens this shard holds (None = all).
+    heads: optional subset of query heads to compute (others are left 0 / -inf).
     Returns O [q_len][Hq][Dv], LSE [q_len][Hq].
     """
     q_len, hq, _ = q.shape
@@ -325,7 +326,7 @@ def request_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_len: int,
         vis = t_all <= pos
         if token_mask is not None:
             vis = vis & token_mask[:seq_len]
-        for h in range(hq):
+        for h in (range(hq) if heads is None else heads):
             kh = h // group  # reading R10
             o, l = softmax_rows(q[t, h][None, :], k[kh, :seq_len], v[kh, :seq_len], vis[None, :], scale)
             out[t, h], lse[t, h] = o[0], l[0]
@@ -341,11 +342,12 @@ def shard_token_mask(global_pages: Sequence[int], page_size: int, seq_len: int, 
     return mask
 
 
-def request_partials(q, k, v, seq_len, scale, global_pages, page_size, n):
+def request_partials(q, k, v, seq_len, scale, global_pages, page_size, n, heads=None):
     """Per-shard partials of one request: O [N][q_len][Hq][Dv], LSE [N][q_len][Hq]."""
     outs, lses = [], []
     for d in range(n):
-        o, l = request_attention(q, k, v, seq_len, scale, shard_token_mask(global_pages, page_size, seq_len, n, d))
+        o, l = request_attention(q, k, v, seq_len, scale, shard_token_mask(global_pages, page_size, seq_len, n, d),
+                                 heads)
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)

@@ -1,0 +1,357 @@
+"""Test harness: builds device inputs for a workload, runs the HIP path through
+the C ABI and computes the oracle's expectation on the same inputs.
+
+Inputs come from workloads.gen (seeded); the page map and block tables come
+from the library (host code under test, checked against the oracle's own page
+map); the oracle reads the inputs only (never a kernel output).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+import context_paged_kv_amd as K
+import oracle as O
+from workloads import gen
+from workloads.configs import MLA_DIM, Workload
+
+
+def kv_dtype_code(w: Workload) -> int:
+    return {"f32": K.KV_F32, "bf16": K.KV_BF16, "fp8": K.KV_FP8E4M3}[w.kv_dtype]
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# decode inputs
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class DecodeCase:
+    w: Workload
+    seq_lens: np.ndarray
+    pages: List[np.ndarray]            # global pages per request (library page map)
+    max_local: int
+    tables: np.ndarray                 # [N][B][max_local]
+    pools: List[torch.Tensor]          # per shard uint8 [L][M][page_bytes]
+    scales: Optional[List[torch.Tensor]]  # per shard int16 [L][M]
+    q: torch.Tensor                    # [B][q_len][Hq][Dqk]
+    bt_dev: torch.Tensor
+    sl_dev: torch.Tensor
+    layer: int = 0
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.seq_lens.sum())
+
+
+def page_map_pages(w: Workload, seq_lens: Sequence[int], check_oracle: bool = True) -> List[np.ndarray]:
+    free = gen.draw_free_order(w)
+    pm = K.PageMap(w.dcp_size, w.page_size, w.pool_pages, free)
+    pages = [pm.alloc(int(t)) for t in seq_lens]
+    pm.close()
+    if check_oracle:  # host page map vs the oracle's, bit for bit
+        opm = O.PageMap(w.dcp_size, w.page_size, w.pool_pages, free)
+        for t, g in zip(seq_lens, pages):
+            assert list(g) == opm.alloc(int(t))
+    return pages
+
+
+def alloc_pools(w: Workload, device, fill: str = "random", tag: str = "pool"):
+    n, L, M, pb = w.dcp_size, w.num_layers, w.pool_pages, w.page_bytes
+    pools, scales = [], [] if w.has_scales else None
+    for d in range(n):
+        p = torch.empty((L, M, pb), dtype=torch.uint8, device=device)
+        s = torch.empty((L, M), dtype=torch.int16, device=device) if w.has_scales else None
+        if fill == "random":
+            gen.fill_pages_(p.view(L * M, pb), w, tag, sub=d, scales=None if s is None else s.view(-1))
+        else:
+            gen.sentinel_fill_(p, gen.DST_SENTINEL)
+            if s is not None:
+                s.fill_(gen.SCALE_SENTINEL)
+        pools.append(p)
+        if s is not None:
+            scales.append(s)
+    return pools, scales
+
+
+def make_decode_case(w: Workload, device="cuda", seq_lens=None, pools=None, scales=None) -> DecodeCase:
+    sl = gen.draw_seq_lens(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
+    assert len(sl) == w.num_requests
+    pages = page_map_pages(w, sl)
+    max_local = max(1, max(-(-len(p) // w.dcp_size) for p in pages))
+    tables, counts = K.dcp_build_block_tables(w.dcp_size, pages, max_local)
+    if pools is None:
+        pools, scales = alloc_pools(w, device)
+    q = gen.draw_q(w, device)
+    return DecodeCase(w=w, seq_lens=sl, pages=pages, max_local=max_local, tables=tables, pools=pools,
+                      scales=scales, q=q, bt_dev=torch.from_numpy(tables).to(device),
+                      sl_dev=torch.from_numpy(sl.astype(np.int32)).to(device), layer=w.attn_layer)
+
+
+def attn_desc(case: DecodeCase, layer: Optional[int] = None):
+    w = case.w
+    return K.make_attn_desc(
+        kv_dtype=kv_dtype_code(w), kv_layout=K.LAYOUT_MLA if w.layout == "mla" else K.LAYOUT_SPLIT,
+        q_dtype=K.Q_BF16 if w.q_dtype == "bf16" else K.Q_F32, num_q_heads=w.num_q_heads,
+        num_kv_heads=w.num_kv_heads, head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
+        page_size=w.page_size, dcp_size=w.dcp_size, batch=w.num_requests, q_len=w.q_len,
+        max_local_pages=case.max_local, layer=case.layer if layer is None else layer, num_layers=w.num_layers,
+        pages_per_layer=w.pool_pages, softmax_scale=w.softmax_scale)
+
+
+@dataclass
+class DecodeOut:
+    partial_out: torch.Tensor
+    partial_lse: torch.Tensor
+    out: torch.Tensor
+    lse: torch.Tensor
+
+
+def alloc_outputs(case: DecodeCase):
+    w = case.w
+    dev = case.q.device
+    B, ql, hq, dv, n = w.num_requests, w.q_len, w.num_q_heads, w.head_dim_v, w.dcp_size
+    desc = attn_desc(case)
+    ws = torch.empty(K.dcp_decode_partial_workspace(desc, case.total_tokens), dtype=torch.uint8, device=dev)
+    return DecodeOut(
+        partial_out=torch.full((n, B, ql, hq, dv), float("nan"), dtype=torch.float32, device=dev),
+        partial_lse=torch.full((n, B, ql, hq), float("nan"), dtype=torch.float32, device=dev),
+        out=torch.full((B, ql, hq, dv), float("nan"), dtype=torch.float32, device=dev),
+        lse=torch.full((B, ql, hq), float("nan"), dtype=torch.float32, device=dev)), ws
+
+
+def run_decode(case: DecodeCase, outs: Optional[DecodeOut] = None, ws=None, layer=None,
+               shard_begin=0, shard_count=None, merge=True) -> DecodeOut:
+    w = case.w
+    if outs is None:
+        outs, ws = alloc_outputs(case)
+    desc = attn_desc(case, layer)
+    K.dcp_decode_partial(desc, q=case.q, kv_pools=case.pools, kv_scales=case.scales, block_tables=case.bt_dev,
+                         seq_lens=case.sl_dev, total_tokens=case.total_tokens, partial_out=outs.partial_out,
+                         partial_lse=outs.partial_lse, workspace=ws, shard_begin=shard_begin,
+                         shard_count=shard_count)
+    if merge:
+        rows = w.num_requests * w.q_len * w.num_q_heads
+        K.dcp_lse_merge(w.dcp_size, rows, w.head_dim_v, outs.partial_out, outs.partial_lse, outs.out, outs.lse)
+    return outs
+
+
+# ---------------------------------------------------------------------------
+# oracle side
+# ---------------------------------------------------------------------------
+
+
+def gather_request_pages(pools, scales, pages, n: int, layer: int):
+    """Host copies of one request's pages (and scales) in sequence order."""
+    dev = pools[0].device
+    owners = np.array([O.dcp_owner(int(g), n) for g in pages])
+    slots = np.array([O.dcp_local_slot(int(g), n) for g in pages])
+    pb = pools[0].shape[-1]
+    out = np.empty((len(pages), pb), dtype=np.uint8)
+    sc = np.empty(len(pages), dtype=np.int64) if scales is not None else None
+    for d in range(n):
+        idx = np.nonzero(owners == d)[0]
+        if idx.size == 0:
+            continue
+        sl = torch.from_numpy(slots[idx]).to(dev)
+        out[idx] = pools[d][layer].index_select(0, sl).cpu().numpy()
+        if scales is not None:
+            sc[idx] = scales[d][layer].index_select(0, sl).cpu().numpy().astype(np.int64) & 0xFFFF
+    return out, sc
+
+
+def oracle_logical_kv(w: Workload, page_bytes: np.ndarray, page_scales, seq_len: int):
+    """Logical K, V of one request from its pages (host bytes, sequence order), decoded by the oracle."""
+    if w.layout == "mla":
+        lat = np.concatenate([O.decode_mla_page(page_bytes[i], int(page_scales[i]), w.page_size)
+                              for i in range(len(page_bytes))], axis=0)[:seq_len]
+        return lat[None], lat[None, :, :w.head_dim_v]
+    ks, vs = zip(*[O.decode_split_page(page_bytes[i], w.kv_dtype, w.num_kv_heads, w.page_size, w.head_dim_qk)
+                   for i in range(len(page_bytes))])
+    return np.concatenate(ks, axis=1)[:, :seq_len], np.concatenate(vs, axis=1)[:, :seq_len]
+
+
+def q_host(case: DecodeCase, b: int) -> np.ndarray:
+    return case.q[b].float().cpu().numpy().astype(np.float64)
+
+
+def oracle_request(case: DecodeCase, b: int, heads=None, kv=None, layer=None):
+    """(partials O [N][q_len][Hq][Dv], LSE [N][q_len][Hq]), (unsharded O, LSE) for request b."""
+    w = case.w
+    lay = case.layer if layer is None else layer
+    if kv is None:
+        pb, ps = gather_request_pages(case.pools, case.scales, case.pages[b], w.dcp_size, lay)
+        kv = oracle_logical_kv(w, pb, ps, int(case.seq_lens[b]))
+    k, v = kv
+    q = q_host(case, b)
+    T = int(case.seq_lens[b])
+    po, pl = O.request_partials(q, k, v, T, w.softmax_scale, case.pages[b], w.page_size, w.dcp_size, heads)
+    uo, ul = O.request_attention(q, k, v, T, w.softmax_scale, None, heads)
+    return (po, pl), (uo, ul)
+
+
+def rel_row_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-row relative L2 error ||got - ref|| / ||ref|| over the last axis (0 when both are 0)."""
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def lse_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    both_inf = np.isneginf(got) & np.isneginf(ref)
+    return np.where(both_inf, 0.0, np.abs(got - ref))
+
+
+def check_rows(name, got_o, got_l, ref_o, ref_l, tol_o, tol_l):
+    eo = rel_row_err(np.asarray(got_o, np.float64), ref_o)
+    el = lse_err(np.asarray(got_l, np.float64), ref_l)
+    assert np.isfinite(eo).all(), f"{name}: non-finite output error"
+    assert eo.max() <= tol_o, f"{name}: max relative row error {eo.max():.3e} > {tol_o}"
+    assert el.max() <= tol_l, f"{name}: max |LSE error| {el.max():.3e} > {tol_l}"
+    return float(eo.max()), float(el.max())
+
+
+def tolerance(w: Workload):
+    # the stated bars: 1e-5 for fp32, 2e-3 relative for bf16 / fp8
+    return (1e-5, 1e-5) if w.kv_dtype == "f32" else (2e-3, 2e-3)
+
+
+def check_decode(case: DecodeCase, outs: DecodeOut, requests=None, heads=None, shards=None):
+    """Compare partials, merged output and LSE with the oracle for the listed requests/heads."""
+    w = case.w
+    tol_o, tol_l = tolerance(w)
+    n = w.dcp_size
+    shards = range(n) if shards is None else shards
+    hs = list(range(w.num_q_heads)) if heads is None else list(heads)
+    worst = [0.0, 0.0]
+    for b in (range(w.num_requests) if requests is None else requests):
+        (po, pl), (uo, ul) = oracle_request(case, b, heads=hs)
+        for d in shards:
+            e = check_rows(f"partial d={d} b={b}", outs.partial_out[d, b][:, hs].cpu().numpy(),
+                           outs.partial_lse[d, b][:, hs].cpu().numpy(), po[d][:, hs], pl[d][:, hs], tol_o, tol_l)
+            worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+        if shards == range(n):
+            e = check_rows(f"merged b={b}", outs.out[b][:, hs].cpu().numpy(), outs.lse[b][:, hs].cpu().numpy(),
+                           uo[:, hs], ul[:, hs], tol_o, tol_l)
+            worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+    return worst
+
+
+# ---------------------------------------------------------------------------
+# reshard inputs
+# ---------------------------------------------------------------------------
+
+
+@dataclass
+class ReshardCase:
+    w: Workload
+    num_layers: int
+    num_sources: int
+    src_pools: List[torch.Tensor]            # [|L_r|+1][S][pb]
+    src_scales: Optional[List[torch.Tensor]]  # [|L_r|+1][S]
+    dst_pools: List[torch.Tensor]            # [L][M][pb]
+    dst_scales: Optional[List[torch.Tensor]]
+    src_ids: np.ndarray                      # per entry
+    dst_ids: np.ndarray                      # per entry (global pages)
+    first_uncached: int
+    src_pages: int
+
+
+def make_source_pools(w: Workload, num_sources: int, S: int, device, tag="src"):
+    pools, scales = [], [] if w.has_scales else None
+    pb = w.page_bytes
+    for r in range(num_sources):
+        a, b = K.cp_layersplit_layer_range(w.num_layers, num_sources, r)
+        slots = (b - a) + 1
+        p = torch.empty((slots, S, pb), dtype=torch.uint8, device=device)
+        s = torch.empty((slots, S), dtype=torch.int16, device=device) if w.has_scales else None
+        gen.fill_pages_(p[:-1].reshape((slots - 1) * S, pb), w, tag, sub=r,
+                        scales=None if s is None else s[:-1].reshape(-1))
+        gen.sentinel_fill_(p[-1], gen.SRC_TRANSIENT_SENTINEL)  # transient slot: never read
+        if s is not None:
+            s[-1].fill_(gen.SCALE_SENTINEL)
+        pools.append(p)
+        if s is not None:
+            scales.append(s)
+    return pools, scales
+
+
+def make_reshard_case(w: Workload, device="cuda", seq_lens=None, requests=None, first_uncached=None,
+                      dst_pools=None, dst_scales=None) -> ReshardCase:
+    """One transfer: the listed requests' pages (concatenated) from the layer-split sources."""
+    sl = gen.draw_seq_lens(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
+    pages = page_map_pages(w, sl)
+    reqs = range(len(sl)) if requests is None else requests
+    dst_ids = np.concatenate([pages[b] for b in reqs]).astype(np.int64)
+    P = len(dst_ids)
+    S = P
+    src_ids = gen.draw_src_order(w, S)[:P].astype(np.int64)
+    src_pools, src_scales = make_source_pools(w, w.num_sources, S, device)
+    if dst_pools is None:
+        dst_pools, dst_scales = alloc_pools(w, device, fill="sentinel")
+    c = int(math.floor(w.cached_frac * P)) if first_uncached is None else first_uncached
+    return ReshardCase(w=w, num_layers=w.num_layers, num_sources=w.num_sources, src_pools=src_pools,
+                       src_scales=src_scales, dst_pools=dst_pools, dst_scales=dst_scales, src_ids=src_ids,
+                       dst_ids=dst_ids, first_uncached=c, src_pages=S)
+
+
+def run_reshard(rc: ReshardCase, dst_filter=-1, bad=None, src_ids=None, dst_ids=None, stream=None):
+    w = rc.w
+    dev = rc.src_pools[0].device
+    si = torch.from_numpy((rc.src_ids if src_ids is None else src_ids).astype(np.int32)).to(dev)
+    di = torch.from_numpy((rc.dst_ids if dst_ids is None else dst_ids).astype(np.int64)).to(dev)
+    K.kv_reshard_pages(num_layers=rc.num_layers, dcp_size=w.dcp_size, page_bytes=w.page_bytes,
+                       src_pages=rc.src_pages, dst_pages=w.pool_pages, src_pools=rc.src_pools,
+                       dst_pools=rc.dst_pools, src_page_ids=si, dst_global_pages=di,
+                       first_uncached=rc.first_uncached, dst_filter=dst_filter, src_scales=rc.src_scales,
+                       dst_scales=rc.dst_scales, bad_entries=bad, stream=stream)
+    return si, di
+
+
+def check_reshard_by_plan(rc: ReshardCase, dst_filter=-1, sentinel=gen.DST_SENTINEL):
+    """Bit-exact check of every destination page against the oracle's copy plan.
+
+    The plan (which source page lands where) is the oracle's; the byte compare
+    runs on the device with torch indexing.  Pages outside the plan must still
+    hold the sentinel; sources must be unchanged (checked by the caller)."""
+    w = rc.w
+    n, L, M = w.dcp_size, rc.num_layers, w.pool_pages
+    plan = O.reshard_plan(L, rc.num_sources, n, rc.src_ids, rc.dst_ids, rc.first_uncached, dst_filter)
+    dev = rc.dst_pools[0].device
+    arr = np.asarray(plan, dtype=np.int64).reshape(-1, 6)
+    touched = [np.zeros((L, M), dtype=bool) for _ in range(n)]
+    for d in range(n):
+        sel = arr[arr[:, 3] == d]
+        touched[d][sel[:, 4], sel[:, 5]] = True
+        for r in range(rc.num_sources):
+            s2 = sel[sel[:, 0] == r]
+            if s2.size == 0:
+                continue
+            for start in range(0, len(s2), 4096):
+                blk = s2[start:start + 4096]
+                src_flat = rc.src_pools[r].view(-1, w.page_bytes)
+                dst_flat = rc.dst_pools[d].view(-1, w.page_bytes)
+                si = torch.from_numpy(blk[:, 1] * rc.src_pages + blk[:, 2]).to(dev)
+                di = torch.from_numpy(blk[:, 4] * M + blk[:, 5]).to(dev)
+                want = src_flat.index_select(0, si)
+                got = dst_flat.index_select(0, di)
+                assert torch.equal(got, want), f"page bytes differ (d={d}, source {r})"
+                if rc.src_scales is not None:
+                    assert torch.equal(rc.dst_scales[d].view(-1).index_select(0, di),
+                                       rc.src_scales[r].view(-1).index_select(0, si)), "scales differ"
+        for layer in range(L):
+            mask = torch.from_numpy(~touched[d][layer]).to(dev)
+            rest = rc.dst_pools[d][layer][mask]
+            assert bool((rest == sentinel).all()), f"untouched pages of d={d} layer={layer} changed"
+            if rc.dst_scales is not None:
+                assert bool((rc.dst_scales[d][layer][mask] == gen.SCALE_SENTINEL).all())
+    return len(plan)

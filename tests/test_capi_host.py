@@ -1,0 +1,147 @@
+"""C-ABI library on the CPU: exported symbols, host logic against the oracle,
+and argument errors that return before anything reaches a GPU."""
+
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import context_paged_kv_amd as K
+import oracle as O
+from context_paged_kv_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dcpkv.h")
+
+
+def declared_symbols():
+    txt = open(HEADER).read()
+    return re.findall(r"^DCPKV_API[^;(]*?\b(\w+)\s*\(", txt, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 14
+    lib = C.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+    assert K.dcpkv_abi_version() == 1
+
+
+@pytest.mark.parametrize("L_,n", [(78, 8), (64, 4), (4, 4), (17, 5), (1, 1), (100, 7)])
+def test_layer_range_matches_oracle(L_, n):
+    for r in range(n):
+        assert K.cp_layersplit_layer_range(L_, n, r) == O.layer_range(L_, n, r)
+
+
+def test_layer_range_errors():
+    for args in [(3, 8, 0), (8, 0, 0), (8, 4, 4), (8, 4, -1)]:
+        with pytest.raises(L.DcpkvError) as e:
+            K.cp_layersplit_layer_range(*args)
+        assert e.value.code == L.DCPKV_EINVAL
+
+
+def test_filter_matches_oracle():
+    rng = np.random.default_rng(2)
+    idx = rng.permutation(500)[:300]
+    for n in (1, 2, 4, 8):
+        for d in range(n):
+            assert list(K.dcp_filter_kv_indices(idx, n, d)) == O.filter_kv_indices_for_dcp_rank(idx, n, d)
+    assert len(K.dcp_filter_kv_indices(range(256), 4, 3)) == 64
+    with pytest.raises(L.DcpkvError):
+        K.dcp_filter_kv_indices([1, -2], 4, 0)
+    with pytest.raises(L.DcpkvError):
+        K.dcp_filter_kv_indices([1, 2], 4, 4)
+
+
+@pytest.mark.parametrize("n,page,M", [(1, 16, 40), (2, 16, 64), (4, 64, 97), (8, 64, 300)])
+def test_pagemap_matches_oracle(n, page, M):
+    rng = np.random.default_rng(n * 1000 + M)
+    free = rng.permutation(M)
+    pm = K.PageMap(n, page, M, free)
+    om = O.PageMap(n, page, M, free)
+    live = []
+    for step in range(60):
+        if live and rng.random() < 0.35:
+            g = live.pop(int(rng.integers(len(live))))
+            pm.release(g)
+            om.release(list(g))
+        else:
+            T = int(rng.integers(1, page * n * 6))
+            try:
+                want = om.alloc(T)
+            except MemoryError:
+                with pytest.raises(L.DcpkvError) as e:
+                    pm.alloc(T)
+                assert e.value.code == L.DCPKV_ENOSPC
+                continue
+            got = pm.alloc(T)
+            assert list(got) == want
+            live.append(got)
+        assert pm.num_free() == len(om.free)
+
+
+def test_pagemap_errors():
+    with pytest.raises(L.DcpkvError):
+        K.PageMap(0, 64, 10)
+    with pytest.raises(L.DcpkvError):
+        K.PageMap(4, 64, 3, [0, 0, 1])
+    pm = K.PageMap(2, 4, 4)
+    g = pm.alloc(9)
+    pm.release(g)
+    with pytest.raises(L.DcpkvError):  # double free
+        pm.release(g)
+    with pytest.raises(L.DcpkvError):
+        pm.release([10**6])
+    with pytest.raises(L.DcpkvError):
+        pm.alloc(0)
+
+
+def test_block_tables_match_oracle():
+    rng = np.random.default_rng(5)
+    n, page, M = 4, 16, 200
+    om = O.PageMap(n, page, M, rng.permutation(M))
+    pages = [om.alloc(int(t)) for t in rng.integers(1, 600, size=9)]
+    mx = max(-(-len(p) // n) for p in pages) + 2
+    tables, counts = K.dcp_build_block_tables(n, pages, mx)
+    want = O.block_tables(pages, n)
+    for d in range(n):
+        for b in range(len(pages)):
+            c = counts[d, b]
+            assert list(tables[d, b, :c]) == want[d][b]
+            assert (tables[d, b, c:] == -1).all()
+    # placement where sequence page i is not on rank i mod N is rejected
+    with pytest.raises(L.DcpkvError):
+        K.dcp_build_block_tables(4, [[1, 0, 2, 3]], 4)
+    with pytest.raises(L.DcpkvError):  # too narrow
+        K.dcp_build_block_tables(n, pages, 1)
+
+
+def test_device_entry_points_reject_bad_arguments_on_host():
+    d = L.kv_reshard_desc(1, 1, 2, -1, 100, 4, 4)  # page_bytes not a multiple of 16
+    p = (C.c_void_p * 2)(16, 16)
+    rc = L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, C.c_void_p(16), C.c_void_p(16), 4, 0, None, None)
+    assert rc == L.DCPKV_EINVAL and "page_bytes" in K.dcpkv_last_error()
+    d = L.kv_reshard_desc(2, 1, 2, -1, 64, 4, 4)  # fewer layers than sources
+    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 0, None, None) == L.DCPKV_EINVAL
+    d = L.kv_reshard_desc(1, 1, 2, -1, 64, 4, 4)
+    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 5, None, None) == L.DCPKV_EINVAL
+    # nothing to copy is a no-op success even without a GPU
+    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 4, None, None) == 0
+    assert L._lib.dcp_lse_merge(0, 4, 4, None, None, None, None, None) == L.DCPKV_EINVAL
+    assert L._lib.dcp_lse_merge(2, 0, 4, None, None, None, None, None) == 0
+    good = K.make_attn_desc(kv_dtype=K.KV_BF16, kv_layout=K.LAYOUT_SPLIT, q_dtype=K.Q_BF16, num_q_heads=32,
+                            num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64, dcp_size=4, batch=2,
+                            q_len=1, max_local_pages=4, layer=0, num_layers=1, pages_per_layer=16, softmax_scale=0.1)
+    assert K.dcp_decode_partial_workspace(good, 1000) > 0
+    bad = K.make_attn_desc(kv_dtype=K.KV_FP8E4M3, kv_layout=K.LAYOUT_SPLIT, q_dtype=K.Q_BF16, num_q_heads=32,
+                           num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64, dcp_size=4, batch=2,
+                           q_len=1, max_local_pages=4, layer=0, num_layers=1, pages_per_layer=16, softmax_scale=0.1)
+    assert L._lib.dcp_decode_partial_workspace(C.byref(bad), 1000) == 0
+    rc = L._lib.dcp_decode_partial(C.byref(good), None, None, None, None, None, 0, 0, 4, None, None, None, 0, None)
+    assert rc == L.DCPKV_EINVAL
+    rc = L._lib.dcp_decode_partial(C.byref(good), C.c_void_p(256), p, None, C.c_void_p(256), C.c_void_p(256), 0,
+                                   2, 3, C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1 << 30, None)
+    assert rc == L.DCPKV_EINVAL and "shard range" in K.dcpkv_last_error()

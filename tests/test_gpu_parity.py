@@ -1,0 +1,212 @@
+"""GPU parity of the HIP path against the float64 oracle at sizes the oracle
+finishes in seconds: several tiles, ragged last pages, empty shards, causal
+drafts.  Reshards must match bit for bit; attention within the stated
+tolerance (1e-5 fp32, 2e-3 relative bf16/fp8)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import context_paged_kv_amd as K
+import oracle as O
+from tests import harness as H
+from workloads import gen
+from workloads.configs import get_workload, scaled
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+# --------------------------------------------------------------------------- decode
+
+
+def test_decode_tiny_fp32_full():
+    w = get_workload("tiny_fp32")
+    H.log("decode tiny_fp32: B=1 T=1000 page 16 N=2 fp32")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs)
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("seed_shift", [0, 1])
+def test_decode_gqa_bf16_small(seed_shift):
+    base = get_workload("gqa_bf16_16x4k-32k")
+    w = scaled(base, seed=base.seed + 100 + seed_shift, seq_segments=((5, 70, 3000),), pool_pages=256)
+    H.log(f"decode gqa bf16 small seed {w.seed}")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs)
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+def test_decode_mla_fp8_small():
+    base = get_workload("mla_fp8_48x100k")
+    w = scaled(base, seed=base.seed + 100, seq_segments=((3, 200, 5000),), pool_pages=512)
+    H.log("decode mla fp8 small q_len 1")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs)
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+def test_decode_mla_fp8_verify_small():
+    base = get_workload("mla_fp8_longmix_verify")
+    w = scaled(base, seed=base.seed + 100, seq_segments=((2, 3000, 9000), (3, 2048, 2048)),
+               pool_pages=512, num_layers=2, attn_layer=1)
+    H.log("decode mla fp8 small q_len 4 causal, layer 1 of 2")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs)
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "gqa_bf16_16x4k-32k", "mla_fp8_longmix_verify"])
+def test_decode_edge_lengths(name):
+    # T = q_len (only the drafts), T = 1 page + 1 token, lengths below N pages (empty shards)
+    base = get_workload(name)
+    ql = base.q_len
+    lens = [ql, base.page_size + 1, 2 * base.page_size - 1, 3]
+    lens = [max(ql, t) for t in lens]
+    w = scaled(base, seed=base.seed + 200, seq_segments=tuple((1, t, t) for t in lens), pool_pages=64,
+               num_layers=1, attn_layer=0)
+    H.log(f"decode edge lengths {name}: {lens}")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    _sync()
+    H.check_decode(case, outs)
+    # shards that own no page of a request give (0, -inf)
+    for b, t in enumerate(lens):
+        pages = -(-t // w.page_size)
+        for d in range(pages, w.dcp_size):
+            assert torch.isneginf(outs.partial_lse[d, b]).all()
+            assert (outs.partial_out[d, b] == 0).all()
+
+
+def test_decode_shard_subset_calls():
+    # partials computed one shard range at a time equal the all-shard call
+    base = get_workload("gqa_bf16_16x4k-32k")
+    w = scaled(base, seed=base.seed + 300, seq_segments=((3, 500, 2500),), pool_pages=128)
+    case = H.make_decode_case(w, DEV)
+    full = H.run_decode(case)
+    part, ws = H.alloc_outputs(case)
+    H.run_decode(case, part, ws, shard_begin=0, shard_count=1, merge=False)
+    H.run_decode(case, part, ws, shard_begin=1, shard_count=3, merge=False)
+    _sync()
+    assert torch.equal(part.partial_out, full.partial_out)
+    assert torch.equal(part.partial_lse, full.partial_lse)
+
+
+# --------------------------------------------------------------------------- merge
+
+
+@pytest.mark.parametrize("n,rows,dv", [(1, 7, 64), (2, 33, 128), (8, 100, 512), (5, 9, 10)])
+def test_lse_merge_vs_oracle(n, rows, dv):
+    g = torch.Generator().manual_seed(n * 1000 + rows)
+    po = torch.randn((n, rows, dv), generator=g)
+    pl = torch.randn((n, rows), generator=g) * 5
+    pl[0, : rows // 3] = float("-inf")          # some shards empty
+    if n > 1:
+        pl[:, rows - 1] = float("-inf")         # a row with nothing anywhere
+        po[:, rows - 1] = 0
+    out = torch.empty((rows, dv), device=DEV)
+    lse = torch.empty((rows,), device=DEV)
+    K.dcp_lse_merge(n, rows, dv, po.to(DEV), pl.to(DEV), out, lse)
+    _sync()
+    ro, rl = O.lse_merge(po.double().numpy(), pl.double().numpy())
+    H.check_rows("merge", out.cpu().numpy(), lse.cpu().numpy(), ro, rl, 1e-6, 1e-6)
+    if n > 1:
+        assert torch.isneginf(lse[rows - 1]) and (out[rows - 1] == 0).all()
+
+
+# --------------------------------------------------------------------------- reshard
+
+
+def _host_pools(ts):
+    return [t.cpu().numpy() for t in ts]
+
+
+def test_reshard_tiny_fp32_full_oracle():
+    w = get_workload("tiny_fp32")
+    H.log("reshard tiny_fp32: 1 source, 1 layer, N=2")
+    rc = H.make_reshard_case(w, DEV)
+    src_before = [t.clone() for t in rc.src_pools]
+    dst_host = _host_pools(rc.dst_pools)
+    sent = O.reshard(_host_pools(rc.src_pools), dst_host, rc.num_layers, w.dcp_size, rc.src_ids, rc.dst_ids,
+                     rc.first_uncached)
+    H.run_reshard(rc)
+    _sync()
+    for d in range(w.dcp_size):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+    for a, b in zip(src_before, rc.src_pools):
+        assert torch.equal(a, b)
+    assert sum(sent) == len(rc.dst_ids)
+
+
+@pytest.mark.parametrize("cached,dst_filter", [(0, -1), (5, -1), (3, 2)])
+def test_reshard_multi_source_scales(cached, dst_filter):
+    base = get_workload("reshard_mla_128k")
+    w = scaled(base, seed=base.seed + 100, seq_segments=((1, 64 * 37 + 13, 64 * 37 + 13),), num_layers=7,
+               num_sources=3, pool_pages=16, dcp_size=4)
+    H.log(f"reshard 3 sources x 7 layers N=4 cached={cached} filter={dst_filter}")
+    rc = H.make_reshard_case(w, DEV, first_uncached=cached)
+    src_before = [t.clone() for t in rc.src_pools]
+    dst_host = _host_pools(rc.dst_pools)
+    dsc_host = _host_pools(rc.dst_scales)
+    O.reshard(_host_pools(rc.src_pools), dst_host, rc.num_layers, w.dcp_size, rc.src_ids, rc.dst_ids,
+              rc.first_uncached, dst_filter, _host_pools(rc.src_scales), dsc_host)
+    H.run_reshard(rc, dst_filter=dst_filter)
+    _sync()
+    for d in range(w.dcp_size):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+        assert np.array_equal(rc.dst_scales[d].cpu().numpy(), dsc_host[d])
+    for a, b in zip(src_before, rc.src_pools):
+        assert torch.equal(a, b)
+    H.check_reshard_by_plan(rc, dst_filter)
+
+
+def test_reshard_follows_destination_value_not_position():
+    base = get_workload("reshard_mla_128k")
+    w = scaled(base, seed=base.seed + 101, seq_segments=((1, 64 * 8, 64 * 8),), num_layers=2, num_sources=1,
+               pool_pages=8, dcp_size=4)
+    rc = H.make_reshard_case(w, DEV, first_uncached=0)
+    # destination ids whose residues mod 4 do not follow their list positions
+    rc.dst_ids = np.array([7, 2, 4, 13, 0, 9, 30, 17], dtype=np.int64)
+    dst_host = _host_pools(rc.dst_pools)
+    O.reshard(_host_pools(rc.src_pools), dst_host, 2, 4, rc.src_ids, rc.dst_ids, 0)
+    H.run_reshard(rc)
+    _sync()
+    for d in range(4):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
+def test_reshard_out_of_range_entries_are_skipped_and_counted():
+    base = get_workload("reshard_mla_128k")
+    w = scaled(base, seed=base.seed + 102, seq_segments=((1, 64 * 6, 64 * 6),), num_layers=3, num_sources=2,
+               pool_pages=4, dcp_size=2)
+    rc = H.make_reshard_case(w, DEV, first_uncached=0)
+    src = rc.src_ids.copy()
+    dst = rc.dst_ids.copy()
+    src[1] = rc.src_pages + 5       # source page out of range
+    dst[4] = w.pool_pages * 2 + 3   # destination page out of range
+    dst[5] = -1
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.run_reshard(rc, bad=bad, src_ids=src, dst_ids=dst)
+    _sync()
+    assert int(bad.item()) == 3 * w.num_layers
+    keep = [i for i in range(len(dst)) if i not in (1, 4, 5)]
+    dst_host = _host_pools([torch.full_like(t, gen.DST_SENTINEL) for t in rc.dst_pools])
+    O.reshard(_host_pools(rc.src_pools), dst_host, 3, 2, src[keep], dst[keep], 0)
+    for d in range(2):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])

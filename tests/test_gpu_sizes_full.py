@@ -1,0 +1,100 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times.  The reshard is checked completely and bit for bit against the
+oracle's copy plan; attention on sampled (request, head) rows that the oracle
+computes one by one, all shards, all draft positions."""
+
+import numpy as np
+import pytest
+import torch
+
+from tests import harness as H
+from workloads.configs import get_workload
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def test_full_reshard_mla_128k():
+    w = get_workload("reshard_mla_128k")
+    H.log("full reshard: 4 sources x 16 of 64 layers, 2048 pages, 40% cached, N=8")
+    rc = H.make_reshard_case(w, DEV)
+    assert rc.first_uncached == 819
+    chk = [t.view(torch.int64).sum().item() for t in rc.src_pools]
+    H.run_reshard(rc)
+    torch.cuda.synchronize()
+    n_copies = H.check_reshard_by_plan(rc)
+    assert n_copies == 64 * (2048 - 819)
+    assert chk == [t.view(torch.int64).sum().item() for t in rc.src_pools]  # sources untouched
+    H.log(f"  {n_copies} page copies verified")
+
+
+def test_full_gqa_bf16_16x4k_32k():
+    w = get_workload("gqa_bf16_16x4k-32k")
+    H.log("full decode: gqa bf16 16 x U[4K,32K], N=4")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs.out).all()
+    worst = H.check_decode(case, outs, requests=[0, 5, 10, 15], heads=[0, 7, 18, 31])
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+def test_full_mla_fp8_48x100k():
+    w = get_workload("mla_fp8_48x100k")
+    H.log("full decode: mla fp8 48 x 100000, Hq=128, N=8")
+    case = H.make_decode_case(w, DEV)
+    outs = H.run_decode(case)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs.out).all()
+    worst = H.check_decode(case, outs, requests=[0, 47], heads=[0, 77, 127])
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+@pytest.mark.timeout(400)
+def test_full_longmix_verify_pipeline():
+    """Reshard of the long requests from 4 layer-split sources, then q_len 4
+    causal verify attention on every layer; sampled rows against the oracle
+    computed from the inputs (source pages for long requests, pool pages for
+    the short ones)."""
+    w = get_workload("mla_fp8_longmix_verify")
+    H.log("full pipeline: 8 x U[500K,1M] + 40 x 2048, q_len 4, 4 layers, N=8")
+    sl = np.asarray(H.gen.draw_seq_lens(w))
+    long_ids = [b for b in range(len(sl)) if sl[b] >= w.reshard_min_len]
+    pools, scales = H.alloc_pools(w, DEV)  # random pages: what the short requests hold
+    rc = H.make_reshard_case(w, DEV, seq_lens=sl, requests=long_ids, first_uncached=0, dst_pools=pools,
+                             dst_scales=scales)
+    H.run_reshard(rc)
+    torch.cuda.synchronize()
+    case = H.make_decode_case(w, DEV, seq_lens=sl, pools=pools, scales=scales)
+    # logical KV of a sampled long request comes from the SOURCE pages (the
+    # reshard's inputs), of a short one from the pools (never overwritten)
+    b_long, b_short = long_ids[0], [b for b in range(len(sl)) if b not in long_ids][3]
+    off = 0
+    for b in long_ids:
+        if b == b_long:
+            break
+        off += len(case.pages[b])
+    n_long = len(case.pages[b_long])
+    for layer in range(w.num_layers):
+        outs = H.run_decode(case, layer=layer)
+        torch.cuda.synchronize()
+        assert torch.isfinite(outs.out).all()
+        if layer not in (0, 3):
+            continue
+        r, first = next((r, a) for r in range(w.num_sources)
+                        for a, bb in [H.K.cp_layersplit_layer_range(w.num_layers, w.num_sources, r)]
+                        if a <= layer < bb)
+        sids = torch.from_numpy(rc.src_ids[off:off + n_long]).to(DEV)
+        pb = rc.src_pools[r][layer - first].index_select(0, sids).cpu().numpy()
+        ps = rc.src_scales[r][layer - first].index_select(0, sids).cpu().numpy().astype(np.int64) & 0xFFFF
+        kv_long = H.oracle_logical_kv(w, pb, ps, int(sl[b_long]))
+        tol_o, tol_l = H.tolerance(w)
+        for b, kv, heads in ((b_long, kv_long, [5]), (b_short, None, [5, 100])):
+            (po, pl), (uo, ul) = H.oracle_request(case, b, heads=heads, kv=kv, layer=layer)
+            for d in range(w.dcp_size):
+                H.check_rows(f"L{layer} partial d={d} b={b}", outs.partial_out[d, b][:, heads].cpu().numpy(),
+                             outs.partial_lse[d, b][:, heads].cpu().numpy(), po[d][:, heads], pl[d][:, heads],
+                             tol_o, tol_l)
+            H.check_rows(f"L{layer} merged b={b}", outs.out[b][:, heads].cpu().numpy(),
+                         outs.lse[b][:, heads].cpu().numpy(), uo[:, heads], ul[:, heads], tol_o, tol_l)
+        H.log(f"  layer {layer}: sampled rows match")

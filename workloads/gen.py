@@ -22,7 +22,7 @@ import torch
 
 from .configs import MLA_DIM, Workload
 
-_TAGS = {"seq_lens": 1, "free": 2, "src_order": 3, "q": 4, "kv": 5, "pool": 6, "misc": 7}
+_TAGS = {"seq_lens": 1, "free": 2, "src_order": 3, "q": 4, "kv": 5, "pool": 6, "misc": 7, "src": 8}
 FILL_CHUNK_PAGES = 2048
 
 
