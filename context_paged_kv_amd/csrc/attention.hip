@@ -135,23 +135,6 @@ __device__ __forceinline__ float load_q<uint16_t>(const uint16_t* q, int64_t i) 
   return bf16_to_float(q[i]);
 }
 
-// Decode item w into its pair, chunk and head block.
-__device__ __forceinline__ void decode_item(const AttnParams& p, int w, int& pair, int& chunk,
-                                            int& hb) {
-  const int gc = w / p.hb_count;
-  hb = w - gc * p.hb_count;
-  int lo = 0, hi = p.shard_count * p.batch - 1;
-  while (lo < hi) {  // last pair with chunk_begin <= gc
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.pairs[mid].chunk_begin <= gc)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  pair = lo;
-  chunk = gc - p.pairs[lo].chunk_begin;
-}
-
 template <int KIND, typename QT>
 __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams p) {
   constexpr int RB = GenCfg<KIND>::RB;

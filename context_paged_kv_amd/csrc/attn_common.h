@@ -136,6 +136,23 @@ __device__ inline void wave_merge_row(int count, const float* __restrict__ lse, 
   }
 }
 
+// Decode item w into its pair, chunk and head block.
+__device__ __forceinline__ void decode_item(const AttnParams& p, int w, int& pair, int& chunk,
+                                            int& hb) {
+  const int gc = w / p.hb_count;
+  hb = w - gc * p.hb_count;
+  int lo = 0, hi = p.shard_count * p.batch - 1;
+  while (lo < hi) {  // last pair with chunk_begin <= gc
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.pairs[mid].chunk_begin <= gc)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  pair = lo;
+  chunk = gc - p.pairs[lo].chunk_begin;
+}
+
 // Value of an OCP e4m3fn code (bias 7) computed exactly: the code's exponent
 // and mantissa bits placed in an IEEE half (bias 15) give the value / 2^8 for
 // normal and subnormal codes alike.  The NaN codes 0x7F/0xFF decode to +-480.

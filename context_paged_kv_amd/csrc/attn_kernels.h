@@ -23,5 +23,7 @@ int launch_partial(int kind, const AttnParams& p, const dcp_attn_desc& D, int cu
                    int64_t item_bound, hipStream_t st);
 int launch_generic(const AttnParams& p, const dcp_attn_desc& D, int cus, int64_t item_bound,
                    hipStream_t st);
+bool gqa_bf16_supported(const dcp_attn_desc& D);
+int launch_gqa_bf16(const AttnParams& p, const dcp_attn_desc& D, int64_t item_bound, hipStream_t st);
 
 }  // namespace dcpkv

@@ -5,21 +5,23 @@
 
 namespace dcpkv {
 
-// DCPKV_FORCE_GENERIC=1 routes every call to the generic kernel (a debugging
-// aid for comparing kernels; it is still this library's own GPU code).
+// DCPKV_FORCE_GENERIC=1 routes every call to the generic kernel (used to
+// compare the two kernels of this library against each other).
 static bool force_generic() {
   const char* e = std::getenv("DCPKV_FORCE_GENERIC");
   return e && e[0] == '1';
 }
 
 int choose_kernel(const dcp_attn_desc& D) {
-  (void)D;
   if (force_generic()) return KK_GENERIC;
+  if (gqa_bf16_supported(D)) return KK_GQA_BF16;
   return KK_GENERIC;
 }
 
 int kernel_rows_per_block(int kind, const dcp_attn_desc& D) {
   switch (kind) {
+    case KK_GQA_BF16:
+      return (D.num_q_heads / D.num_kv_heads) * D.q_len;  // the whole group in one MFMA row block
     default:
       return D.kv_layout == DCPKV_LAYOUT_MLA ? 8 : 16;
   }
@@ -27,6 +29,8 @@ int kernel_rows_per_block(int kind, const dcp_attn_desc& D) {
 
 int kernel_items_per_cu(int kind) {
   switch (kind) {
+    case KK_GQA_BF16:
+      return 16;  // one wavefront per item
     default:
       return 4;
   }
@@ -43,6 +47,8 @@ int kernel_min_chunk_pages(int kind, const dcp_attn_desc& D) {
 int launch_partial(int kind, const AttnParams& p, const dcp_attn_desc& D, int cus,
                    int64_t item_bound, hipStream_t st) {
   switch (kind) {
+    case KK_GQA_BF16:
+      return launch_gqa_bf16(p, D, item_bound, st);
     default:
       return launch_generic(p, D, cus, item_bound, st);
   }

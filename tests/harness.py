@@ -208,7 +208,8 @@ def rel_row_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
 
 def lse_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     both_inf = np.isneginf(got) & np.isneginf(ref)
-    return np.where(both_inf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):
+        return np.where(both_inf, 0.0, np.abs(got - ref))
 
 
 def check_rows(name, got_o, got_l, ref_o, ref_l, tol_o, tol_l):

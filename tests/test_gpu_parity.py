@@ -37,16 +37,29 @@ def test_decode_tiny_fp32_full():
     H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
 
 
-@pytest.mark.parametrize("seed_shift", [0, 1])
-def test_decode_gqa_bf16_small(seed_shift):
+@pytest.mark.parametrize("seed_shift,q_len", [(0, 1), (1, 1), (2, 2), (3, 4)])
+def test_decode_gqa_bf16_small(seed_shift, q_len):
     base = get_workload("gqa_bf16_16x4k-32k")
-    w = scaled(base, seed=base.seed + 100 + seed_shift, seq_segments=((5, 70, 3000),), pool_pages=256)
-    H.log(f"decode gqa bf16 small seed {w.seed}")
+    w = scaled(base, seed=base.seed + 100 + seed_shift, seq_segments=((5, 70, 3000),), pool_pages=256,
+               q_len=q_len)
+    H.log(f"decode gqa bf16 small seed {w.seed} q_len {q_len}")
     case = H.make_decode_case(w, DEV)
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
     H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+def test_decode_gqa_bf16_generic_kernel(monkeypatch):
+    # the generic VALU kernel on the same shape, selected through the library's switch
+    base = get_workload("gqa_bf16_16x4k-32k")
+    w = scaled(base, seed=base.seed + 150, seq_segments=((3, 70, 2000),), pool_pages=128)
+    case = H.make_decode_case(w, DEV)
+    monkeypatch.setenv("DCPKV_FORCE_GENERIC", "1")
+    outs = H.run_decode(case)
+    _sync()
+    monkeypatch.delenv("DCPKV_FORCE_GENERIC")
+    H.check_decode(case, outs)
 
 
 def test_decode_mla_fp8_small():
