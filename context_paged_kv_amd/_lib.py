@@ -16,7 +16,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdcpkv.so")
+# DCPKV_LIBRARY may point at another build of the same library (same ABI)
+LIB_PATH = os.environ.get("DCPKV_LIBRARY") or os.path.join(_HERE, "libdcpkv.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(

@@ -2,19 +2,28 @@
 // 2D KV Resharding", sections 2, 4.1, 6.2-6.6).
 //
 // One launch moves one request's uncached pages over every (layer-split
-// source r, DCP destination d) path.  The grid is (entry, layer): each
-// workgroup copies one (layer, page) of page_bytes bytes.  The source-side
-// filter of section 6.2 is fused: the destination global page VALUE g picks
-// the shard (g mod N) and the local slot (g div N), pairing with the source
-// page id at the same list position (section 6.3).  Pages are streamed with
-// 16-byte lane loads, all of a thread's loads issued before its stores, and
-// non-temporal hints (the data is touched exactly once).
+// source r, DCP destination d) path.  The source-side filter of section 6.2
+// is fused: the destination global page VALUE g picks the shard (g mod N) and
+// the local slot (g div N), pairing with the source page id at the same list
+// position (section 6.3).
+//
+// Work is split into items (layer, entry, segment): each page is cut into
+// equal segments of at most 16 KB so that large pages do not leave a ragged
+// tail of workgroups.  A persistent grid (4 workgroups per compute unit)
+// strides over the items; every thread keeps four 16-byte non-temporal loads
+// in flight before its stores (the data is touched exactly once).  Measured
+// on MI355X this shape streams scattered pages within a few percent of a
+// plain contiguous copy.
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "common.h"
 
 namespace dcpkv {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct ReshardArgs {
   const uint8_t* src[kMaxSources];
@@ -25,9 +34,13 @@ struct ReshardArgs {
   const int64_t* dst_ids;
   int32_t* bad;
   int64_t page_bytes;
+  int64_t seg_bytes;   // bytes per segment (a multiple of 16)
   int64_t src_pages;   // S
   int64_t dst_pages;   // M
   int64_t first;       // first uncached entry
+  int64_t work;        // entries to move (num_pages - first)
+  int64_t items;       // num_layers * work * segs
+  int32_t segs;        // segments per page
   int32_t num_layers;
   int32_t num_sources;
   int32_t n;           // DCP size
@@ -35,10 +48,10 @@ struct ReshardArgs {
   int32_t has_scales;
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kReshardThreads = 256;
-constexpr int kReshardUnroll = 9;  // 256 x 9 x 16 B = one 36 KB fp8 latent page per round
+constexpr int kReshardUnroll = 4;                                       // 16 KB per round
+constexpr int64_t kReshardSegMax = 16 * kReshardThreads * kReshardUnroll;  // 16384 bytes
+constexpr int kReshardBlocksPerCU = 4;
 
 // Owner of `layer` under the section 4.1 split, and the first layer it owns.
 __device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_sources, int& r,
@@ -55,49 +68,65 @@ __device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_s
 }
 
 __global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a) {
-  const int64_t i = a.first + blockIdx.x;
-  const int layer = blockIdx.y;
-  const int64_t g = a.dst_ids[i];
-  const int32_t sp = a.src_ids[i];
-  int d;
-  int64_t s;
-  if (a.n > 1) {
-    d = (int)(g % a.n);
-    s = g / a.n;
-  } else {
-    d = 0;
-    s = g;
-  }
-  const bool ok = g >= 0 && s < a.dst_pages && sp >= 0 && sp < a.src_pages;
-  if (!ok) {
-    if (threadIdx.x == 0 && a.bad) atomicAdd(a.bad, 1);
-    return;
-  }
-  if (a.dst_filter >= 0 && d != a.dst_filter) return;
-  int r, begin;
-  layer_owner(layer, a.num_layers, a.num_sources, r, begin);
-  const int64_t src_off = ((int64_t)(layer - begin) * a.src_pages + sp) * a.page_bytes;
-  const int64_t dst_off = ((int64_t)layer * a.dst_pages + s) * a.page_bytes;
-  const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(a.src[r] + src_off);
-  u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.dst[d] + dst_off);
-  const int64_t chunks = a.page_bytes >> 4;
-  for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kReshardThreads * kReshardUnroll) {
-    u32x4 v[kReshardUnroll];
-#pragma unroll
-    for (int u = 0; u < kReshardUnroll; ++u) {
-      const int64_t c = c0 + u * kReshardThreads + threadIdx.x;
-      if (c < chunks) v[u] = __builtin_nontemporal_load(src + c);
+  for (int64_t it = blockIdx.x; it < a.items; it += gridDim.x) {
+    const int64_t per_layer = a.work * a.segs;
+    const int layer = (int)(it / per_layer);
+    const int64_t rest = it - (int64_t)layer * per_layer;
+    const int64_t e = rest / a.segs;
+    const int sg = (int)(rest - e * a.segs);
+    const int64_t i = a.first + e;
+    const int64_t g = a.dst_ids[i];
+    const int32_t sp = a.src_ids[i];
+    int d;
+    int64_t s;
+    if (a.n > 1) {
+      d = (int)(g % a.n);
+      s = g / a.n;
+    } else {
+      d = 0;
+      s = g;
     }
+    const bool ok = g >= 0 && s < a.dst_pages && sp >= 0 && sp < a.src_pages;
+    if (!ok) {
+      if (sg == 0 && threadIdx.x == 0 && a.bad) atomicAdd(a.bad, 1);
+      continue;
+    }
+    if (a.dst_filter >= 0 && d != a.dst_filter) continue;
+    int r, begin;
+    layer_owner(layer, a.num_layers, a.num_sources, r, begin);
+    const int64_t off = (int64_t)sg * a.seg_bytes;
+    const int64_t src_off = ((int64_t)(layer - begin) * a.src_pages + sp) * a.page_bytes + off;
+    const int64_t dst_off = ((int64_t)layer * a.dst_pages + s) * a.page_bytes + off;
+    const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(a.src[r] + src_off);
+    u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.dst[d] + dst_off);
+    const int64_t len = (a.page_bytes - off) < a.seg_bytes ? (a.page_bytes - off) : a.seg_bytes;
+    const int chunks = (int)(len >> 4);
+    for (int c0 = 0; c0 < chunks; c0 += kReshardThreads * kReshardUnroll) {
+      u32x4 v[kReshardUnroll];
 #pragma unroll
-    for (int u = 0; u < kReshardUnroll; ++u) {
-      const int64_t c = c0 + u * kReshardThreads + threadIdx.x;
-      if (c < chunks) __builtin_nontemporal_store(v[u], dst + c);
+      for (int u = 0; u < kReshardUnroll; ++u) {
+        const int c = c0 + u * kReshardThreads + threadIdx.x;
+        if (c < chunks) v[u] = __builtin_nontemporal_load(src + c);
+      }
+#pragma unroll
+      for (int u = 0; u < kReshardUnroll; ++u) {
+        const int c = c0 + u * kReshardThreads + threadIdx.x;
+        if (c < chunks) __builtin_nontemporal_store(v[u], dst + c);
+      }
+    }
+    if (a.has_scales && sg == 0 && threadIdx.x == 0) {
+      a.dst_scale[d][(int64_t)layer * a.dst_pages + s] =
+          a.src_scale[r][(int64_t)(layer - begin) * a.src_pages + sp];
     }
   }
-  if (a.has_scales && threadIdx.x == 0) {
-    a.dst_scale[d][(int64_t)layer * a.dst_pages + s] =
-        a.src_scale[r][(int64_t)(layer - begin) * a.src_pages + sp];
-  }
+}
+
+static int device_cus_reshard() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
 }
 
 }  // namespace dcpkv
@@ -129,9 +158,6 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   if (work == 0) return DCPKV_OK;
   if (!src_page_ids || !dst_global_pages)
     return set_error(DCPKV_EINVAL, "reshard: NULL page id arrays");
-  // a dispatch dimension counts work-items in 32 bits: entries * 256 threads
-  if (work > (int64_t)(UINT32_MAX / kReshardThreads))
-    return set_error(DCPKV_EINVAL, "reshard: %lld pages exceed one call's limit", (long long)work);
   ReshardArgs a = {};
   for (int r = 0; r < D.num_sources; ++r) {
     if (!src_pools[r] || !aligned16(src_pools[r]))
@@ -156,16 +182,24 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   a.dst_ids = dst_global_pages;
   a.bad = bad_entries;
   a.page_bytes = D.page_bytes;
+  {  // near-equal segments of at most 16 KB, 16-byte multiples, covering the page exactly
+    const int64_t nseg = (D.page_bytes + kReshardSegMax - 1) / kReshardSegMax;
+    a.seg_bytes = (((D.page_bytes + nseg - 1) / nseg + 15) / 16) * 16;
+    a.segs = (int32_t)((D.page_bytes + a.seg_bytes - 1) / a.seg_bytes);
+  }
   a.src_pages = D.src_pages;
   a.dst_pages = D.dst_pages;
   a.first = first_uncached;
+  a.work = work;
+  a.items = (int64_t)D.num_layers * work * a.segs;
   a.num_layers = D.num_layers;
   a.num_sources = D.num_sources;
   a.n = D.dcp_size;
   a.dst_filter = D.dst_filter;
   a.has_scales = src_scales != nullptr;
-  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)work, (unsigned)D.num_layers),
-                     dim3(kReshardThreads), 0, static_cast<hipStream_t>(stream), a);
+  const int64_t grid = std::min<int64_t>(a.items, (int64_t)device_cus_reshard() * kReshardBlocksPerCU);
+  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kReshardThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "reshard: launch failed: %s", hipGetErrorString(e));
   return DCPKV_OK;
