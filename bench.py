@@ -26,6 +26,7 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 matrix peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -37,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="gqa_bf16_16x4k-32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain torch copy of this many MiB before timing (a known-size kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -78,11 +82,15 @@ class Step:
         pm = K.PageMap(N, w.page_size, M, gen.draw_free_order(w))
         self.pages = [pm.alloc(int(t)) for t in self.seq_lens]
         pm.close()
-        self.num_pages = sum(len(p) for p in self.pages)
         self.max_local = max(-(-len(p) // N) for p in self.pages)
         tables, _ = K.dcp_build_block_tables(N, self.pages, self.max_local)
-        # layer-split source(s) holding the batch's pages in permuted order
-        S = self.num_pages
+        # the transfer: every request's pages (or only the long ones), from the layer-split sources
+        self.has_reshard = w.num_sources > 0
+        self.has_attention = w.has_attention
+        self.reshard_reqs = ([b for b in range(w.num_requests) if self.seq_lens[b] >= w.reshard_min_len]
+                             if self.has_reshard else [])
+        self.num_pages = sum(len(self.pages[b]) for b in self.reshard_reqs)
+        S = max(1, self.num_pages)
         self.src_pages = S
         self.src, self.src_scales = [], ([] if w.has_scales else None)
         for r in range(w.num_sources):
@@ -95,12 +103,27 @@ class Step:
             if sc is not None:
                 sc[-1].fill_(gen.SCALE_SENTINEL)
                 self.src_scales.append(sc)
-        self.pools = [torch.full((w.num_layers, M, pb), gen.DST_SENTINEL, dtype=torch.uint8, device=dev)
-                      for _ in range(N)]
-        self.scales = ([torch.full((w.num_layers, M), gen.SCALE_SENTINEL, dtype=torch.int16, device=dev)
-                        for _ in range(N)] if w.has_scales else None)
-        self.src_ids = torch.from_numpy(gen.draw_src_order(w, S).astype(np.int32)).to(dev)
-        self.dst_ids = torch.from_numpy(np.concatenate(self.pages).astype(np.int64)).to(dev)
+        # pools: random pages where requests are not transferred in the step, else a sentinel
+        fill_random = self.has_attention and len(self.reshard_reqs) < w.num_requests
+        self.pools, self.scales = [], ([] if w.has_scales else None)
+        for d in range(N):
+            t = torch.empty((w.num_layers, M, pb), dtype=torch.uint8, device=dev)
+            sc = torch.empty((w.num_layers, M), dtype=torch.int16, device=dev) if w.has_scales else None
+            if fill_random:
+                gen.fill_pages_(t.view(-1, pb), w, "pool", sub=d, scales=None if sc is None else sc.view(-1))
+            else:
+                t.fill_(gen.DST_SENTINEL)
+                if sc is not None:
+                    sc.fill_(gen.SCALE_SENTINEL)
+            self.pools.append(t)
+            if sc is not None:
+                self.scales.append(sc)
+        self.src_ids = torch.from_numpy(gen.draw_src_order(w, S)[: self.num_pages].astype(np.int32)).to(dev)
+        self.dst_ids = torch.from_numpy(np.concatenate([self.pages[b] for b in self.reshard_reqs] or [np.zeros(0)])
+                                        .astype(np.int64)).to(dev)
+        self.first_uncached = int(np.floor(w.cached_frac * self.num_pages)) if self.has_reshard else 0
+        if not self.has_attention:
+            return
         self.q = gen.draw_q(w, dev)
         self.bt = torch.from_numpy(tables).to(dev)
         self.sl = torch.from_numpy(self.seq_lens.astype(np.int32)).to(dev)
@@ -122,31 +145,49 @@ class Step:
 
     # --- the three calls ---------------------------------------------------
     def reshard(self):
+        if not self.has_reshard:
+            return
         w = self.w
         self.K.kv_reshard_pages(num_layers=w.num_layers, dcp_size=w.dcp_size, page_bytes=w.page_bytes,
                                 src_pages=self.src_pages, dst_pages=w.pool_pages, src_pools=self.src,
                                 dst_pools=self.pools, src_page_ids=self.src_ids, dst_global_pages=self.dst_ids,
-                                first_uncached=0, src_scales=self.src_scales, dst_scales=self.scales)
+                                first_uncached=self.first_uncached, src_scales=self.src_scales,
+                                dst_scales=self.scales)
 
     def partial(self):
+        if not self.has_attention:
+            return
         self.K.dcp_decode_partial(self.desc, q=self.q, kv_pools=self.pools, kv_scales=self.scales,
                                   block_tables=self.bt, seq_lens=self.sl, total_tokens=self.total_tokens,
                                   partial_out=self.po, partial_lse=self.pl, workspace=self.ws)
 
     def merge(self):
+        if not self.has_attention:
+            return
         self.K.dcp_lse_merge(self.w.dcp_size, self.rows, self.w.head_dim_v, self.po, self.pl, self.out, self.lse)
 
     # --- algorithmic bytes ---------------------------------------------------
     def bytes_reshard(self):
         w = self.w
-        moved = self.num_pages * w.num_layers * w.page_bytes
-        scales = self.num_pages * w.num_layers * 2 * 2 if w.has_scales else 0
-        ids = self.num_pages * (4 + 8)
+        moved_pages = self.num_pages - self.first_uncached
+        moved = moved_pages * w.num_layers * w.page_bytes
+        scales = moved_pages * w.num_layers * 2 * 2 if w.has_scales else 0
+        ids = moved_pages * (4 + 8)
         return 2 * moved + scales + ids  # read + write
+
+    def flops_attn(self):
+        w = self.w
+        if not self.has_attention:
+            return 0
+        # visible (query, key) pairs x heads x (Dqk + Dv) x 2
+        pairs = sum(int(t) * w.q_len - w.q_len * (w.q_len - 1) // 2 for t in self.seq_lens)
+        return 2.0 * pairs * w.num_q_heads * (w.head_dim_qk + w.head_dim_v)
 
     def bytes_kv(self):
         """KV bytes the attention must read: every token once (tail of the last page excluded)."""
         w = self.w
+        if not self.has_attention:
+            return 0
         if w.layout == "mla":
             per_tok = 576
             scales = sum(len(p) for p in self.pages) * 2
@@ -157,6 +198,8 @@ class Step:
 
     def bytes_attn_other(self):
         w = self.w
+        if not self.has_attention:
+            return 0
         qb = self.q.numel() * self.q.element_size()
         partial = self.po.numel() * 4 + self.pl.numel() * 4
         out = self.out.numel() * 4 + self.lse.numel() * 4
@@ -164,58 +207,64 @@ class Step:
 
 
 def cpu_baseline(st, budget_s: float):
-    """The float64 oracle on the host, on a bounded sample of the same workload,
-    scaled to the step's GB/s."""
+    """The float64 oracle on the host (one thread), timed on a bounded sample of
+    the same workload and scaled linearly to the step's GB/s."""
     import oracle as O
     import torch
+    from threadpoolctl import threadpool_limits
+    from tests import harness as Hn  # oracle-side page gathering shared with the tests
 
     w = st.w
-    t_budget = budget_s / 2
-    # (1) reshard: the oracle's scalar page copy over a prefix of the batch's pages
-    src_h = [t.cpu().numpy() for t in st.src]
-    dst_h = [np.full((w.num_layers, w.pool_pages, w.page_bytes), 0xA5, np.uint8) for _ in range(w.dcp_size)]
-    ids_s = st.src_ids.cpu().numpy()
-    ids_d = st.dst_ids.cpu().numpy()
-    n_pages, t0 = 0, time.perf_counter()
-    step = 64
-    while time.perf_counter() - t0 < t_budget and n_pages < len(ids_d):
-        hi = min(len(ids_d), n_pages + step)
-        O.reshard(src_h, dst_h, w.num_layers, w.dcp_size, ids_s[n_pages:hi], ids_d[n_pages:hi], 0)
-        n_pages = hi
-    t_rs = time.perf_counter() - t0
-    rs_rate = 2 * n_pages * w.num_layers * w.page_bytes / t_rs  # bytes / s
-    del src_h, dst_h
-    # (2) attention: oracle partials + merge for whole requests, heads in order
-    pools_h = None
-    tok_done, t0 = 0, time.perf_counter()
-    b = 0
-    from tests import harness as Hn  # the oracle-side page gather used by the tests
-    heads_done = 0
-    while time.perf_counter() - t0 < t_budget and b < w.num_requests:
-        pb, ps = Hn.gather_request_pages(st.pools, st.scales, st.pages[b], w.dcp_size, w.attn_layer)
-        kv = Hn.oracle_logical_kv(w, pb, ps, int(st.seq_lens[b]))
-        q = st.q[b].float().cpu().numpy().astype(np.float64)
-        for h in range(w.num_q_heads):
-            po, pl = O.request_partials(q, kv[0], kv[1], int(st.seq_lens[b]), w.softmax_scale, st.pages[b],
-                                        w.page_size, w.dcp_size, heads=[h])
-            O.lse_merge(po[:, :, [h]], pl[:, :, [h]])
-            heads_done += 1
-            tok_done += int(st.seq_lens[b]) * w.q_len
-            if time.perf_counter() - t0 >= t_budget:
-                break
-        b += 1
-    t_at = time.perf_counter() - t0
-    # KV bytes per (token, query row) of work, scaled to the full batch
-    full_work = st.total_tokens * w.q_len * w.num_q_heads
-    at_time_full = t_at * full_work / max(tok_done, 1)
-    rs_time_full = st.bytes_reshard() / rs_rate
+    budget = budget_s / (2 if (st.has_reshard and st.has_attention) else 1)
+    notes = []
+    rs_time_full = at_time_full = 0.0
+    with threadpool_limits(limits=1):
+        if st.has_reshard:
+            # the real source bytes of the first uncached pages, one layer per source,
+            # re-addressed into compact host pools (same per-page work as the full geometry)
+            n = min(len(st.dst_ids) - st.first_uncached, 16 if w.page_bytes > 65536 else 64)
+            sel = slice(st.first_uncached, st.first_uncached + n)
+            sids = st.src_ids[sel]
+            src_h = []
+            for r in range(w.num_sources):
+                t = np.full((2, n, w.page_bytes), 0x5A, np.uint8)
+                t[0] = st.src[r][0].index_select(0, sids.long()).cpu().numpy()
+                src_h.append(t)
+            g = st.dst_ids[sel].cpu().numpy()
+            g2 = np.arange(n) * w.dcp_size + (g % w.dcp_size)
+            dst_h = [np.zeros((w.num_sources, n, w.page_bytes), np.uint8) for _ in range(w.dcp_size)]
+            reps, t0 = 0, time.perf_counter()
+            while time.perf_counter() - t0 < budget and reps < 10000:
+                O.reshard(src_h, dst_h, w.num_sources, w.dcp_size, np.arange(n), g2, 0)
+                reps += 1
+            t_rs = time.perf_counter() - t0
+            rate = 2.0 * reps * n * w.num_sources * w.page_bytes / t_rs
+            rs_time_full = st.bytes_reshard() / rate
+            notes.append(f"scalar reshard of {n} pages x {w.num_sources} layer(s), {reps} passes in {t_rs:.1f}s")
+        if st.has_attention:
+            done, t0, rows = 0, time.perf_counter(), 0
+            b = 0
+            while time.perf_counter() - t0 < budget and b < w.num_requests:
+                pb, ps = Hn.gather_request_pages(st.pools, st.scales, st.pages[b], w.dcp_size, w.attn_layer)
+                kv = Hn.oracle_logical_kv(w, pb, ps, int(st.seq_lens[b]))
+                q = st.q[b].float().cpu().numpy().astype(np.float64)
+                for h in range(w.num_q_heads):
+                    po, pl = O.request_partials(q, kv[0], kv[1], int(st.seq_lens[b]), w.softmax_scale,
+                                                st.pages[b], w.page_size, w.dcp_size, heads=[h])
+                    O.lse_merge(po[:, :, [h]], pl[:, :, [h]])
+                    rows += 1
+                    done += int(st.seq_lens[b]) * w.q_len
+                    if time.perf_counter() - t0 >= budget:
+                        break
+                b += 1
+            t_at = time.perf_counter() - t0
+            at_time_full = t_at * (st.total_tokens * w.q_len * w.num_q_heads) / max(done, 1)
+            notes.append(f"partials + merge for {rows} of {w.num_requests * w.num_q_heads} (request, head) "
+                         f"rows in {t_at:.1f}s (page gather and decode included)")
     step_bytes = st.bytes_reshard() + st.bytes_kv() + st.bytes_attn_other()
     value = step_bytes / (rs_time_full + at_time_full) / 1e9
     return {"value": round(value, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": (f"float64 numpy oracle, one thread: scalar reshard of {n_pages} of {len(ids_d)} pages "
-                       f"x {w.num_layers} layer(s) in {t_rs:.1f}s; partials+merge for {heads_done} "
-                       f"(request, head) rows of {w.num_requests * w.num_q_heads} in {t_at:.1f}s; "
-                       f"scaled linearly to the full step")}
+            "sample": "float64 numpy oracle, one thread: " + "; ".join(notes) + "; scaled linearly to the full step"}
 
 
 def main():
@@ -236,6 +285,13 @@ def main():
     print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
     st = Step(w, dev)
     torch.cuda.synchronize()
+    if a.calib_copy_mib:
+        n = a.calib_copy_mib * (1 << 20) // 16
+        src_c = torch.ones(n, 4, dtype=torch.int32, device=dev)
+        dst_c = torch.empty_like(src_c)
+        dst_c.copy_(src_c)
+        torch.cuda.synchronize()
+        del src_c, dst_c
     for _ in range(a.warmup):
         st.reshard()
         st.partial()
@@ -261,29 +317,55 @@ def main():
     t_pa = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
     t_mg = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
     t_step = np.array([e[0].elapsed_time(e[3]) for e in evs]) * 1e-3
-    assert torch.isfinite(st.out).all() and torch.isfinite(st.lse).all(), "non-finite attention output"
+    if st.has_attention:
+        assert torch.isfinite(st.out).all() and torch.isfinite(st.lse).all(), "non-finite attention output"
     ms_per_step = wall / a.steps * 1e3
     b_rs, b_kv, b_other = st.bytes_reshard(), st.bytes_kv(), st.bytes_attn_other()
     step_bytes = b_rs + b_kv + b_other
     value = step_bytes / (wall / a.steps) / 1e9
-    rs_gbps = b_rs / t_rs.mean() / 1e9
-    kv_gbps = b_kv / (t_pa.mean() + t_mg.mean()) / 1e9
-    attn_total_gbps = (b_kv + b_other) / (t_pa.mean() + t_mg.mean()) / 1e9
-    # dominant kernel of the step
-    if t_rs.mean() >= t_pa.mean():
-        dom, dom_bytes, dom_t = "reshard_kernel", b_rs, t_rs.mean()
-        src_files = ["reshard.hip", "common.h"]
+    parts = {"step_event_us": round(t_step.mean() * 1e6, 2),
+             "bytes": {"reshard_rw": b_rs, "kv": b_kv, "attn_other": b_other}}
+    if st.has_reshard:
+        rs_gbps = b_rs / t_rs.mean() / 1e9
+        parts.update({"reshard_GBps": round(rs_gbps, 1), "reshard_frac_hbm": round(rs_gbps / HBM_PEAK_GBPS, 4),
+                      "reshard_us": round(t_rs.mean() * 1e6, 2)})
+    if st.has_attention:
+        t_attn = t_pa.mean() + t_mg.mean()
+        kv_gbps = b_kv / t_attn / 1e9
+        parts.update({"attn_kv_GBps": round(kv_gbps, 1), "attn_kv_frac_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
+                      "attn_all_bytes_GBps": round((b_kv + b_other) / t_attn / 1e9, 1),
+                      "attn_TFLOPs": round(st.flops_attn() / t_pa.mean() / 1e12, 1),
+                      "partial_us": round(t_pa.mean() * 1e6, 2), "merge_us": round(t_mg.mean() * 1e6, 2),
+                      "decode_tokens_per_s": round(w.num_requests * w.q_len / t_attn, 1)})
+    # roofline of the dominant call of the step
+    if st.has_reshard and (not st.has_attention or t_rs.mean() >= t_pa.mean()):
+        dom, src_files = "reshard_kernel", ["reshard.hip", "common.h"]
+        achieved = b_rs / t_rs.mean() / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4)}
+        dom_bytes = b_rs
     else:
-        dom, dom_bytes, dom_t = "dcp_decode_partial", b_kv + b_other - (st.out.numel() + st.lse.numel()) * 4, t_pa.mean()
-        src_files = ["attention.hip", "attn_common.h", "attn_kernels.h", "dispatch.hip"]
+        dom = "dcp_decode_partial (plan + partial + chunk-reduce kernels)"
+        src_files = ["attention.hip", "attn_common.h", "attn_kernels.h", "dispatch.hip", "gqa_bf16.hip",
+                     "mla_fp8.hip"]
+        dom_bytes = b_kv + b_other - (st.out.numel() + st.lse.numel()) * 4
+        if w.layout == "mla":  # 128 heads share one latent: the matrix cores bind, fp16 MFMA peak
+            achieved = st.flops_attn() / t_pa.mean() / 1e12
+            roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
+        else:
+            achieved = dom_bytes / t_pa.mean() / 1e9
+            roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBPS, 4)}
     src_hash = kernel_source_hash(src_files)
-    achieved = dom_bytes / dom_t / 1e9
-    traffic = load_traffic(f"{w.name}:{dom}", src_hash, dom_bytes)
+    roof.update({"traffic": load_traffic(f"{w.name}:{dom.split()[0]}", src_hash, dom_bytes), "kernel": dom,
+                 "source_hash": src_hash})
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
         cpu = cpu_baseline(st, a.cpu_seconds)
-    tokens_per_s = w.num_requests * w.q_len / (t_pa.mean() + t_mg.mean())
+    steps_desc = " + ".join(x for x, on in (("reshard", st.has_reshard), ("partial attention", st.has_attention),
+                                           ("LSE merge", st.has_attention)) if on)
     line = {
         "metric": "DCP decode attention KV GB/s (% HBM peak) + reshard GB/s, 1 MI355X",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -292,19 +374,9 @@ def main():
         "config": {"workload": w.name, "requests": w.num_requests, "total_tokens": st.total_tokens,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_qk,
                    "page_size": w.page_size, "dcp_size": w.dcp_size, "q_len": w.q_len,
-                   "step": "reshard + partial attention + LSE merge"},
-        "parts": {
-            "reshard_GBps": round(rs_gbps, 1), "reshard_frac_hbm": round(rs_gbps / HBM_PEAK_GBPS, 4),
-            "reshard_us": round(t_rs.mean() * 1e6, 2),
-            "attn_kv_GBps": round(kv_gbps, 1), "attn_kv_frac_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
-            "attn_all_bytes_GBps": round(attn_total_gbps, 1),
-            "partial_us": round(t_pa.mean() * 1e6, 2), "merge_us": round(t_mg.mean() * 1e6, 2),
-            "step_event_us": round(t_step.mean() * 1e6, 2), "decode_tokens_per_s": round(tokens_per_s, 1),
-            "bytes": {"reshard_rw": b_rs, "kv": b_kv, "attn_other": b_other},
-        },
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
-                     "source_hash": src_hash},
+                   "layers": w.num_layers, "step": steps_desc},
+        "parts": parts,
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -31,27 +31,32 @@ constexpr int kPlanThreads = 256;
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
   __shared__ int32_t s_k[kPlanThreads];
   __shared__ int32_t s_w[kPlanThreads];
-  __shared__ unsigned long long s_need;
+  __shared__ unsigned long long s_need, s_need_all;
   __shared__ int32_t s_carry_k, s_carry_w;
   const int tid = threadIdx.x;
   const int num_pairs = p.shard_count * p.batch;
   const int C = p.chunk_pages;
   if (tid == 0) {
     s_need = 0;
+    s_need_all = 0;
     s_carry_k = 0;
     s_carry_w = 0;
   }
   __syncthreads();
-  unsigned long long mine = 0;
+  unsigned long long mine = 0, mine_all = 0;
   for (int i = tid; i < num_pairs; i += kPlanThreads) {
     const int d = p.shard_begin + i / p.batch, b = i % p.batch;
     const int nl = local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
     const int k = nl > C ? (nl + C - 1) / C : 1;
     if (k >= 2) mine += k;
+    mine_all += k;
   }
   atomicAdd(&s_need, mine);
+  atomicAdd(&s_need_all, mine_all);
   __syncthreads();
-  const int fallback = s_need > (unsigned long long)p.ws_cap ? 1 : 0;
+  // one chunk per pair when the split would not fit the workspace or the launched grid
+  const int fallback =
+      (s_need > (unsigned long long)p.ws_cap || s_need_all > (unsigned long long)p.max_chunks) ? 1 : 0;
   for (int base = 0; base < num_pairs; base += kPlanThreads) {
     const int i = base + tid;
     int k = 0, kw = 0, nl = 0;
@@ -512,14 +517,16 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int cus = device_cus();
 
+  // items: at most (pairs + local pages / C) chunks per head block; the grid covers
+  // max_chunks chunks and the planner never produces more (it falls back to one
+  // chunk per pair, which pairs <= max_chunks always allows)
+  const int64_t pairs = (int64_t)shard_count * D.batch;
+  const int64_t est_pages = std::max<int64_t>(total_tokens, 0) / D.page_size + D.batch;
+  p.max_chunks = pairs + est_pages / g.chunk_pages + 1;
+  const int64_t item_bound = p.max_chunks * g.hb_count;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: plan launch: %s", hipGetErrorString(e));
-
-  // items: at most (pairs + local pages / C) chunks per head block
-  const int64_t pairs = (int64_t)shard_count * D.batch;
-  const int64_t est_pages = std::max<int64_t>(total_tokens, 0) / D.page_size + D.batch;
-  const int64_t item_bound = (pairs + est_pages / g.chunk_pages + 1) * g.hb_count;
   rc = launch_partial(g.kind, p, D, cus, item_bound, st);
   if (rc) return rc;
 

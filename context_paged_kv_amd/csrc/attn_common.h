@@ -51,6 +51,7 @@ struct AttnParams {
   float* ws_o;
   float* ws_lse;
   int64_t ws_cap;           // chunk partial slots in the workspace
+  int64_t max_chunks;       // chunks the launched grid covers
   int64_t pages_per_layer;  // M
   int64_t page_bytes;
   int32_t kv_dtype, layout, q_dtype;

@@ -15,6 +15,7 @@ static bool force_generic() {
 int choose_kernel(const dcp_attn_desc& D) {
   if (force_generic()) return KK_GENERIC;
   if (gqa_bf16_supported(D)) return KK_GQA_BF16;
+  if (mla_fp8_supported(D)) return KK_MLA_FP8;
   return KK_GENERIC;
 }
 
@@ -22,6 +23,8 @@ int kernel_rows_per_block(int kind, const dcp_attn_desc& D) {
   switch (kind) {
     case KK_GQA_BF16:
       return (D.num_q_heads / D.num_kv_heads) * D.q_len;  // the whole group in one MFMA row block
+    case KK_MLA_FP8:
+      return 64;  // four wavefronts x 16 query rows
     default:
       return D.kv_layout == DCPKV_LAYOUT_MLA ? 8 : 16;
   }
@@ -49,6 +52,8 @@ int launch_partial(int kind, const AttnParams& p, const dcp_attn_desc& D, int cu
   switch (kind) {
     case KK_GQA_BF16:
       return launch_gqa_bf16(p, D, item_bound, st);
+    case KK_MLA_FP8:
+      return launch_mla_fp8(p, D, item_bound, st);
     default:
       return launch_generic(p, D, cus, item_bound, st);
   }
