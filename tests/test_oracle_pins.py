@@ -473,3 +473,30 @@ def test_logical_kv_gather_from_pools():
         pools[gg % n, gg // n, 1] = v[:, i * page:(i + 1) * page]
     kk, vv = O.logical_kv_split(lambda d, s: pools[d, s].reshape(-1).view(np.uint8), g, n, "f32", hkv, page, dd, T)
     assert np.array_equal(kk, k[:, :T].astype(np.float64)) and np.array_equal(vv, v[:, :T].astype(np.float64))
+
+
+def test_block_tables_worked_example():
+    # [2DR] section 5.1 with N = 2: pages 6, 7, 2, 3, 10 -> rank 0 holds 6, 2, 10 at slots 3, 1, 5;
+    # rank 1 holds 7, 3 at slots 3, 1 (slots written out by hand from p div N)
+    got = O.block_tables([[6, 7, 2, 3, 10], [1]], 2)
+    assert got == [[[3, 1, 5], []], [[3, 1], [0]]]
+
+
+def test_logical_kv_mla_vs_torch():
+    rng = np.random.default_rng(13)
+    n, page, M = 4, 8, 6
+    pm = O.PageMap(n, page, M, rng.permutation(M))
+    T = 29
+    g = pm.alloc(T)
+    codes = rng.integers(0, 0x7E, size=(n, M, page, 576), dtype=np.uint8)
+    sbits = (torch.tensor(rng.uniform(0.001, 0.1, size=(n, M)), dtype=torch.bfloat16)
+             .view(torch.int16).numpy().astype(np.int64) & 0xFFFF)
+    k, v = O.logical_kv_mla(lambda d, s: (codes[d, s], sbits[d, s]), g, n, page, T)
+    ref = []
+    for gg in g:
+        d, s = gg % n, gg // n
+        sc = torch.tensor([int(sbits[d, s])], dtype=torch.int32).to(torch.int16).view(torch.bfloat16).double()
+        ref.append(torch.from_numpy(codes[d, s]).view(torch.float8_e4m3fn).double() * sc)
+    ref = torch.cat(ref)[:T].numpy()
+    assert k.shape == (1, T, 576) and v.shape == (1, T, 512)
+    assert np.array_equal(k[0], ref) and np.array_equal(v[0], ref[:, :512])
