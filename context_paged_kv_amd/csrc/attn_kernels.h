@@ -26,6 +26,7 @@ int launch_generic(const AttnParams& p, const dcp_attn_desc& D, int cus, int64_t
 bool gqa_bf16_supported(const dcp_attn_desc& D);
 int launch_gqa_bf16(const AttnParams& p, const dcp_attn_desc& D, int64_t item_bound, hipStream_t st);
 bool mla_fp8_supported(const dcp_attn_desc& D);
+int mla_fp8_rows_per_block();
 int launch_mla_fp8(const AttnParams& p, const dcp_attn_desc& D, int64_t item_bound, hipStream_t st);
 
 }  // namespace dcpkv

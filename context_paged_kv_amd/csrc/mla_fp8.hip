@@ -9,27 +9,36 @@
 //
 // Absorbed MLA: every query head has a 576-d query; K is the whole latent and
 // V its first 512 entries, shared by all heads.  With 128 heads the work is
-// about 480 flop per KV byte, so this kernel is bound by the matrix cores,
-// not by HBM.
+// about 480 flop per KV byte, so the matrix cores bind, not HBM.
 //
 // Work item: (shard d, request b, chunk of local pages, block of 64 query
-// rows); a workgroup of four wavefronts owns one item, each wavefront 16 rows
-// (the N = 16 columns of its MFMAs).  Per page:
-//   * the 36 KB of codes are fetched one page ahead with coalesced
-//     non-temporal 16-byte loads (36 VGPRs per thread);
-//   * the workgroup converts them once, exactly, to an fp16 tile
-//     [64 tokens][576] in LDS (v_cvt_scalef32_pk_f16_fp8, two codes per
-//     instruction; tokens past the sequence end are written as zeros);
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_f16: A = 16 token rows of the tile,
-//     B = the wavefront's queries (fp16) held in registers;
-//   * online softmax in base 2, scores scaled by softmax_scale x page scale;
-//   * O^T += V^T P^T on the same MFMA: the V^T operand is read straight from
-//     the row-major tile with ds_read_b64_tr_b16 (each lane receives four
-//     tokens of one latent dim); the token order of the k slots is chosen so
-//     that P^T is lane-local after the S^T MFMA.  The page scale of V is
-//     folded into the running rescale of the accumulator.
-// The tile row stride (1168 bytes) keeps both the 16-row K reads and the
-// transposing V reads free of LDS bank conflicts.
+// rows).  A workgroup of four wavefronts owns one item.  Wavefronts w and
+// w ^ 2 form a pair that owns 32 rows (two N = 16 column tiles, so every
+// operand a wavefront converts feeds two MFMAs); half hh = w >> 1 of the pair
+//   * computes the scores over dims [288 hh, 288 hh + 288) and swaps that
+//     partial S^T with its partner through LDS, so both hold the full scores
+//     (the same sum, bit for bit, hence the same softmax decisions);
+//   * accumulates O over the value dims [256 hh, 256 hh + 256).
+// That keeps a wavefront's accumulator at 128 registers next to the 32 of the
+// score tile, so nothing is shuffled between register files.  Per page:
+//   * the 36 KB of fp8 codes go global -> LDS with global_load_lds_dwordx4
+//     (no registers), double buffered: page j+1 streams in while page j is
+//     computed.  LDS rows are 592 bytes (576 + 16 pad): the transposing reads
+//     below are bank-conflict free, the K reads at most two-way;
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_f16: each lane reads 8 codes of one
+//     token (ds_read_b64) and converts them exactly to fp16 with
+//     v_cvt_scalef32_pk_f16_fp8.  Q is held in fp16, each row scaled by a
+//     power of two so its largest entry sits just below 2^15 (bf16 -> fp16
+//     exact), the factor folded into that row's score scale.  The token order
+//     of the A rows puts, after the MFMA, the eight scores a lane needs for
+//     its P^T operand in that lane;
+//   * online softmax in base 2 with a lazy reference: a row's exponent offset
+//     moves (and the accumulator is rescaled) only when the page maximum
+//     exceeds it by more than 2^8, or when the page scale leaves
+//     [1/4, 4] x the reference scale; in between P carries the page-scale
+//     ratio and the accumulator is touched by MFMAs only;
+//   * O^T += V^T P^T: ds_read_b64_tr_b8 hands each lane eight tokens of one
+//     latent dim straight from the row-major codes, converted as above.
 
 #include <hip/hip_runtime.h>
 
@@ -41,24 +50,31 @@
 namespace dcpkv {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kMlaPage = 64;
 constexpr int kMlaDim = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaRowsPerBlock = 64;
-constexpr int kTileStride = 2 * kMlaDim + 16;  // bytes per fp16 tile row
-constexpr int kPageChunks = kMlaPage * kMlaDim / 16;  // 2304 16-byte chunks per page
-constexpr int kChunksPerThread = kPageChunks / 256;   // 9
+constexpr int kHalfQk = kMlaDim / 2;                // 288 score dims per wavefront
+constexpr int kHalfV = kMlaDv / 2;                  // 256 value dims per wavefront
+constexpr int kQSteps = kHalfQk / 32;               // 9 k-steps of 32 dims
+constexpr int kVTiles = kHalfV / 16;                // 16 M tiles of 16 dims
+constexpr int kRawStride = 592;                     // LDS bytes per token row of codes
+constexpr int kRawBuf = kMlaPage * kRawStride;      // 37888 bytes per page buffer
+constexpr int kSlotsPerRow = kRawStride / 16;       // 37 16-byte slots (36 data + 1 pad)
+constexpr int kSlots = kMlaPage * kSlotsPerRow;     // 2368
+constexpr int kLoadIters = (kSlots + 255) / 256;    // 10
+constexpr float kTau = 8.f;                         // lazy-rescale threshold (log2 units)
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ float mgrp4_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16, 64));
@@ -69,10 +85,47 @@ __device__ __forceinline__ float mgrp4_sum(float v) {
   return v + __shfl_xor(v, 32, 64);
 }
 
+// Eight fp8 e4m3fn codes (two dwords) to eight fp16 values, exactly.
+__device__ __forceinline__ f16x8 cvt8(u32x2 x) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[0], 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true);
+  return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3), __builtin_shufflevector(c, d, 0, 1, 2, 3),
+                                 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Token held by MFMA row m of S^T tile tt: tiles 2ks and 2ks+1 give the lane of
+// group g the tokens 32ks + 8g + [0, 8), the k slots of its P^T operand.
+__device__ __forceinline__ int mla_tok(int tt, int m) {
+  return 32 * (tt >> 1) + 8 * (m >> 2) + 4 * (tt & 1) + (m & 3);
+}
+
+// Start the global -> LDS copy of one page of codes into a 592-byte-row buffer.
+// LDS slot q (16 bytes) of row q / 37, column q % 37 holds page bytes
+// 16 * (q - q / 37) onwards; the pad column refetches a valid chunk.
+__device__ __forceinline__ void issue_page(const uint8_t* page, uint8_t* buf, int wave, int lane) {
+  int ln = lane;
+  asm volatile("" : "+v"(ln));  // recompute the offsets per page instead of holding ten of them
+#pragma unroll
+  for (int i = 0; i < kLoadIters; ++i) {
+    const int base = 256 * i + 64 * wave;  // first slot of this wave's instruction (wave-uniform)
+    if (base < kSlots) {
+      const int slot = base + ln;            // < kSlots: kSlots is a multiple of 64
+      const int row = slot / kSlotsPerRow;
+      const int src = min(16 * (slot - row), kMlaPage * kMlaDim - 16);
+      __builtin_amdgcn_global_load_lds(page + src, (lds_void*)(buf + 16 * base), 16, 0, 0);
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[kMlaPage * kTileStride];  // 74752 B
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBuf];  // 75776 B
+  __shared__ u32x4 s_x[4][8][64];                                     // score-partial swap, 32768 B
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rp = wave & 1, hh = wave >> 1;
   const int g = lane >> 4, c = lane & 15;
 
   // items sharing a chunk run on the same XCD (dispatch is round robin over 8)
@@ -97,181 +150,258 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
   const int chunk = gc - pp.chunk_begin;
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int T = p.seq_lens[b];
-  const int row = hb * kMlaRowsPerBlock + wave * 16 + c;  // this lane's query row within the pair
-  const bool row_ok = row < p.rows;
-  const int t_q = row_ok ? row / p.hq : 0, h_q = row_ok ? row % p.hq : 0;
-  const int64_t lim = row_ok ? (int64_t)T - p.q_len + t_q : -1;  // last visible position
-  const float sl2 = p.scale * kLog2eM;
 
-  // Q^T as B operand: lane (g, c) holds row c of the wave, dims 32*kk + 8*g + [0, 8), fp16
-  f16x8 qb[18];
+  // the lane's two query rows (one per N tile) and their queries over this half's dims
+  // (B operand of S^T: dims 288 hh + 32 kk + 8 g + [0, 8)), as fp16 scaled by 2^qe
+  int rowq[2];
+  int64_t lim[2];
+  float amax[2];
+  u32x4 qraw[2][kQSteps];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const int r = hb * kMlaRowsPerBlock + 32 * rp + 16 * nt + c;
+    const bool ok = r < p.rows;
+    rowq[nt] = ok ? r : -1;
+    const int t = ok ? r / p.hq : 0, h = ok ? r % p.hq : 0;
+    lim[nt] = ok ? (int64_t)T - p.q_len + t : -1;
+    const uint16_t* qr =
+        static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim + kHalfQk * hh;
+    float mx = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < kQSteps; ++kk) {
+      const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qr + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
+      qraw[nt][kk] = w;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        mx = fmaxf(mx, fmaxf(fabsf(__builtin_bit_cast(float, w[e2] << 16)),
+                             fabsf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u))));
+    }
+    amax[nt] = mgrp4_max(mx);
+  }
+  // both halves of a row use one scale: swap the half maxima once
+  if (g == 0) {
+    float* xm = reinterpret_cast<float*>(&s_x[wave][0][0]);
+    xm[c] = amax[0];
+    xm[16 + c] = amax[1];
+  }
+  __syncthreads();
+  float qscale[2];  // 2^qe: the row's largest |q| lands in [2^14, 2^15)
+  f16x8 qb[2][kQSteps];
   {
-    const uint16_t* qbf = static_cast<const uint16_t*>(p.q);
-    const uint16_t* qr = qbf + (((int64_t)b * p.q_len + t_q) * p.hq + h_q) * kMlaDim;
+    const float* xo = reinterpret_cast<const float*>(&s_x[wave ^ 2][0][0]);
 #pragma unroll
-    for (int kk = 0; kk < 18; ++kk) {
-      u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(qr + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
+    for (int nt = 0; nt < 2; ++nt) {
+      const float am = fmaxf(amax[nt], xo[16 * nt + c]);
+      const int qe = am > 0.f ? 14 - ilogbf(am) : 0;
+      qscale[nt] = ldexpf(1.f, qe);
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        qb[kk][2 * e2] = (_Float16)__builtin_bit_cast(float, w[e2] << 16);
-        qb[kk][2 * e2 + 1] = (_Float16)__builtin_bit_cast(float, w[e2] & 0xFFFF0000u);
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        const u32x4 w = qraw[nt][kk];
+        f16x2 h2[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
+                         (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
+        qb[nt][kk] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
+                                             __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3,
+                                             4, 5, 6, 7);
       }
     }
   }
+  const float sl2[2] = {p.scale * kLog2eM / qscale[0], p.scale * kLog2eM / qscale[1]};
 
-  float m = kNegInf, l = 0.f, ps_prev = 1.f;
-  f32x4 o[32];  // O^T tiles (in units of the current page scale): dims 16*mt + 4*g + i of row c
+  float mref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  float ps_ref = 1.f;  // the accumulator is in units of ps_ref
+  f32x4 o[2][kVTiles];  // O^T tiles: dims 256 hh + 16 mt + 4 g + i of row (nt, c)
 #pragma unroll
-  for (int mt = 0; mt < 32; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int j_begin = chunk * p.chunk_pages;
   const int j_end = min(pp.n_local, j_begin + p.chunk_pages);
   const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
   const uint8_t* pool = p.pools[d] + (int64_t)p.layer * p.pages_per_layer * p.page_bytes;
   const uint16_t* scl = p.scales[d] + (int64_t)p.layer * p.pages_per_layer;
-
-  u32x4 raw[kChunksPerThread];
-  int jj = j_begin;
-  int32_t slot = -1;
-  for (; jj < j_end; ++jj) {
-    slot = bt[jj];
-    if (slot >= 0 && slot < p.pages_per_layer) break;
+  // Block-table entries come in windows of 64 (one per lane, the next window loaded a whole
+  // window ahead) and page scales one page ahead, so no dependent load sits between a barrier
+  // and the next page's copies.  Entries outside [0, pages_per_layer) are skipped.
+  auto ok = [&](int32_t sl) { return sl >= 0 && (int64_t)sl < p.pages_per_layer; };
+  int wbase = j_begin;
+  int32_t win0 = j_begin + lane < j_end ? bt[j_begin + lane] : -1;
+  int32_t win1 = j_begin + 64 + lane < j_end ? bt[j_begin + 64 + lane] : -1;
+  int32_t slot_cur = __builtin_amdgcn_readlane(win0, 0);
+  uint16_t sc_cur = 0, sc_nxt = 0;
+  if (j_begin < j_end && ok(slot_cur)) {
+    issue_page(pool + (int64_t)slot_cur * p.page_bytes, s_raw[0], wave, lane);
+    sc_cur = scl[slot_cur];
   }
-  float pscale = 1.f;
-  if (jj < j_end) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(pool + (int64_t)slot * p.page_bytes);
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) raw[i] = __builtin_nontemporal_load(src + tid + 256 * i);
-    pscale = bf16_to_float(scl[slot]);
-  }
-
-  while (jj < j_end) {
+  int buf = 0;
+  for (int jj = j_begin; jj < j_end; ++jj) {
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of page jj (and the prefetched words) have landed
+    __syncthreads();                // ... and everyone's; the other buffer and the swap area are free
+    if (jj + 1 - wbase == 64) {
+      wbase += 64;
+      win0 = win1;
+      win1 = wbase + 64 + lane < j_end ? bt[wbase + 64 + lane] : -1;
+    }
+    const int32_t slot_nxt = jj + 1 < j_end ? __builtin_amdgcn_readlane(win0, jj + 1 - wbase) : -1;
+    if (ok(slot_nxt)) {
+      issue_page(pool + (int64_t)slot_nxt * p.page_bytes, s_raw[buf ^ 1], wave, lane);
+      sc_nxt = scl[slot_nxt];
+    }
+    if (ok(slot_cur)) {
     const int64_t pos0 = ((int64_t)jj * p.n + d) * kMlaPage;
     const int64_t rem = (int64_t)T - pos0;
     const int valid = rem < kMlaPage ? (int)rem : kMlaPage;
-    const float ps = fmaxf(pscale, 1e-30f);
-    __syncthreads();  // every wave is done reading the previous tile
-#pragma unroll
-    for (int i = 0; i < kChunksPerThread; ++i) {
-      const int q = tid + 256 * i;
-      const int r = q / 36, cc = q - r * 36;
-      u32x4 h0, h1;
-      if (r < valid) {
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          h0[2 * e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i][e2], 1.0f, false));
-          h0[2 * e2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i][e2], 1.0f, true));
-          h1[2 * e2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i][2 + e2], 1.0f, false));
-          h1[2 * e2 + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[i][2 + e2], 1.0f, true));
-        }
-      } else {
-        h0 = u32x4{0, 0, 0, 0};
-        h1 = u32x4{0, 0, 0, 0};
+    const bool full = pos0 + kMlaPage - 1 <= (int64_t)T - p.q_len;  // no row masks a token of this page
+    const float ps = fmaxf(bf16_to_float(sc_cur), 1e-30f);
+    uint8_t* cur = s_raw[buf];
+    if (valid < kMlaPage) {  // tail of the last page: no code past T reaches a product
+      for (int i = tid; i < (kMlaPage - valid) * 36; i += 256) {
+        const int r = valid + i / 36, cc = i - (i / 36) * 36;
+        *reinterpret_cast<u32x4*>(cur + r * kRawStride + 16 * cc) = u32x4{0, 0, 0, 0};
       }
-      u32x4* dst = reinterpret_cast<u32x4*>(&s_tile[r * kTileStride + 32 * cc]);
-      dst[0] = h0;
-      dst[1] = h1;
-    }
-    __syncthreads();
-    // next page in flight while this one is computed
-    int jn = jj + 1;
-    for (; jn < j_end; ++jn) {
-      slot = bt[jn];
-      if (slot >= 0 && slot < p.pages_per_layer) break;
-    }
-    if (jn < j_end) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(pool + (int64_t)slot * p.page_bytes);
-#pragma unroll
-      for (int i = 0; i < kChunksPerThread; ++i) raw[i] = __builtin_nontemporal_load(src + tid + 256 * i);
-      pscale = bf16_to_float(scl[slot]);
+      __syncthreads();
     }
 
-    // ---- S^T = K Q^T: tile tt covers tokens 16*tt + m; lane gets tokens 16*tt + 4*g + i of row c
-    f32x4 s[4];
+    // ---- partial S^T = K Q^T over this half's dims, both column tiles
+    f32x4 s[2][4];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = &s_tile[(16 * tt + c) * kTileStride + 16 * g];
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int kk = 0; kk < 18; ++kk) {
-        const f16x8 a = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 64 * kk));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[kk], acc, 0, 0, 0);
+      for (int tt = 0; tt < 4; ++tt) s[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* krow = cur + kHalfQk * hh + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < kQSteps; ++kk) {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(krow + mla_tok(tt, c) * kRawStride + 32 * kk);
+        const f16x8 a = cvt8(x);
+        s[0][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[0][kk], s[0][tt], 0, 0, 0);
+        s[1][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[1][kk], s[1][tt], 0, 0, 0);
       }
-      s[tt] = acc;
     }
-    // ---- online softmax
-    const float f = sl2 * ps;
-    float mx = kNegInf;
+    // ---- swap partials with the partner wavefront; both then hold the same full scores
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t pos = pos0 + 16 * tt + 4 * g + i;
-        const float v = pos <= lim ? s[tt][i] * f : kNegInf;
-        s[tt][i] = v;
-        mx = fmaxf(mx, v);
+      for (int tt = 0; tt < 4; ++tt) s_x[wave][4 * nt + tt][lane] = __builtin_bit_cast(u32x4, s[nt][tt]);
+    __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) s[nt][tt] += __builtin_bit_cast(f32x4, s_x[wave ^ 2][4 * nt + tt][lane]);
+
+    // ---- row maxima in log2 units (lane: row (nt, c), tokens mla_tok(tt, 4g + i))
+    float f[2], mx[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f[nt] = sl2[nt] * ps;
+      if (!full) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (pos0 + mla_tok(tt, 4 * g + i) > lim[nt]) s[nt][tt][i] = kNegInf;
       }
-    mx = mgrp4_max(mx);
-    const float mn = fmaxf(m, mx);
-    const float alpha = (m == kNegInf) ? 0.f : exp2f(m - mn);
-    m = mn;
-    float psum = 0.f;
-    f16x8 pb[2];  // P^T operands: k-step ks holds tokens 32ks + 4g + [0,4) and 32ks + 16 + 4g + [0,4)
+      float v_max = kNegInf;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+      for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = (s[tt][i] == kNegInf) ? 0.f : exp2f(s[tt][i] - mn);
-        psum += x;
-        pb[tt >> 1][4 * (tt & 1) + i] = (_Float16)x;
+        for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, s[nt][tt][i]);
+      mx[nt] = mgrp4_max(v_max) * f[nt];
+    }
+    // ---- move the references when a row's maximum outgrows its offset or the scale drifts
+    const float ratio = ps / ps_ref;
+    const bool move = mx[0] > mref[0] + kTau || mx[1] > mref[1] + kTau;
+    if (__any(move) || ratio > 4.f || ratio < 0.25f) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float mn = fmaxf(mref[nt], mx[nt]);
+        const float a = mref[nt] == kNegInf ? 0.f : exp2f(mref[nt] - mn);
+        mref[nt] = mn;
+        l[nt] *= a;
+        const float fo = a * (ps_ref / ps);
+        // the product goes back through an MFMA (adding 0 x 0) so the accumulator keeps one
+        // register class across the loop and the common path carries no copies
+        const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int mt = 0; mt < kVTiles; ++mt) {
+          asm volatile("" : "+a"(o[nt][mt]));  // read the accumulator here, not ahead of the branch
+          o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z, z, o[nt][mt] * fo, 0, 0, 0);
+        }
       }
-    l = l * alpha + mgrp4_sum(psum);
-    // ---- O^T = (alpha * ps_prev / ps) O^T + V^T P^T   (accumulator in units of this page's scale)
-    const float resc = alpha * (ps_prev / ps);
-    ps_prev = ps;
-    // V^T via transposing reads: source lane 4k + q of group g points at token
-    // (32ks + 16*half + 4g + k), dims 16*mt + 4q .. +3
-    const int kq = c >> 2, qq = c & 3;
+      ps_ref = ps;
+    }
+    // ---- P' = 2^(x - mref) * ps / ps_ref (fp16), l += sum 2^(x - mref)
+    const float lr = __builtin_amdgcn_logf(ps / ps_ref);
+    const float inv_ratio = ps_ref / ps;
+    f16x8 pb[2][2];
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      f32x4 acc = o[mt] * resc;
+    for (int nt = 0; nt < 2; ++nt) {
+      const float off = mref[nt] == kNegInf ? 0.f : mref[nt] - lr;  // -inf only if every score so far is masked
+      float psum = 0.f;
+      f16x4 ph[4];
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        float x4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = __builtin_amdgcn_exp2f(fmaf(s[nt][tt][i], f[nt], -off));
+          psum += x;
+          x4[i] = x;
+        }
+        ph[tt] = f16x4{(_Float16)x4[0], (_Float16)x4[1], (_Float16)x4[2], (_Float16)x4[3]};
+      }
+      // k step ks: tokens 32ks + 8g + [0, 4) from tile 2ks, + [4, 8) from tile 2ks + 1
+      pb[nt][0] = __builtin_shufflevector(ph[0], ph[1], 0, 1, 2, 3, 4, 5, 6, 7);
+      pb[nt][1] = __builtin_shufflevector(ph[2], ph[3], 0, 1, 2, 3, 4, 5, 6, 7);
+      l[nt] += mgrp4_sum(psum) * inv_ratio;
+    }
+    // ---- O^T += V^T P^T over this half's value dims
+    // source lane (g, c) of the transposing read points at token 32ks + 8g + (c >> 1),
+    // dims 16*mt + 8*(c & 1) .. +7; lane (g, j) then holds dim 16*mt + j of those 8 tokens
+    const uint8_t* vrow = cur + (8 * g + (c >> 1)) * kRawStride + 8 * (c & 1) + kHalfV * hh;
+#pragma unroll
+    for (int mt = 0; mt < kVTiles; ++mt) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const int tok0 = 32 * ks + 4 * g + kq;
-        const uint8_t* a0 = &s_tile[tok0 * kTileStride + 2 * (16 * mt + 4 * qq)];
-        const uint8_t* a1 = a0 + 16 * kTileStride;
-        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a1));
-        // whole-vector casts: an element-by-element rebuild of these results was
-        // miscompiled (every element became element 0)
-        const f16x8 av = __builtin_shufflevector(__builtin_bit_cast(f16x4, v0), __builtin_bit_cast(f16x4, v1),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[ks], acc, 0, 0, 0);
+        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * mt));
+        const f16x8 a = cvt8(__builtin_bit_cast(u32x2, v));
+        o[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[0][ks], o[0][mt], 0, 0, 0);
+        o[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[1][ks], o[1][mt], 0, 0, 0);
       }
-      o[mt] = acc;
     }
-    jj = jn;
+    }
+    slot_cur = slot_nxt;
+    sc_cur = sc_nxt;
+    buf ^= 1;
   }
 
-  // ---- write the (chunk) partial of row c: O = ps_last * O^T / l
-  if (row_ok) {
-    const bool direct = pp.k == 1;
-    const int64_t orow = (int64_t)t_q * p.hq + h_q;
-    const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
-    const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
-    float* dst = direct ? p.partial_out + (pair_row0 + orow) * kMlaDv : p.ws_o + (ws_row0 + orow) * kMlaDv;
-    const float inv = l > 0.f ? ps_prev / l : 0.f;
+  // ---- write the (chunk) partial of the lane's two rows, this half's dims: O = ps_ref * O^T / l
+  const bool direct = pp.k == 1;
+  const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
+  const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
 #pragma unroll
-    for (int mt = 0; mt < 32; ++mt) {
-      const f32x4 v = o[mt] * inv;
+  for (int nt = 0; nt < 2; ++nt) {
+    if (rowq[nt] < 0) continue;
+    const int r = rowq[nt];
+    float* dst = (direct ? p.partial_out + (pair_row0 + r) * kMlaDv : p.ws_o + (ws_row0 + r) * kMlaDv) +
+                 kHalfV * hh;
+    const float inv = l[nt] > 0.f ? ps_ref / l[nt] : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < kVTiles; ++mt) {
+      const f32x4 v = o[nt][mt] * inv;
       *reinterpret_cast<float4*>(dst + 16 * mt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    if (g == 0) {
-      const float lse = l > 0.f ? (m + log2f(l)) * kLn2M : kNegInf;
+    if (g == 0 && hh == 0) {
+      const float lse = l[nt] > 0.f ? (mref[nt] + log2f(l[nt])) * kLn2M : kNegInf;
       if (direct)
-        p.partial_lse[pair_row0 + orow] = lse;
+        p.partial_lse[pair_row0 + r] = lse;
       else
-        p.ws_lse[ws_row0 + orow] = lse;
+        p.ws_lse[ws_row0 + r] = lse;
     }
   }
 }
@@ -280,6 +410,8 @@ bool mla_fp8_supported(const dcp_attn_desc& D) {
   return D.kv_layout == DCPKV_LAYOUT_MLA && D.kv_dtype == DCPKV_KV_FP8E4M3 && D.q_dtype == DCPKV_Q_BF16 &&
          D.head_dim_qk == kMlaDim && D.head_dim_v == kMlaDv && D.num_kv_heads == 1 && D.page_size == kMlaPage;
 }
+
+int mla_fp8_rows_per_block() { return kMlaRowsPerBlock; }
 
 int launch_mla_fp8(const AttnParams& p, const dcp_attn_desc& D, int64_t item_bound, hipStream_t st) {
   (void)D;
