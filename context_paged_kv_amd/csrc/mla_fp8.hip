@@ -12,19 +12,21 @@
 // about 480 flop per KV byte, so the matrix cores bind, not HBM.
 //
 // Work item: (shard d, request b, chunk of local pages, block of 64 query
-// rows).  A workgroup of four wavefronts owns one item.  Wavefronts w and
-// w ^ 2 form a pair that owns 32 rows (two N = 16 column tiles, so every
-// operand a wavefront converts feeds two MFMAs); half hh = w >> 1 of the pair
+// rows).  A workgroup owns one item.  Its wavefronts come in pairs (w and
+// w ^ kPairStride) that own kNT column tiles of 16 rows each; half
+// hh = w / kPairStride of the pair
 //   * computes the scores over dims [288 hh, 288 hh + 288) and swaps that
 //     partial S^T with its partner through LDS, so both hold the full scores
 //     (the same sum, bit for bit, hence the same softmax decisions);
 //   * accumulates O over the value dims [256 hh, 256 hh + 256).
-// That keeps a wavefront's accumulator at 128 registers next to the 32 of the
-// score tile, so nothing is shuffled between register files.  Per page:
-//   * the 36 KB of fp8 codes go global -> LDS with global_load_lds_dwordx4
-//     (no registers), double buffered: page j+1 streams in while page j is
-//     computed.  LDS rows are 592 bytes (576 + 16 pad): the transposing reads
-//     below are bank-conflict free, the K reads at most two-way;
+// With kNT = 1 a wavefront needs about 130 registers, so two run on each SIMD
+// and hide each other's latencies; with kNT = 2 every converted operand feeds
+// two MFMAs but only one wavefront fits per SIMD.  Per page:
+//   * the 36 KB of fp8 codes are double buffered in LDS: the loads of page
+//     j+1 go out between the score MFMAs of page j and land in registers,
+//     and are written to the other buffer between its PV MFMAs (copies into
+//     LDS by DMA were slower to issue and held up the wave's LDS reads).
+//     LDS rows are 592 bytes (576 + 16 pad);
 //   * S^T = K Q^T on v_mfma_f32_16x16x32_f16: each lane reads 8 codes of one
 //     token (ds_read_b64) and converts them exactly to fp16 with
 //     v_cvt_scalef32_pk_f16_fp8.  Q is held in fp16, each row scaled by a
@@ -57,12 +59,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
-typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kMlaPage = 64;
 constexpr int kMlaDim = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaRowsPerBlock = 64;
+#ifndef MLA_NT
+#define MLA_NT 2
+#endif
+constexpr int kNT = MLA_NT;                          // 16-row column tiles per wavefront
+constexpr int kWaves = 8 / kNT;                      // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPairStride = kWaves / 2;              // partner of wave w is w ^ kPairStride
 constexpr int kHalfQk = kMlaDim / 2;                // 288 score dims per wavefront
 constexpr int kHalfV = kMlaDv / 2;                  // 256 value dims per wavefront
 constexpr int kQSteps = kHalfQk / 32;               // 9 k-steps of 32 dims
@@ -71,18 +79,39 @@ constexpr int kRawStride = 592;                     // LDS bytes per token row o
 constexpr int kRawBuf = kMlaPage * kRawStride;      // 37888 bytes per page buffer
 constexpr int kSlotsPerRow = kRawStride / 16;       // 37 16-byte slots (36 data + 1 pad)
 constexpr int kSlots = kMlaPage * kSlotsPerRow;     // 2368
-constexpr int kLoadIters = (kSlots + 255) / 256;    // 10
+constexpr int kLoadIters = (kSlots + kThreads - 1) / kThreads;  // copy instructions per wave and page
+constexpr int kWaitLgkm0 = 0xC07F;                 // s_waitcnt lgkmcnt(0), other counters untouched
 constexpr float kTau = 8.f;                         // lazy-rescale threshold (log2 units)
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;
 
+// Reductions over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one MFMA column).
+// v_permlane16_swap a, b (v_permlane32_swap a, b) with a = b = v leaves, in
+// every lane, v[l] and v[l ^ 16] (v[l ^ 32]) in the two registers.  Written as
+// asm with both registers as operands: the compiler's builtin for these
+// instructions loses track of the second result.  The s_nop gives the two wait
+// states a swap needs after a VALU write of its operands.
+__device__ __forceinline__ void xpair16(float v, float& a, float& b) {
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void xpair32(float v, float& a, float& b) {
+  a = v;
+  b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
 __device__ __forceinline__ float mgrp4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  float a, b;
+  xpair16(v, a, b);
+  xpair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
 }
 __device__ __forceinline__ float mgrp4_sum(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  float a, b;
+  xpair16(v, a, b);
+  xpair32(a + b, a, b);
+  return a + b;
 }
 
 // Eight fp8 e4m3fn codes (two dwords) to eight fp16 values, exactly.
@@ -104,28 +133,31 @@ __device__ __forceinline__ int mla_tok(int tt, int m) {
 // Start the global -> LDS copy of one page of codes into a 592-byte-row buffer.
 // LDS slot q (16 bytes) of row q / 37, column q % 37 holds page bytes
 // 16 * (q - q / 37) onwards; the pad column refetches a valid chunk.
-__device__ __forceinline__ void issue_page(const uint8_t* page, uint8_t* buf, int wave, int lane) {
-  int ln = lane;
-  asm volatile("" : "+v"(ln));  // recompute the offsets per page instead of holding ten of them
+// Per-lane source offsets of the page copy: load i of wave w moves the 64
+// consecutive 16-byte LDS slots from kThreads * i + 64 * w (none past the page;
+// the pad column of a row refetches a valid chunk).
+struct CopyPlan {
+  uint32_t off[kLoadIters];
+};
+__device__ __forceinline__ CopyPlan copy_plan(int wave, int lane) {
+  CopyPlan cp;
 #pragma unroll
   for (int i = 0; i < kLoadIters; ++i) {
-    const int base = 256 * i + 64 * wave;  // first slot of this wave's instruction (wave-uniform)
-    if (base < kSlots) {
-      const int slot = base + ln;            // < kSlots: kSlots is a multiple of 64
-      const int row = slot / kSlotsPerRow;
-      const int src = min(16 * (slot - row), kMlaPage * kMlaDim - 16);
-      __builtin_amdgcn_global_load_lds(page + src, (lds_void*)(buf + 16 * base), 16, 0, 0);
-    }
+    const int slot = kThreads * i + 64 * wave + lane;
+    const int row = slot / kSlotsPerRow;
+    cp.off[i] = (uint32_t)min(16 * (slot - row), kMlaPage * kMlaDim - 16);
   }
+  return cp;
 }
 
-__global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBuf];  // 75776 B
-  __shared__ u32x4 s_x[4][8][64];                                     // score-partial swap, 32768 B
+  __shared__ u32x4 s_x[kWaves][4 * kNT][64];                          // score-partial swap, 32768 B
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rp = wave & 1, hh = wave >> 1;
+  const int rq = wave % kPairStride, hh = wave / kPairStride;
+  const int partner = wave ^ kPairStride;
   const int g = lane >> 4, c = lane & 15;
 
   // items sharing a chunk run on the same XCD (dispatch is round robin over 8)
@@ -151,15 +183,15 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int T = p.seq_lens[b];
 
-  // the lane's two query rows (one per N tile) and their queries over this half's dims
+  // the lane's query rows (one per column tile) and their queries over this half's dims
   // (B operand of S^T: dims 288 hh + 32 kk + 8 g + [0, 8)), as fp16 scaled by 2^qe
-  int rowq[2];
-  int64_t lim[2];
-  float amax[2];
-  u32x4 qraw[2][kQSteps];
+  int rowq[kNT];
+  int64_t lim[kNT];
+  float amax[kNT];
+  u32x4 qraw[kNT][kQSteps];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int r = hb * kMlaRowsPerBlock + 32 * rp + 16 * nt + c;
+  for (int nt = 0; nt < kNT; ++nt) {
+    const int r = hb * kMlaRowsPerBlock + 16 * (kNT * rq + nt) + c;
     const bool ok = r < p.rows;
     rowq[nt] = ok ? r : -1;
     const int t = ok ? r / p.hq : 0, h = ok ? r % p.hq : 0;
@@ -181,16 +213,16 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
   // both halves of a row use one scale: swap the half maxima once
   if (g == 0) {
     float* xm = reinterpret_cast<float*>(&s_x[wave][0][0]);
-    xm[c] = amax[0];
-    xm[16 + c] = amax[1];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) xm[16 * nt + c] = amax[nt];
   }
   __syncthreads();
-  float qscale[2];  // 2^qe: the row's largest |q| lands in [2^14, 2^15)
-  f16x8 qb[2][kQSteps];
+  float qscale[kNT];  // 2^qe: the row's largest |q| lands in [2^14, 2^15)
+  f16x8 qb[kNT][kQSteps];
   {
-    const float* xo = reinterpret_cast<const float*>(&s_x[wave ^ 2][0][0]);
+    const float* xo = reinterpret_cast<const float*>(&s_x[partner][0][0]);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < kNT; ++nt) {
       const float am = fmaxf(amax[nt], xo[16 * nt + c]);
       const int qe = am > 0.f ? 14 - ilogbf(am) : 0;
       qscale[nt] = ldexpf(1.f, qe);
@@ -208,13 +240,17 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
       }
     }
   }
-  const float sl2[2] = {p.scale * kLog2eM / qscale[0], p.scale * kLog2eM / qscale[1]};
-
-  float mref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
-  float ps_ref = 1.f;  // the accumulator is in units of ps_ref
-  f32x4 o[2][kVTiles];  // O^T tiles: dims 256 hh + 16 mt + 4 g + i of row (nt, c)
+  float sl2[kNT], mref[kNT], l[kNT];  // l: this lane's share of the row's denominator
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < kNT; ++nt) {
+    sl2[nt] = p.scale * kLog2eM / qscale[nt];
+    mref[nt] = kNegInf;
+    l[nt] = 0.f;
+  }
+  float ps_ref = 1.f;  // the accumulator is in units of ps_ref
+  f32x4 o[kNT][kVTiles];  // O^T tiles: dims 256 hh + 16 mt + 4 g + i of row (nt, c)
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -232,8 +268,22 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
   int32_t win1 = j_begin + 64 + lane < j_end ? bt[j_begin + 64 + lane] : -1;
   int32_t slot_cur = __builtin_amdgcn_readlane(win0, 0);
   uint16_t sc_cur = 0, sc_nxt = 0;
+  // The page copy goes through registers: load i of page j + 1 is issued next to k-step i of
+  // page j's scores and written to the other LDS buffer next to the last M tiles of page j's
+  // PV, so both hide behind MFMAs.
+  const CopyPlan cp = copy_plan(wave, lane);
   if (j_begin < j_end && ok(slot_cur)) {
-    issue_page(pool + (int64_t)slot_cur * p.page_bytes, s_raw[0], wave, lane);
+    const uint8_t* page = pool + (int64_t)slot_cur * p.page_bytes;
+    u32x4 stg[kLoadIters];
+#pragma unroll
+    for (int i = 0; i < kLoadIters; ++i)
+      if (kThreads * i + 64 * wave < kSlots)
+        stg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(page + cp.off[i]));
+#pragma unroll
+    for (int i = 0; i < kLoadIters; ++i) {
+      const int base = kThreads * i + 64 * wave;
+      if (base < kSlots) *reinterpret_cast<u32x4*>(s_raw[0] + 16 * (base + lane)) = stg[i];
+    }
     sc_cur = scl[slot_cur];
   }
   int buf = 0;
@@ -246,134 +296,177 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
       win1 = wbase + 64 + lane < j_end ? bt[wbase + 64 + lane] : -1;
     }
     const int32_t slot_nxt = jj + 1 < j_end ? __builtin_amdgcn_readlane(win0, jj + 1 - wbase) : -1;
-    if (ok(slot_nxt)) {
-      issue_page(pool + (int64_t)slot_nxt * p.page_bytes, s_raw[buf ^ 1], wave, lane);
-      sc_nxt = scl[slot_nxt];
+    const bool have_nxt = ok(slot_nxt);
+    const uint8_t* npage = pool + (int64_t)(have_nxt ? slot_nxt : 0) * p.page_bytes;
+    uint8_t* nbuf = s_raw[buf ^ 1];
+    u32x4 stg[kLoadIters];  // page j + 1 on its way to the other buffer
+    auto ld = [&](int i) {
+      if (have_nxt && kThreads * i + 64 * wave < kSlots)
+        stg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(npage + cp.off[i]));
+    };
+    auto st = [&](int i) {
+      const int base = kThreads * i + 64 * wave;
+      if (have_nxt && base < kSlots) *reinterpret_cast<u32x4*>(nbuf + 16 * (base + lane)) = stg[i];
+    };
+    if (have_nxt) sc_nxt = scl[slot_nxt];
+    if (!ok(slot_cur)) {
+#pragma unroll
+      for (int i = 0; i < kLoadIters; ++i) ld(i);
+#pragma unroll
+      for (int i = 0; i < kLoadIters; ++i) st(i);
     }
     if (ok(slot_cur)) {
-    const int64_t pos0 = ((int64_t)jj * p.n + d) * kMlaPage;
-    const int64_t rem = (int64_t)T - pos0;
-    const int valid = rem < kMlaPage ? (int)rem : kMlaPage;
-    const bool full = pos0 + kMlaPage - 1 <= (int64_t)T - p.q_len;  // no row masks a token of this page
-    const float ps = fmaxf(bf16_to_float(sc_cur), 1e-30f);
-    uint8_t* cur = s_raw[buf];
-    if (valid < kMlaPage) {  // tail of the last page: no code past T reaches a product
-      for (int i = tid; i < (kMlaPage - valid) * 36; i += 256) {
-        const int r = valid + i / 36, cc = i - (i / 36) * 36;
-        *reinterpret_cast<u32x4*>(cur + r * kRawStride + 16 * cc) = u32x4{0, 0, 0, 0};
+      const int64_t pos0 = ((int64_t)jj * p.n + d) * kMlaPage;
+      const int64_t rem = (int64_t)T - pos0;
+      const int valid = rem < kMlaPage ? (int)rem : kMlaPage;
+      const bool full = pos0 + kMlaPage - 1 <= (int64_t)T - p.q_len;  // no row masks a token of this page
+      const float ps = fmaxf(bf16_to_float(sc_cur), 1e-30f);
+      uint8_t* cur = s_raw[buf];
+      if (valid < kMlaPage) {  // tail of the last page: no code past T reaches a product
+        for (int i = tid; i < (kMlaPage - valid) * 36; i += kThreads) {
+          const int r = valid + i / 36, cc = i - (i / 36) * 36;
+          *reinterpret_cast<u32x4*>(cur + r * kRawStride + 16 * cc) = u32x4{0, 0, 0, 0};
+        }
+        __syncthreads();
       }
-      __syncthreads();
-    }
 
-    // ---- partial S^T = K Q^T over this half's dims, both column tiles
-    f32x4 s[2][4];
+      // ---- partial S^T = K Q^T over this half's dims
+      f32x4 s[kNT][4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) s[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const uint8_t* krow = cur + kHalfQk * hh + 8 * g;
+        for (int tt = 0; tt < 4; ++tt) s[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* krow = cur + kHalfQk * hh + 8 * g;
+      u32x2 kx[2][4];  // codes of k-steps kk (in use) and kk + 1 (in flight)
 #pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk) {
+      for (int tt = 0; tt < 4; ++tt) kx[0][tt] = *reinterpret_cast<const u32x2*>(krow + mla_tok(tt, c) * kRawStride);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const u32x2 x = *reinterpret_cast<const u32x2*>(krow + mla_tok(tt, c) * kRawStride + 32 * kk);
-        const f16x8 a = cvt8(x);
-        s[0][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[0][kk], s[0][tt], 0, 0, 0);
-        s[1][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[1][kk], s[1][tt], 0, 0, 0);
+      for (int kk = 0; kk < kQSteps; ++kk) {
+        ld(kk);
+        if (kk == kQSteps - 1) {
+#pragma unroll
+          for (int i = kQSteps; i < kLoadIters; ++i) ld(i);
+        }
+        if (kk + 1 < kQSteps) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+            kx[(kk + 1) & 1][tt] =
+                *reinterpret_cast<const u32x2*>(krow + mla_tok(tt, c) * kRawStride + 32 * (kk + 1));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          const f16x8 a = cvt8(kx[kk & 1][tt]);
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            s[nt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[nt][kk], s[nt][tt], 0, 0, 0);
+        }
       }
-    }
-    // ---- swap partials with the partner wavefront; both then hold the same full scores
+      // ---- swap partials with the partner wavefront; both then hold the same full scores
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) s_x[wave][4 * nt + tt][lane] = __builtin_bit_cast(u32x4, s[nt][tt]);
-    __syncthreads();
+        for (int tt = 0; tt < 4; ++tt) s_x[wave][4 * nt + tt][lane] = __builtin_bit_cast(u32x4, s[nt][tt]);
+      // LDS writes done, then a bare barrier: a full __syncthreads would also wait for the
+      // next page's copy, which is still in flight
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_s_barrier();
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) s[nt][tt] += __builtin_bit_cast(f32x4, s_x[wave ^ 2][4 * nt + tt][lane]);
+        for (int tt = 0; tt < 4; ++tt) s[nt][tt] += __builtin_bit_cast(f32x4, s_x[partner][4 * nt + tt][lane]);
 
-    // ---- row maxima in log2 units (lane: row (nt, c), tokens mla_tok(tt, 4g + i))
-    float f[2], mx[2];
+      // ---- row maxima in log2 units (lane: row (nt, c), tokens mla_tok(tt, 4g + i))
+      float f[kNT], mx[kNT];
+      bool move = false;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f[nt] = sl2[nt] * ps;
-      if (!full) {
+      for (int nt = 0; nt < kNT; ++nt) {
+        f[nt] = sl2[nt] * ps;
+        if (!full) {
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (pos0 + mla_tok(tt, 4 * g + i) > lim[nt]) s[nt][tt][i] = kNegInf;
+        }
+        float v_max = kNegInf;
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (pos0 + mla_tok(tt, 4 * g + i) > lim[nt]) s[nt][tt][i] = kNegInf;
+          for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, s[nt][tt][i]);
+        mx[nt] = v_max * f[nt];  // this lane's 16 scores; the row maximum is formed only on a move
+        move = move || mx[nt] > mref[nt] + kTau;
       }
-      float v_max = kNegInf;
+      // ---- move the references when a row's maximum outgrows its offset or the scale drifts
+      const float ratio = ps * __builtin_amdgcn_rcpf(ps_ref);  // page scales are normal bf16 values
+      if (__any(move) || ratio > 4.f || ratio < 0.25f) {
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+        for (int nt = 0; nt < kNT; ++nt) {
+          const float mn = fmaxf(mref[nt], mgrp4_max(mx[nt]));
+          const float a = mref[nt] == kNegInf ? 0.f : exp2f(mref[nt] - mn);
+          mref[nt] = mn;
+          l[nt] *= a;
+          const float fo = a * ps_ref * __builtin_amdgcn_rcpf(ps);
+          // the product goes back through an MFMA (adding 0 x 0) so the accumulator keeps one
+          // register class across the loop and the common path carries no copies
+          const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, s[nt][tt][i]);
-      mx[nt] = mgrp4_max(v_max) * f[nt];
-    }
-    // ---- move the references when a row's maximum outgrows its offset or the scale drifts
-    const float ratio = ps / ps_ref;
-    const bool move = mx[0] > mref[0] + kTau || mx[1] > mref[1] + kTau;
-    if (__any(move) || ratio > 4.f || ratio < 0.25f) {
+          for (int mt = 0; mt < kVTiles; ++mt) {
+            asm volatile("" : "+a"(o[nt][mt]));  // read the accumulator here, not ahead of the branch
+            o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z, z, o[nt][mt] * fo, 0, 0, 0);
+          }
+        }
+        ps_ref = ps;
+      }
+      // ---- P' = 2^(x - mref) * ps / ps_ref (fp16), l += sum 2^(x - mref)
+      const float lr = __builtin_amdgcn_logf(ps * __builtin_amdgcn_rcpf(ps_ref));
+      const float inv_ratio = ps_ref * __builtin_amdgcn_rcpf(ps);
+      f16x8 pb[kNT][2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const float mn = fmaxf(mref[nt], mx[nt]);
-        const float a = mref[nt] == kNegInf ? 0.f : exp2f(mref[nt] - mn);
-        mref[nt] = mn;
-        l[nt] *= a;
-        const float fo = a * (ps_ref / ps);
-        // the product goes back through an MFMA (adding 0 x 0) so the accumulator keeps one
-        // register class across the loop and the common path carries no copies
-        const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+      for (int nt = 0; nt < kNT; ++nt) {
+        const float off = mref[nt] == kNegInf ? 0.f : mref[nt] - lr;  // -inf only if every score so far is masked
+        float psum = 0.f;
+        f16x4 ph[4];
 #pragma unroll
-        for (int mt = 0; mt < kVTiles; ++mt) {
-          asm volatile("" : "+a"(o[nt][mt]));  // read the accumulator here, not ahead of the branch
-          o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z, z, o[nt][mt] * fo, 0, 0, 0);
+        for (int tt = 0; tt < 4; ++tt) {
+          float x4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = __builtin_amdgcn_exp2f(fmaf(s[nt][tt][i], f[nt], -off));
+            psum += x;
+            x4[i] = x;
+          }
+          ph[tt] = f16x4{(_Float16)x4[0], (_Float16)x4[1], (_Float16)x4[2], (_Float16)x4[3]};
+        }
+        // k step ks: tokens 32ks + 8g + [0, 4) from tile 2ks, + [4, 8) from tile 2ks + 1
+        pb[nt][0] = __builtin_shufflevector(ph[0], ph[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        pb[nt][1] = __builtin_shufflevector(ph[2], ph[3], 0, 1, 2, 3, 4, 5, 6, 7);
+        l[nt] += psum * inv_ratio;  // this lane's part of the row's denominator
+      }
+      // ---- O^T += V^T P^T over this half's value dims
+      // source lane (g, c) of the transposing read points at token 32ks + 8g + (c >> 1),
+      // dims 16*mt + 8*(c & 1) .. +7; lane (g, j) then holds dim 16*mt + j of those 8 tokens
+      const uint8_t* vrow = cur + (8 * g + (c >> 1)) * kRawStride + 8 * (c & 1) + kHalfV * hh;
+      i32x2 vx[2][2];  // codes of M tiles mt (in use) and mt + 1 (in flight)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        vx[0][ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 32 * ks * kRawStride));
+#pragma unroll
+      for (int mt = 0; mt < kVTiles; ++mt) {
+        if (mt >= kVTiles - kLoadIters) st(mt - (kVTiles - kLoadIters));
+        if (mt + 1 < kVTiles) {
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            vx[(mt + 1) & 1][ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * (mt + 1)));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 a = cvt8(__builtin_bit_cast(u32x2, vx[mt & 1][ks]));
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[nt][ks], o[nt][mt], 0, 0, 0);
         }
       }
-      ps_ref = ps;
-    }
-    // ---- P' = 2^(x - mref) * ps / ps_ref (fp16), l += sum 2^(x - mref)
-    const float lr = __builtin_amdgcn_logf(ps / ps_ref);
-    const float inv_ratio = ps_ref / ps;
-    f16x8 pb[2][2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const float off = mref[nt] == kNegInf ? 0.f : mref[nt] - lr;  // -inf only if every score so far is masked
-      float psum = 0.f;
-      f16x4 ph[4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        float x4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = __builtin_amdgcn_exp2f(fmaf(s[nt][tt][i], f[nt], -off));
-          psum += x;
-          x4[i] = x;
-        }
-        ph[tt] = f16x4{(_Float16)x4[0], (_Float16)x4[1], (_Float16)x4[2], (_Float16)x4[3]};
-      }
-      // k step ks: tokens 32ks + 8g + [0, 4) from tile 2ks, + [4, 8) from tile 2ks + 1
-      pb[nt][0] = __builtin_shufflevector(ph[0], ph[1], 0, 1, 2, 3, 4, 5, 6, 7);
-      pb[nt][1] = __builtin_shufflevector(ph[2], ph[3], 0, 1, 2, 3, 4, 5, 6, 7);
-      l[nt] += mgrp4_sum(psum) * inv_ratio;
-    }
-    // ---- O^T += V^T P^T over this half's value dims
-    // source lane (g, c) of the transposing read points at token 32ks + 8g + (c >> 1),
-    // dims 16*mt + 8*(c & 1) .. +7; lane (g, j) then holds dim 16*mt + j of those 8 tokens
-    const uint8_t* vrow = cur + (8 * g + (c >> 1)) * kRawStride + 8 * (c & 1) + kHalfV * hh;
-#pragma unroll
-    for (int mt = 0; mt < kVTiles; ++mt) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * mt));
-        const f16x8 a = cvt8(__builtin_bit_cast(u32x2, v));
-        o[0][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[0][ks], o[0][mt], 0, 0, 0);
-        o[1][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[1][ks], o[1][mt], 0, 0, 0);
-      }
-    }
     }
     slot_cur = slot_nxt;
     sc_cur = sc_nxt;
@@ -384,20 +477,23 @@ __global__ __launch_bounds__(256) void mla_fp8_kernel(AttnParams p) {
   const bool direct = pp.k == 1;
   const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
   const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
+  float lrow[kNT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) lrow[nt] = mgrp4_sum(l[nt]);
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt) {
     if (rowq[nt] < 0) continue;
     const int r = rowq[nt];
     float* dst = (direct ? p.partial_out + (pair_row0 + r) * kMlaDv : p.ws_o + (ws_row0 + r) * kMlaDv) +
                  kHalfV * hh;
-    const float inv = l[nt] > 0.f ? ps_ref / l[nt] : 0.f;
+    const float inv = lrow[nt] > 0.f ? ps_ref / lrow[nt] : 0.f;
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) {
       const f32x4 v = o[nt][mt] * inv;
       *reinterpret_cast<float4*>(dst + 16 * mt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
     }
     if (g == 0 && hh == 0) {
-      const float lse = l[nt] > 0.f ? (mref[nt] + log2f(l[nt])) * kLn2M : kNegInf;
+      const float lse = lrow[nt] > 0.f ? (mref[nt] + log2f(lrow[nt])) * kLn2M : kNegInf;
       if (direct)
         p.partial_lse[pair_row0 + r] = lse;
       else
@@ -418,7 +514,7 @@ int launch_mla_fp8(const AttnParams& p, const dcp_attn_desc& D, int64_t item_bou
   const int64_t chunks_bound = (item_bound + p.hb_count - 1) / p.hb_count;
   const int64_t blocks = ((chunks_bound + 7) / 8) * 8 * p.hb_count;
   if (blocks > INT32_MAX / 256) return set_error(DCPKV_EINVAL, "attn: too many work items");
-  hipLaunchKernelGGL(mla_fp8_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(256), 0, st, p);
+  hipLaunchKernelGGL(mla_fp8_kernel, dim3((unsigned)std::max<int64_t>(blocks, 1)), dim3(kThreads), 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: mla launch: %s", hipGetErrorString(e));
   return DCPKV_OK;
