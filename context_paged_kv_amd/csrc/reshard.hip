@@ -8,12 +8,12 @@
 // position (section 6.3).
 //
 // Work is split into items (layer, entry, segment): each page is cut into
-// equal segments of at most 16 KB so that large pages do not leave a ragged
-// tail of workgroups.  A persistent grid (4 workgroups per compute unit)
-// strides over the items; every thread keeps four 16-byte non-temporal loads
-// in flight before its stores (the data is touched exactly once).  Measured
-// on MI355X this shape streams scattered pages within a few percent of a
-// plain contiguous copy.
+// near-equal segments of at most 36 KB (a whole 576-byte x 64-token fp8 page
+// is one segment).  A persistent grid strides over the items; every thread
+// issues all of its 16-byte non-temporal loads for the segment (up to nine)
+// before its stores, and the page ids of the workgroup's next item are read
+// while the current one is in flight, so neither the id lookup nor the data
+// latency is exposed per item.
 
 #include <hip/hip_runtime.h>
 
@@ -49,9 +49,12 @@ struct ReshardArgs {
 };
 
 constexpr int kReshardThreads = 256;
-constexpr int kReshardUnroll = 4;                                       // 16 KB per round
-constexpr int64_t kReshardSegMax = 16 * kReshardThreads * kReshardUnroll;  // 16384 bytes
-constexpr int kReshardBlocksPerCU = 4;
+constexpr int kReshardUnroll = 9;                                          // 16-byte loads per thread
+constexpr int64_t kReshardSegMax = 16 * kReshardThreads * kReshardUnroll;  // 36864 bytes
+#ifndef RESHARD_BLOCKS_PER_CU
+#define RESHARD_BLOCKS_PER_CU 4
+#endif
+constexpr int kReshardBlocksPerCU = RESHARD_BLOCKS_PER_CU;
 
 // Owner of `layer` under the section 4.1 split, and the first layer it owns.
 __device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_sources, int& r,
@@ -67,16 +70,33 @@ __device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_s
   }
 }
 
+// Entry e of the list: source page id and destination global page (plain loads; the
+// compiler turns them into scalar loads since every lane reads the same word).
+struct ReshardEntry {
+  int64_t g;
+  int32_t sp;
+};
+__device__ __forceinline__ ReshardEntry reshard_entry(const ReshardArgs& a, int64_t it) {
+  ReshardEntry en{-1, -1};
+  if (it < a.items) {
+    const int64_t e = (it % (a.work * a.segs)) / a.segs;
+    en.g = a.dst_ids[a.first + e];
+    en.sp = a.src_ids[a.first + e];
+  }
+  return en;
+}
+
 __global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a) {
+  const int64_t per_layer = a.work * a.segs;
+  ReshardEntry en = reshard_entry(a, blockIdx.x);
   for (int64_t it = blockIdx.x; it < a.items; it += gridDim.x) {
-    const int64_t per_layer = a.work * a.segs;
+    const ReshardEntry nx = reshard_entry(a, it + gridDim.x);  // in flight during this copy
     const int layer = (int)(it / per_layer);
     const int64_t rest = it - (int64_t)layer * per_layer;
-    const int64_t e = rest / a.segs;
-    const int sg = (int)(rest - e * a.segs);
-    const int64_t i = a.first + e;
-    const int64_t g = a.dst_ids[i];
-    const int32_t sp = a.src_ids[i];
+    const int sg = (int)(rest % a.segs);
+    const int64_t g = en.g;
+    const int32_t sp = en.sp;
+    en = nx;
     int d;
     int64_t s;
     if (a.n > 1) {
@@ -100,19 +120,17 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a)
     const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(a.src[r] + src_off);
     u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.dst[d] + dst_off);
     const int64_t len = (a.page_bytes - off) < a.seg_bytes ? (a.page_bytes - off) : a.seg_bytes;
-    const int chunks = (int)(len >> 4);
-    for (int c0 = 0; c0 < chunks; c0 += kReshardThreads * kReshardUnroll) {
-      u32x4 v[kReshardUnroll];
+    const int chunks = (int)(len >> 4);  // <= kReshardThreads * kReshardUnroll
+    u32x4 v[kReshardUnroll];
 #pragma unroll
-      for (int u = 0; u < kReshardUnroll; ++u) {
-        const int c = c0 + u * kReshardThreads + threadIdx.x;
-        if (c < chunks) v[u] = __builtin_nontemporal_load(src + c);
-      }
+    for (int u = 0; u < kReshardUnroll; ++u) {
+      const int c = u * kReshardThreads + threadIdx.x;
+      if (c < chunks) v[u] = __builtin_nontemporal_load(src + c);
+    }
 #pragma unroll
-      for (int u = 0; u < kReshardUnroll; ++u) {
-        const int c = c0 + u * kReshardThreads + threadIdx.x;
-        if (c < chunks) __builtin_nontemporal_store(v[u], dst + c);
-      }
+    for (int u = 0; u < kReshardUnroll; ++u) {
+      const int c = u * kReshardThreads + threadIdx.x;
+      if (c < chunks) __builtin_nontemporal_store(v[u], dst + c);
     }
     if (a.has_scales && sg == 0 && threadIdx.x == 0) {
       a.dst_scale[d][(int64_t)layer * a.dst_pages + s] =
