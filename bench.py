@@ -39,8 +39,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="run one plain torch copy of this many MiB before timing (a known-size kernel "
-                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+                    help="run one plain copy of this many MiB (torch bitwise_not, int32) before timing: a "
+                         "known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_JSON"),
+                    help="no GPU run: turn the counter_collection.csv files of a FETCH_SIZE pass and a "
+                         "WRITE_SIZE pass of this bench (run with --calib-copy-mib) plus the JSON line that "
+                         "run printed into HBM bytes per launch of the dominant kernel, stored in "
+                         "profiles/pmc_traffic.json")
     return ap.parse_args()
 
 
@@ -267,8 +272,79 @@ def cpu_baseline(st, budget_s: float):
             "sample": "float64 numpy oracle, one thread: " + "; ".join(notes) + "; scaled linearly to the full step"}
 
 
+# kernels of each timed call, as rocprofv3 names them
+CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",),
+                "dcp_decode_partial": ("plan_kernel", "gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
+                                       "chunk_reduce_kernel")}
+
+
+def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: int) -> None:
+    """Scale the FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) of the dominant call's kernels by
+    what the same counters read for the calibration copy, and store HBM bytes per launch."""
+    import csv
+    import re
+
+    line = None
+    with open(bench_json) as f:
+        for ln in f:
+            ln = ln.strip()
+            if ln.startswith("{") and '"roofline"' in ln:
+                line = json.loads(ln)
+    if line is None:
+        sys.exit(f"no bench JSON line in {bench_json}")
+    wl, roof = line["config"]["workload"], line["roofline"]
+    call = roof["kernel"].split()[0]
+    names = CALL_KERNELS[call]
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
+        return [rows[k] for k in sorted(rows)]
+
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        ds = per_dispatch(path, counter)
+        calib = [v for k, v in ds if "bitwise_not" in k]
+        if len(calib) != 1:
+            sys.exit(f"{path}: expected one calibration copy dispatch, found {len(calib)}")
+        scale = calib_mib * (1 << 20) / (calib[0] * 1024.0)  # true bytes per counted byte
+        # the timed call's kernels, grouped per launch of the call: one group per launch of its main kernel
+        mine = [(k, v) for k, v in ds if any(re.search(r"\b" + n + r"\b", k) for n in names)]
+        main_name = [n for n in names if n not in ("plan_kernel", "chunk_reduce_kernel")]
+        launches = sum(1 for k, _ in mine if any(n in k for n in main_name))
+        if launches == 0:
+            sys.exit(f"{path}: no dispatch of {names}")
+        out[counter] = {"kib_per_launch": sum(v for _, v in mine) / launches, "scale": scale,
+                        "calib_kib": calib[0], "launches": launches}
+    hbm = sum(out[c]["kib_per_launch"] * 1024.0 * out[c]["scale"] for c in out)
+    key = f"{wl}:{call}"
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            db = json.load(f)
+    except FileNotFoundError:
+        db = {}
+    db[key] = {"source_hash": roof["source_hash"], "hbm_bytes_per_launch": round(hbm),
+               "fetch_kib_per_launch": round(out["FETCH_SIZE"]["kib_per_launch"], 1),
+               "write_kib_per_launch": round(out["WRITE_SIZE"]["kib_per_launch"], 1),
+               "scale_fetch": round(out["FETCH_SIZE"]["scale"], 4), "scale_write": round(out["WRITE_SIZE"]["scale"], 4),
+               "calib_copy_mib": calib_mib, "launches": out["FETCH_SIZE"]["launches"],
+               "algorithmic_bytes_per_launch": roof.get("algorithmic_bytes")}
+    with open(path, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps({key: db[key]}))
+
+
 def main():
     a = parse()
+    if a.pmc_summarize:
+        pmc_summarize(*a.pmc_summarize, a.calib_copy_mib or sys.exit("--pmc-summarize needs --calib-copy-mib"))
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the multi-GPU design "
               "is described in the design notes but not built", file=sys.stderr)
@@ -285,11 +361,11 @@ def main():
     print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
     st = Step(w, dev)
     torch.cuda.synchronize()
-    if a.calib_copy_mib:
-        n = a.calib_copy_mib * (1 << 20) // 16
-        src_c = torch.ones(n, 4, dtype=torch.int32, device=dev)
+    if a.calib_copy_mib:  # one elementwise kernel reading and writing exactly this many bytes
+        n = a.calib_copy_mib * (1 << 20) // 4
+        src_c = torch.ones(n, dtype=torch.int32, device=dev)
         dst_c = torch.empty_like(src_c)
-        dst_c.copy_(src_c)
+        torch.bitwise_not(src_c, out=dst_c)
         torch.cuda.synchronize()
         del src_c, dst_c
     for _ in range(a.warmup):
@@ -359,7 +435,7 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBPS, 4)}
     src_hash = kernel_source_hash(src_files)
     roof.update({"traffic": load_traffic(f"{w.name}:{dom.split()[0]}", src_hash, dom_bytes), "kernel": dom,
-                 "source_hash": src_hash})
+                 "algorithmic_bytes": int(dom_bytes), "source_hash": src_hash})
     cpu = None
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
