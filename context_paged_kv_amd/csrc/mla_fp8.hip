@@ -156,6 +156,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(wave >= 0 && wave < kWaves);
   const int rq = wave % kPairStride, hh = wave / kPairStride;
   const int partner = wave ^ kPairStride;
   const int g = lane >> 4, c = lane & 15;
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   // the lane's query rows (one per column tile) and their queries over this half's dims
   // (B operand of S^T: dims 288 hh + 32 kk + 8 g + [0, 8)), as fp16 scaled by 2^qe
   int rowq[kNT];
-  int64_t lim[kNT];
+  int lim[kNT];  // last visible position of the row (positions are below T <= INT32_MAX)
   float amax[kNT];
   u32x4 qraw[kNT][kQSteps];
 #pragma unroll
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
     const bool ok = r < p.rows;
     rowq[nt] = ok ? r : -1;
     const int t = ok ? r / p.hq : 0, h = ok ? r % p.hq : 0;
-    lim[nt] = ok ? (int64_t)T - p.q_len + t : -1;
+    lim[nt] = ok ? T - p.q_len + t : -1;
     const uint16_t* qr =
         static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim + kHalfQk * hh;
     float mx = 0.f;
@@ -262,7 +263,8 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   // Block-table entries come in windows of 64 (one per lane, the next window loaded a whole
   // window ahead) and page scales one page ahead, so no dependent load sits between a barrier
   // and the next page's copies.  Entries outside [0, pages_per_layer) are skipped.
-  auto ok = [&](int32_t sl) { return sl >= 0 && (int64_t)sl < p.pages_per_layer; };
+  const uint32_t slots = (uint32_t)min<int64_t>(p.pages_per_layer, INT32_MAX);
+  auto ok = [&](int32_t sl) { return (uint32_t)sl < slots; };
   int wbase = j_begin;
   int32_t win0 = j_begin + lane < j_end ? bt[j_begin + lane] : -1;
   int32_t win1 = j_begin + 64 + lane < j_end ? bt[j_begin + 64 + lane] : -1;
@@ -316,10 +318,9 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
       for (int i = 0; i < kLoadIters; ++i) st(i);
     }
     if (ok(slot_cur)) {
-      const int64_t pos0 = ((int64_t)jj * p.n + d) * kMlaPage;
-      const int64_t rem = (int64_t)T - pos0;
-      const int valid = rem < kMlaPage ? (int)rem : kMlaPage;
-      const bool full = pos0 + kMlaPage - 1 <= (int64_t)T - p.q_len;  // no row masks a token of this page
+      const int pos0 = (jj * p.n + d) * kMlaPage;  // local page jj holds positions below T
+      const int valid = min(T - pos0, kMlaPage);
+      const bool full = pos0 <= T - p.q_len - (kMlaPage - 1);  // no row masks a token of this page
       const float ps = fmaxf(bf16_to_float(sc_cur), 1e-30f);
       uint8_t* cur = s_raw[buf];
       if (valid < kMlaPage) {  // tail of the last page: no code past T reaches a product
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
           for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              if (pos0 + mla_tok(tt, 4 * g + i) > lim[nt]) s[nt][tt][i] = kNegInf;
+              if (mla_tok(tt, 4 * g + i) > lim[nt] - pos0) s[nt][tt][i] = kNegInf;
         }
         float v_max = kNegInf;
 #pragma unroll
