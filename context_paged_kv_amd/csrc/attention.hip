@@ -187,8 +187,8 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) acc[k] = 0.f;
 
-    const int j_begin = chunk * p.chunk_pages;
-    const int j_end = min(pp.n_local, j_begin + p.chunk_pages);
+    int j_begin, j_end;
+    chunk_range(pp, chunk, j_begin, j_end);
     const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
     for (int jj = j_begin; jj < j_end; ++jj) {
       const int32_t slot = bt[jj];

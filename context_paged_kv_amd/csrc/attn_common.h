@@ -137,6 +137,16 @@ __device__ inline void wave_merge_row(int count, const float* __restrict__ lse, 
   }
 }
 
+// Local pages [begin, end) of chunk `chunk` of a pair: its k chunks split the
+// pair's pages evenly (sizes differ by at most one), so no work item is more
+// than one page longer than another of the same pair.
+__device__ __forceinline__ void chunk_range(const PairPlan& pp, int chunk, int& begin, int& end) {
+  const int k = pp.k > 0 ? pp.k : 1;
+  const int base = pp.n_local / k, extra = pp.n_local - base * k;
+  begin = chunk * base + min(chunk, extra);
+  end = begin + base + (chunk < extra ? 1 : 0);
+}
+
 // Decode item w into its pair, chunk and head block.
 __device__ __forceinline__ void decode_item(const AttnParams& p, int w, int& pair, int& chunk,
                                             int& hb) {

@@ -120,8 +120,8 @@ __global__ __launch_bounds__(256) void gqa_bf16_kernel(AttnParams p) {
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int j_begin = chunk * p.chunk_pages;
-  const int j_end = min(pp.n_local, j_begin + p.chunk_pages);
+  int j_begin, j_end;
+  chunk_range(pp, chunk, j_begin, j_end);
   const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
   const int64_t head_bytes = (int64_t)kGqaPage * kGqaRow;
   const uint8_t* pool = p.pools[d] + (int64_t)p.layer * p.pages_per_layer * p.page_bytes;

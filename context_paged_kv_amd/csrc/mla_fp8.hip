@@ -255,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int j_begin = chunk * p.chunk_pages;
-  const int j_end = min(pp.n_local, j_begin + p.chunk_pages);
+  int j_begin, j_end;
+  chunk_range(pp, chunk, j_begin, j_end);
   const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
   const uint8_t* pool = p.pools[d] + (int64_t)p.layer * p.pages_per_layer * p.page_bytes;
   const uint16_t* scl = p.scales[d] + (int64_t)p.layer * p.pages_per_layer;
