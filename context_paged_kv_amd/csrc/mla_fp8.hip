@@ -15,32 +15,37 @@
 // rows).  A workgroup owns one item.  Its wavefronts come in pairs (w and
 // w ^ kPairStride) that own kNT column tiles of 16 rows each; half
 // hh = w / kPairStride of the pair
-//   * computes the scores over dims [288 hh, 288 hh + 288) and swaps that
-//     partial S^T with its partner through LDS, so both hold the full scores
-//     (the same sum, bit for bit, hence the same softmax decisions);
+//   * computes the scores over latent dims [256 hh, 256 hh + 256) and rope
+//     dims [512 + 32 hh, 512 + 32 hh + 32), and swaps that partial S^T with
+//     its partner through LDS, so both hold the full scores (the same sum,
+//     bit for bit, hence the same softmax decisions);
 //   * accumulates O over the value dims [256 hh, 256 hh + 256).
-// With kNT = 1 a wavefront needs about 130 registers, so two run on each SIMD
-// and hide each other's latencies; with kNT = 2 every converted operand feeds
-// two MFMAs but only one wavefront fits per SIMD.  Per page:
+// With kNT = 2 every converted V operand feeds two MFMAs and one wavefront
+// runs per SIMD (128 accumulator registers plus the query operands); kNT = 1
+// runs two wavefronts per SIMD but converts twice as much and was slower.
+// Per page:
 //   * the 36 KB of fp8 codes are double buffered in LDS: the loads of page
 //     j+1 go out between the score MFMAs of page j and land in registers,
 //     and are written to the other buffer between its PV MFMAs (copies into
 //     LDS by DMA were slower to issue and held up the wave's LDS reads).
 //     LDS rows are 592 bytes (576 + 16 pad);
-//   * S^T = K Q^T on v_mfma_f32_16x16x32_f16: each lane reads 8 codes of one
-//     token (ds_read_b64) and converts them exactly to fp16 with
-//     v_cvt_scalef32_pk_f16_fp8.  Q is held in fp16, each row scaled by a
-//     power of two so its largest entry sits just below 2^15 (bf16 -> fp16
-//     exact), the factor folded into that row's score scale.  The token order
-//     of the A rows puts, after the MFMA, the eight scores a lane needs for
-//     its P^T operand in that lane;
+//   * latent scores on v_mfma_scale_f32_16x16x128_f8f6f4 straight from the
+//     fp8 codes (unit scales): each query row is held as two e4m3 terms,
+//     hi = e4m3(q) and lo = e4m3(q - hi), whose sum is the bf16 query
+//     exactly (8 significant bits = 4 + 4), so no K conversion is needed;
+//     the rope dims use v_mfma_f32_16x16x32_f16 with K converted by
+//     v_cvt_scalef32_pk_f16_fp8 (exact).  The query is scaled by 2^qe per row
+//     so its largest entry lies in [128, 256); the factor leaves with the
+//     softmax scale.  The token order of the A rows puts, after the MFMA, the
+//     eight scores a lane needs for its P^T operand in that lane;
 //   * online softmax in base 2 with a lazy reference: a row's exponent offset
 //     moves (and the accumulator is rescaled) only when the page maximum
 //     exceeds it by more than 2^8, or when the page scale leaves
 //     [1/4, 4] x the reference scale; in between P carries the page-scale
 //     ratio and the accumulator is touched by MFMAs only;
-//   * O^T += V^T P^T: ds_read_b64_tr_b8 hands each lane eight tokens of one
-//     latent dim straight from the row-major codes, converted as above.
+//   * O^T += V^T P^T on the f16 MFMA: ds_read_b64_tr_b8 hands each lane eight
+//     tokens of one latent dim straight from the row-major codes, converted
+//     to fp16 as above.
 
 #include <hip/hip_runtime.h>
 
@@ -58,6 +63,7 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kMlaPage = 64;
@@ -71,9 +77,11 @@ constexpr int kNT = MLA_NT;                          // 16-row column tiles per 
 constexpr int kWaves = 8 / kNT;                      // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kPairStride = kWaves / 2;              // partner of wave w is w ^ kPairStride
-constexpr int kHalfQk = kMlaDim / 2;                // 288 score dims per wavefront
+constexpr int kLatHalf = 256;                       // latent score dims per wavefront (fp8 MFMA)
+constexpr int kRopeHalf = 32;                       // rope score dims per wavefront (f16 MFMA)
+constexpr int kRope0 = kMlaDv;                      // first rope dim
 constexpr int kHalfV = kMlaDv / 2;                  // 256 value dims per wavefront
-constexpr int kQSteps = kHalfQk / 32;               // 9 k-steps of 32 dims
+constexpr int kLatSteps = kLatHalf / 128;           // 2 k-steps of 128 dims
 constexpr int kVTiles = kHalfV / 16;                // 16 M tiles of 16 dims
 constexpr int kRawStride = 592;                     // LDS bytes per token row of codes
 constexpr int kRawBuf = kMlaPage * kRawStride;      // 37888 bytes per page buffer
@@ -122,6 +130,24 @@ __device__ __forceinline__ f16x8 cvt8(u32x2 x) {
   const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x[1], 1.0f, true);
   return __builtin_shufflevector(__builtin_shufflevector(a, b, 0, 1, 2, 3), __builtin_shufflevector(c, d, 0, 1, 2, 3),
                                  0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Four values (already scaled so |v| < 256) as two e4m3fn words: hi = e4m3(v),
+// lo = e4m3(v - hi).  A bf16 value has 8 significant bits, each e4m3 term 4, so
+// hi + lo is v itself for every value whose terms stay in the normal e4m3
+// range (the rest lose less than 2^-9 of the row's largest entry).
+__device__ __forceinline__ void split_e4m3(const float v[4], uint32_t& hi, uint32_t& lo) {
+  int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  h = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], h, true);
+  float r[4];
+  r[0] = v[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0);
+  r[1] = v[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1);
+  r[2] = v[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2);
+  r[3] = v[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w, true);
+  hi = (uint32_t)h;
+  lo = (uint32_t)w;
 }
 
 // Token held by MFMA row m of S^T tile tt: tiles 2ks and 2ks+1 give the lane of
@@ -184,12 +210,15 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int T = p.seq_lens[b];
 
-  // the lane's query rows (one per column tile) and their queries over this half's dims
-  // (B operand of S^T: dims 288 hh + 32 kk + 8 g + [0, 8)), as fp16 scaled by 2^qe
+  // The lane's query rows (one per column tile) and their operands.  Latent dims
+  // 256 hh + 128 ks + 32 g + [0, 32) go to the fp8 MFMA as two exact e4m3 terms
+  // (hi, lo); rope dims 512 + 32 hh + 8 g + [0, 8) go to the f16 MFMA.  Both are
+  // scaled by 2^qe per row (largest |q| in [128, 256)); the factor is taken out
+  // of the scores with the softmax scale.
   int rowq[kNT];
   int lim[kNT];  // last visible position of the row (positions are below T <= INT32_MAX)
   float amax[kNT];
-  u32x4 qraw[kNT][kQSteps];
+  u32x4 qraw[kNT][kLatSteps * 4 + 1];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
     const int r = hb * kMlaRowsPerBlock + 16 * (kNT * rq + nt) + c;
@@ -197,13 +226,14 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
     rowq[nt] = ok ? r : -1;
     const int t = ok ? r / p.hq : 0, h = ok ? r % p.hq : 0;
     lim[nt] = ok ? T - p.q_len + t : -1;
-    const uint16_t* qr =
-        static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim + kHalfQk * hh;
+    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim;
     float mx = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < kQSteps; ++kk) {
-      const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(qr + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
-      qraw[nt][kk] = w;
+    for (int i = 0; i < kLatSteps * 4 + 1; ++i) {
+      const uint16_t* src = i < kLatSteps * 4 ? qr + kLatHalf * hh + 128 * (i >> 2) + 32 * g + 8 * (i & 3)
+                                              : qr + kRope0 + kRopeHalf * hh + 8 * g;
+      const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+      qraw[nt][i] = w;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2)
         mx = fmaxf(mx, fmaxf(fabsf(__builtin_bit_cast(float, w[e2] << 16)),
@@ -218,27 +248,46 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
     for (int nt = 0; nt < kNT; ++nt) xm[16 * nt + c] = amax[nt];
   }
   __syncthreads();
-  float qscale[kNT];  // 2^qe: the row's largest |q| lands in [2^14, 2^15)
-  f16x8 qb[kNT][kQSteps];
+  float qscale[kNT];
+  i32x8 qhi[kNT][kLatSteps], qlo[kNT][kLatSteps];
+  f16x8 qrope[kNT];
   {
     const float* xo = reinterpret_cast<const float*>(&s_x[partner][0][0]);
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt) {
       const float am = fmaxf(amax[nt], xo[16 * nt + c]);
-      const int qe = am > 0.f ? 14 - ilogbf(am) : 0;
+      const int qe = am > 0.f ? 7 - ilogbf(am) : 0;
       qscale[nt] = ldexpf(1.f, qe);
 #pragma unroll
-      for (int kk = 0; kk < kQSteps; ++kk) {
-        const u32x4 w = qraw[nt][kk];
-        f16x2 h2[4];
+      for (int ks = 0; ks < kLatSteps; ++ks) {
+        i32x8 hv, lv;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
-                         (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
-        qb[nt][kk] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
-                                             __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3,
-                                             4, 5, 6, 7);
+        for (int j = 0; j < 4; ++j) {  // 8 dims per u32x4 -> two words of four e4m3 codes
+          const u32x4 w = qraw[nt][4 * ks + j];
+#pragma unroll
+          for (int hw = 0; hw < 2; ++hw) {
+            const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), qe),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), qe),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), qe),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), qe)};
+            uint32_t hw32, lw32;
+            split_e4m3(v, hw32, lw32);
+            hv[2 * j + hw] = (int)hw32;
+            lv[2 * j + hw] = (int)lw32;
+          }
+        }
+        qhi[nt][ks] = hv;
+        qlo[nt][ks] = lv;
       }
+      const u32x4 w = qraw[nt][kLatSteps * 4];
+      f16x2 h2[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2)
+        h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
+                       (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
+      qrope[nt] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
+                                          __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
+                                          6, 7);
     }
   }
   float sl2[kNT], mref[kNT], l[kNT];  // l: this lane's share of the row's denominator
@@ -302,13 +351,15 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
     const uint8_t* npage = pool + (int64_t)(have_nxt ? slot_nxt : 0) * p.page_bytes;
     uint8_t* nbuf = s_raw[buf ^ 1];
     u32x4 stg[kLoadIters];  // page j + 1 on its way to the other buffer
+    // No test of have_nxt here: without a next page the loads read slot 0 (in bounds) and the
+    // writes land in the buffer nothing reads before it is filled again; branch-free this way.
     auto ld = [&](int i) {
-      if (have_nxt && kThreads * i + 64 * wave < kSlots)
+      if (kThreads * i + 64 * wave < kSlots)
         stg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(npage + cp.off[i]));
     };
     auto st = [&](int i) {
       const int base = kThreads * i + 64 * wave;
-      if (have_nxt && base < kSlots) *reinterpret_cast<u32x4*>(nbuf + 16 * (base + lane)) = stg[i];
+      if (base < kSlots) *reinterpret_cast<u32x4*>(nbuf + 16 * (base + lane)) = stg[i];
     };
     if (have_nxt) sc_nxt = scl[slot_nxt];
     if (!ok(slot_cur)) {
@@ -337,30 +388,42 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
       for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) s[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = cur + kHalfQk * hh + 8 * g;
-      u32x2 kx[2][4];  // codes of k-steps kk (in use) and kk + 1 (in flight)
+      // latent: A = 32 fp8 codes of token mla_tok(tt, c) (two 16-byte LDS reads), B = the
+      // row's hi and lo terms; rope: one f16 k-step as in the PV loop's operands
+      const uint8_t* klat = cur + kLatHalf * hh + 32 * g;
+      const uint8_t* krope = cur + kRope0 + kRopeHalf * hh + 8 * g;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) kx[0][tt] = *reinterpret_cast<const u32x2*>(krow + mla_tok(tt, c) * kRawStride);
-#pragma unroll
-      for (int kk = 0; kk < kQSteps; ++kk) {
-        ld(kk);
-        if (kk == kQSteps - 1) {
-#pragma unroll
-          for (int i = kQSteps; i < kLoadIters; ++i) ld(i);
-        }
-        if (kk + 1 < kQSteps) {
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
-            kx[(kk + 1) & 1][tt] =
-                *reinterpret_cast<const u32x2*>(krow + mla_tok(tt, c) * kRawStride + 32 * (kk + 1));
-        }
+      for (int ks = 0; ks < kLatSteps; ++ks) {
+        i32x8 a[4];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
-          const f16x8 a = cvt8(kx[kk & 1][tt]);
+          const uint8_t* kp = klat + mla_tok(tt, c) * kRawStride + 128 * ks;
+          const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
+          const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
+          a[tt] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+#pragma unroll
+        for (int i = 0; i < kLoadIters / kLatSteps; ++i) ld(ks * (kLoadIters / kLatSteps) + i);
+        // each accumulator is touched every 8th MFMA: hi terms of all tiles, then lo terms
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
           for (int nt = 0; nt < kNT; ++nt)
-            s[nt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qb[nt][kk], s[nt][tt], 0, 0, 0);
-        }
+            s[nt][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qhi[nt][ks], s[nt][tt], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+          for (int nt = 0; nt < kNT; ++nt)
+            s[nt][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qlo[nt][ks], s[nt][tt], 0, 0, 0, 127, 0, 127);
+      }
+#pragma unroll
+      for (int i = kLatSteps * (kLoadIters / kLatSteps); i < kLoadIters; ++i) ld(i);
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const f16x8 a = cvt8(*reinterpret_cast<const u32x2*>(krope + mla_tok(tt, c) * kRawStride));
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt)
+          s[nt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[nt], s[nt][tt], 0, 0, 0);
       }
       // ---- swap partials with the partner wavefront; both then hold the same full scores
 #pragma unroll
