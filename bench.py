@@ -272,6 +272,27 @@ def cpu_baseline(st, budget_s: float):
             "sample": "float64 numpy oracle, one thread: " + "; ".join(notes) + "; scaled linearly to the full step"}
 
 
+def plain_copy_gbps(torch, dev, nbytes: int, reps: int = 5) -> float:
+    """Read + write GB/s of one contiguous device-to-device copy of about `nbytes` (capped at 2 GiB),
+    timed with events: the practical copy ceiling of this GPU, next to which the reshard is read."""
+    n = max(1 << 20, min(int(nbytes), 2 << 30)) // 16 * 16
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    return 2 * n / float(np.median(ts)) / 1e9
+
+
 # kernels of each timed call, as rocprofv3 names them
 CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",),
                 "dcp_decode_partial": ("plan_kernel", "gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
@@ -403,8 +424,11 @@ def main():
              "bytes": {"reshard_rw": b_rs, "kv": b_kv, "attn_other": b_other}}
     if st.has_reshard:
         rs_gbps = b_rs / t_rs.mean() / 1e9
+        copy_gbps = plain_copy_gbps(torch, dev, b_rs // 2)
         parts.update({"reshard_GBps": round(rs_gbps, 1), "reshard_frac_hbm": round(rs_gbps / HBM_PEAK_GBPS, 4),
-                      "reshard_us": round(t_rs.mean() * 1e6, 2)})
+                      "reshard_us": round(t_rs.mean() * 1e6, 2),
+                      "plain_copy_GBps": round(copy_gbps, 1),
+                      "reshard_frac_of_plain_copy": round(rs_gbps / copy_gbps, 4)})
     if st.has_attention:
         t_attn = t_pa.mean() + t_mg.mean()
         kv_gbps = b_kv / t_attn / 1e9
