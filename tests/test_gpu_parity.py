@@ -85,6 +85,44 @@ def test_decode_mla_fp8_verify_small():
     H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
 
 
+def _rescale_pages(case, f_repr, f_value):
+    """Page (d, slot) of the attention layer: scale x 2^(f_repr + f_value), codes re-encoded as
+    value x 2^-f_repr (e4m3fn, rounded by torch).  f_repr changes only how the page is written,
+    f_value changes its values."""
+    for d, (pool, sc) in enumerate(zip(case.pools, case.scales)):
+        fr = torch.from_numpy(np.exp2(-f_repr[d]).astype(np.float32)).to(pool.device)
+        codes = pool[case.layer].view(torch.float8_e4m3fn).float() * fr[:, None]
+        pool[case.layer].copy_(codes.to(torch.float8_e4m3fn).view(torch.uint8))
+        bits = sc[case.layer].cpu().numpy().astype(np.uint16)
+        vals = (bits.astype(np.uint32) << 16).view(np.float32) * np.exp2(f_repr[d] + f_value[d]).astype(np.float32)
+        sc[case.layer].copy_(torch.from_numpy((vals.view(np.uint32) >> 16).astype(np.uint16).view(np.int16)).to(sc.device))
+
+
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_decode_mla_fp8_rescale_paths(q_len):
+    # Both rare paths of the fp8 MLA kernel's online softmax, against the oracle:
+    #  * every page is rewritten with scale x 2^f, f in {0..3}, and codes x 2^-f: the values (and
+    #    the scores) stay N(0,1)-like, but neighbouring page scales differ by up to 8x, so the
+    #    accumulator's reference scale has to move;
+    #  * one page in the middle of request 0 gets its values x 4: its scores jump past the running
+    #    row maximum by more than 2^8 in log2 units.
+    base = get_workload("mla_fp8_longmix_verify" if q_len == 4 else "mla_fp8_48x100k")
+    w = scaled(base, seed=base.seed + 400 + q_len, seq_segments=((2, 3000, 6000),), pool_pages=512,
+               num_layers=1, attn_layer=0, q_len=q_len)
+    case = H.make_decode_case(w, DEV)
+    rng = np.random.default_rng(11 + q_len)
+    f_repr = [rng.integers(0, 4, size=w.pool_pages).astype(np.float64) for _ in range(w.dcp_size)]
+    f_value = [np.zeros(w.pool_pages) for _ in range(w.dcp_size)]
+    mid = case.pages[0][len(case.pages[0]) // 2]
+    f_value[mid % w.dcp_size][mid // w.dcp_size] = 2.0
+    _rescale_pages(case, f_repr, f_value)
+    H.log(f"decode mla fp8 q_len {q_len}: page scales x 2^U[0, 3] (codes / same), page {mid} values x 4")
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs)
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "gqa_bf16_16x4k-32k", "mla_fp8_longmix_verify"])
 def test_decode_edge_lengths(name):
     # T = q_len (only the drafts), T = 1 page + 1 token, lengths below N pages (empty shards)
