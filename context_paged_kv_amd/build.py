@@ -31,6 +31,10 @@ HIP_FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-result", "-fvisibility=hidden",
 ]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", "-fvisibility=hidden"]
+# Per-source additions.  The MLA kernel runs two wavefronts per SIMD (256 registers
+# each); with accumulators in VGPRs the whole budget is one class, where the default
+# would split it evenly between VGPRs and AGPRs and spill.
+EXTRA_FLAGS = {"mla_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -51,7 +55,8 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     if src.endswith(".hip"):
-        cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+        cmd = [hipcc(), "-x", "hip", *HIP_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-I", INCLUDE,
+               "-I", CSRC, "-c", src, "-o", obj]
     else:
         cmd = [hipcc(), *HOST_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -24,7 +24,7 @@ int kernel_rows_per_block(int kind, const dcp_attn_desc& D) {
     case KK_GQA_BF16:
       return (D.num_q_heads / D.num_kv_heads) * D.q_len;  // the whole group in one MFMA row block
     case KK_MLA_FP8:
-      return mla_fp8_rows_per_block();  // four wavefronts x 32 query rows
+      return mla_fp8_rows_per_block();  // 64 query rows: four 16-row tiles
     default:
       return D.kv_layout == DCPKV_LAYOUT_MLA ? 8 : 16;
   }

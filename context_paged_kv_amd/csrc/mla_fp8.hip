@@ -12,23 +12,21 @@
 // about 480 flop per KV byte, so the matrix cores bind, not HBM.
 //
 // Work item: (shard d, request b, chunk of local pages, block of 64 query
-// rows).  A workgroup owns one item.  Its wavefronts come in pairs (w and
-// w ^ kPairStride) that own kNT column tiles of 16 rows each; half
-// hh = w / kPairStride of the pair
-//   * computes the scores over latent dims [256 hh, 256 hh + 256) and rope
-//     dims [512 + 32 hh, 512 + 32 hh + 32), and swaps that partial S^T with
-//     its partner through LDS, so both hold the full scores (the same sum,
-//     bit for bit, hence the same softmax decisions);
-//   * accumulates O over the value dims [256 hh, 256 hh + 256).
-// With kNT = 2 every converted V operand feeds two MFMAs and one wavefront
-// runs per SIMD (128 accumulator registers plus the query operands); kNT = 1
-// runs two wavefronts per SIMD but converts twice as much and was slower.
+// rows).  A workgroup of eight wavefronts owns one item, two wavefronts per
+// SIMD, so one wavefront's vector work runs under the other's MFMAs.  Every
+// wavefront has two roles per page:
+//   * scores: wave w computes S^T for row tile rt = w % 4 (16 rows) and token
+//     half th = w / 4 (32 tokens) over all 576 dims, the softmax numerators P
+//     of those 16 x 32 scores, and hands them (fp16, already in the P^T
+//     operand layout) to the others through LDS;
+//   * values: wave w accumulates O^T for value dims [64 w, 64 w + 64) of all
+//     64 rows from every wave's P, so each converted V operand feeds four
+//     MFMAs (one per row tile).
 // Per page:
 //   * the 36 KB of fp8 codes are double buffered in LDS: the loads of page
 //     j+1 go out between the score MFMAs of page j and land in registers,
-//     and are written to the other buffer between its PV MFMAs (copies into
-//     LDS by DMA were slower to issue and held up the wave's LDS reads).
-//     LDS rows are 592 bytes (576 + 16 pad);
+//     and are written to the other buffer between its PV MFMAs.  LDS rows
+//     are 592 bytes (576 + 16 pad);
 //   * latent scores on v_mfma_scale_f32_16x16x128_f8f6f4 straight from the
 //     fp8 codes (unit scales): each query row is held as two e4m3 terms,
 //     hi = e4m3(q) and lo = e4m3(q - hi), whose sum is the bf16 query
@@ -36,13 +34,14 @@
 //     the rope dims use v_mfma_f32_16x16x32_f16 with K converted by
 //     v_cvt_scalef32_pk_f16_fp8 (exact).  The query is scaled by 2^qe per row
 //     so its largest entry lies in [128, 256); the factor leaves with the
-//     softmax scale.  The token order of the A rows puts, after the MFMA, the
-//     eight scores a lane needs for its P^T operand in that lane;
-//   * online softmax in base 2 with a lazy reference: a row's exponent offset
-//     moves (and the accumulator is rescaled) only when the page maximum
-//     exceeds it by more than 2^8, or when the page scale leaves
-//     [1/4, 4] x the reference scale; in between P carries the page-scale
-//     ratio and the accumulator is touched by MFMAs only;
+//     softmax scale;
+//   * online softmax in base 2 with a lazy reference per row: a token half
+//     raises its row's exponent offset only when its maximum exceeds the
+//     offset by more than 2^8; after the exchange every wave takes the larger
+//     of the two halves' offsets (the same values in every wave, so the same
+//     decision) and rescales accumulator rows and P operands only then.  The
+//     page scale rides in P as the ratio to a reference scale that moves
+//     (with a rescale) only when the ratio leaves [1/4, 4];
 //   * O^T += V^T P^T on the f16 MFMA: ds_read_b64_tr_b8 hands each lane eight
 //     tokens of one latent dim straight from the row-major codes, converted
 //     to fp16 as above.
@@ -70,26 +69,23 @@ constexpr int kMlaPage = 64;
 constexpr int kMlaDim = 576;
 constexpr int kMlaDv = 512;
 constexpr int kMlaRowsPerBlock = 64;
-#ifndef MLA_NT
-#define MLA_NT 2
-#endif
-constexpr int kNT = MLA_NT;                          // 16-row column tiles per wavefront
-constexpr int kWaves = 8 / kNT;                      // wavefronts per workgroup
+constexpr int kWaves = 8;                              // two per SIMD
 constexpr int kThreads = 64 * kWaves;
-constexpr int kPairStride = kWaves / 2;              // partner of wave w is w ^ kPairStride
-constexpr int kLatHalf = 256;                       // latent score dims per wavefront (fp8 MFMA)
-constexpr int kRopeHalf = 32;                       // rope score dims per wavefront (f16 MFMA)
-constexpr int kRope0 = kMlaDv;                      // first rope dim
-constexpr int kHalfV = kMlaDv / 2;                  // 256 value dims per wavefront
-constexpr int kLatSteps = kLatHalf / 128;           // 2 k-steps of 128 dims
-constexpr int kVTiles = kHalfV / 16;                // 16 M tiles of 16 dims
-constexpr int kRawStride = 592;                     // LDS bytes per token row of codes
-constexpr int kRawBuf = kMlaPage * kRawStride;      // 37888 bytes per page buffer
-constexpr int kSlotsPerRow = kRawStride / 16;       // 37 16-byte slots (36 data + 1 pad)
-constexpr int kSlots = kMlaPage * kSlotsPerRow;     // 2368
+constexpr int kRowTiles = kMlaRowsPerBlock / 16;       // 4 column tiles of 16 query rows
+constexpr int kLatSteps = kMlaDv / 128;                // 4 fp8 k-steps of 128 latent dims
+constexpr int kRope0 = kMlaDv;                         // first rope dim
+constexpr int kRopeSteps = (kMlaDim - kMlaDv) / 32;    // 2 f16 k-steps of 32 rope dims
+constexpr int kQWords = kLatSteps * 4 + kRopeSteps;    // 16-byte query loads per lane
+constexpr int kWaveDv = kMlaDv / kWaves;               // 64 value dims per wavefront
+constexpr int kVTiles = kWaveDv / 16;                  // 4 M tiles of 16 dims
+constexpr int kRawStride = 592;                        // LDS bytes per token row of codes
+constexpr int kRawBuf = kMlaPage * kRawStride;         // 37888 bytes per page buffer
+constexpr int kSlotsPerRow = kRawStride / 16;          // 37 16-byte slots (36 data + 1 pad)
+constexpr int kSlots = kMlaPage * kSlotsPerRow;        // 2368
 constexpr int kLoadIters = (kSlots + kThreads - 1) / kThreads;  // copy instructions per wave and page
-constexpr int kWaitLgkm0 = 0xC07F;                 // s_waitcnt lgkmcnt(0), other counters untouched
-constexpr float kTau = 8.f;                         // lazy-rescale threshold (log2 units)
+constexpr int kEarlyLoads = 3;                         // of them issued between the latent score MFMAs
+constexpr int kWaitLgkm0 = 0xC07F;                     // s_waitcnt lgkmcnt(0), other counters untouched
+constexpr float kTau = 8.f;                            // lazy-rescale threshold (log2 units)
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;
 
@@ -150,16 +146,15 @@ __device__ __forceinline__ void split_e4m3(const float v[4], uint32_t& hi, uint3
   lo = (uint32_t)w;
 }
 
-// Token held by MFMA row m of S^T tile tt: tiles 2ks and 2ks+1 give the lane of
-// group g the tokens 32ks + 8g + [0, 8), the k slots of its P^T operand.
+// Token (within a 32-token half page) held by MFMA row m of S^T tile tt (0 or
+// 1): the two tiles give the lane of group g the tokens 8g + [0, 8) of the
+// half, the k slots of its P^T operand.
 __device__ __forceinline__ int mla_tok(int tt, int m) {
-  return 32 * (tt >> 1) + 8 * (m >> 2) + 4 * (tt & 1) + (m & 3);
+  return 8 * (m >> 2) + 4 * tt + (m & 3);
 }
 
-// Start the global -> LDS copy of one page of codes into a 592-byte-row buffer.
-// LDS slot q (16 bytes) of row q / 37, column q % 37 holds page bytes
-// 16 * (q - q / 37) onwards; the pad column refetches a valid chunk.
-// Per-lane source offsets of the page copy: load i of wave w moves the 64
+// LDS slot q (16 bytes) of a page buffer, row q / 37 and column q % 37, holds
+// page bytes 16 * (q - q / 37) onwards.  Per-lane source offsets of the page copy: load i of wave w moves the 64
 // consecutive 16-byte LDS slots from kThreads * i + 64 * w (none past the page;
 // the pad column of a row refetches a valid chunk).
 struct CopyPlan {
@@ -176,15 +171,26 @@ __device__ __forceinline__ CopyPlan copy_plan(int wave, int lane) {
   return cp;
 }
 
+// Scale the accumulator tile by f.  The product goes back through an MFMA
+// (adding 0 x 0) so the accumulator keeps one register class across the loop
+// and the common path carries no copies; the empty asm makes the read happen
+// here, not ahead of the (rare) branch that calls this.
+__device__ __forceinline__ void scale_acc(f32x4& o, float f) {
+  const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+  asm volatile("" : "+v"(o));
+  o = __builtin_amdgcn_mfma_f32_16x16x32_f16(z, z, o * f, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBuf];  // 75776 B
-  __shared__ u32x4 s_x[kWaves][4 * kNT][64];                          // score-partial swap, 32768 B
+  __shared__ f16x8 s_p[kRowTiles][2][64];          // P^T operands by (row tile, token half, lane), 8 KB
+  __shared__ float s_lr[2][kMlaRowsPerBlock];      // the page's exponent offset of each token half
+  __shared__ float s_l[2][kMlaRowsPerBlock];       // denominators of the two token halves
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < kWaves);
-  const int rq = wave % kPairStride, hh = wave / kPairStride;
-  const int partner = wave ^ kPairStride;
+  const int rt = wave & (kRowTiles - 1), th = wave / kRowTiles;  // score role
   const int g = lane >> 4, c = lane & 15;
 
   // items sharing a chunk run on the same XCD (dispatch is round robin over 8)
@@ -210,97 +216,82 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int T = p.seq_lens[b];
 
-  // The lane's query rows (one per column tile) and their operands.  Latent dims
-  // 256 hh + 128 ks + 32 g + [0, 32) go to the fp8 MFMA as two exact e4m3 terms
-  // (hi, lo); rope dims 512 + 32 hh + 8 g + [0, 8) go to the f16 MFMA.  Both are
-  // scaled by 2^qe per row (largest |q| in [128, 256)); the factor is taken out
-  // of the scores with the softmax scale.
-  int rowq[kNT];
-  int lim[kNT];  // last visible position of the row (positions are below T <= INT32_MAX)
-  float amax[kNT];
-  u32x4 qraw[kNT][kLatSteps * 4 + 1];
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    const int r = hb * kMlaRowsPerBlock + 16 * (kNT * rq + nt) + c;
-    const bool ok = r < p.rows;
-    rowq[nt] = ok ? r : -1;
-    const int t = ok ? r / p.hq : 0, h = ok ? r % p.hq : 0;
-    lim[nt] = ok ? T - p.q_len + t : -1;
+  // Score role: the lane's query row 16 rt + c of the block.  Latent dims
+  // 128 ks + 32 g + [0, 32) go to the fp8 MFMA as two exact e4m3 terms (hi, lo);
+  // rope dims 512 + 32 ks + 8 g + [0, 8) go to the f16 MFMA.  Both are scaled by
+  // 2^qe (largest |q| of the row in [128, 256)); the factor is taken out of the
+  // scores with the softmax scale.
+  const int r_s = hb * kMlaRowsPerBlock + 16 * rt + c;
+  const bool row_ok = r_s < p.rows;
+  const int lim = row_ok ? T - p.q_len + r_s / p.hq : -1;  // last visible position (below T <= INT32_MAX)
+  i32x8 qhi[kLatSteps], qlo[kLatSteps];
+  f16x8 qrope[kRopeSteps];
+  float sl2;
+  {
+    const int t = row_ok ? r_s / p.hq : 0, h = row_ok ? r_s % p.hq : 0;
     const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim;
+    u32x4 qraw[kQWords];
     float mx = 0.f;
 #pragma unroll
-    for (int i = 0; i < kLatSteps * 4 + 1; ++i) {
-      const uint16_t* src = i < kLatSteps * 4 ? qr + kLatHalf * hh + 128 * (i >> 2) + 32 * g + 8 * (i & 3)
-                                              : qr + kRope0 + kRopeHalf * hh + 8 * g;
-      const u32x4 w = ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-      qraw[nt][i] = w;
+    for (int i = 0; i < kQWords; ++i) {
+      const uint16_t* src = i < kLatSteps * 4 ? qr + 128 * (i >> 2) + 32 * g + 8 * (i & 3)
+                                              : qr + kRope0 + 32 * (i - kLatSteps * 4) + 8 * g;
+      const u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+      qraw[i] = w;
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2)
         mx = fmaxf(mx, fmaxf(fabsf(__builtin_bit_cast(float, w[e2] << 16)),
                              fabsf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u))));
     }
-    amax[nt] = mgrp4_max(mx);
-  }
-  // both halves of a row use one scale: swap the half maxima once
-  if (g == 0) {
-    float* xm = reinterpret_cast<float*>(&s_x[wave][0][0]);
+    const float am = mgrp4_max(mx);
+    const int qe = am > 0.f ? 7 - ilogbf(am) : 0;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) xm[16 * nt + c] = amax[nt];
-  }
-  __syncthreads();
-  float qscale[kNT];
-  i32x8 qhi[kNT][kLatSteps], qlo[kNT][kLatSteps];
-  f16x8 qrope[kNT];
-  {
-    const float* xo = reinterpret_cast<const float*>(&s_x[partner][0][0]);
+    for (int ks = 0; ks < kLatSteps; ++ks) {
+      i32x8 hv, lv;
 #pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) {
-      const float am = fmaxf(amax[nt], xo[16 * nt + c]);
-      const int qe = am > 0.f ? 7 - ilogbf(am) : 0;
-      qscale[nt] = ldexpf(1.f, qe);
+      for (int j = 0; j < 4; ++j) {  // 8 dims per u32x4 -> two words of four e4m3 codes
+        const u32x4 w = qraw[4 * ks + j];
 #pragma unroll
-      for (int ks = 0; ks < kLatSteps; ++ks) {
-        i32x8 hv, lv;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {  // 8 dims per u32x4 -> two words of four e4m3 codes
-          const u32x4 w = qraw[nt][4 * ks + j];
-#pragma unroll
-          for (int hw = 0; hw < 2; ++hw) {
-            const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), qe),
-                                ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), qe),
-                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), qe),
-                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), qe)};
-            uint32_t hw32, lw32;
-            split_e4m3(v, hw32, lw32);
-            hv[2 * j + hw] = (int)hw32;
-            lv[2 * j + hw] = (int)lw32;
-          }
+        for (int hw = 0; hw < 2; ++hw) {
+          const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), qe),
+                              ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), qe),
+                              ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), qe),
+                              ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), qe)};
+          uint32_t hw32, lw32;
+          split_e4m3(v, hw32, lw32);
+          hv[2 * j + hw] = (int)hw32;
+          lv[2 * j + hw] = (int)lw32;
         }
-        qhi[nt][ks] = hv;
-        qlo[nt][ks] = lv;
       }
-      const u32x4 w = qraw[nt][kLatSteps * 4];
+      qhi[ks] = hv;
+      qlo[ks] = lv;
+    }
+#pragma unroll
+    for (int ks = 0; ks < kRopeSteps; ++ks) {
+      const u32x4 w = qraw[kLatSteps * 4 + ks];
       f16x2 h2[4];
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2)
         h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
                        (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
-      qrope[nt] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
+      qrope[ks] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
                                           __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
                                           6, 7);
     }
+    sl2 = p.scale * kLog2eM / ldexpf(1.f, qe);
   }
-  float sl2[kNT], mref[kNT], l[kNT];  // l: this lane's share of the row's denominator
+
+  // Exponent offsets (log2 units) of rows 16 nt + c: every wave holds the same
+  // values, updated from the same LDS words.  ref_s is the score row's (= ref[rt]).
+  float ref[kRowTiles];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    sl2[nt] = p.scale * kLog2eM / qscale[nt];
-    mref[nt] = kNegInf;
-    l[nt] = 0.f;
-  }
+  for (int nt = 0; nt < kRowTiles; ++nt) ref[nt] = kNegInf;
+  float ref_s = kNegInf;
+  float l_s = 0.f;     // this lane's share of the score row's denominator over this token half
   float ps_ref = 1.f;  // the accumulator is in units of ps_ref
-  f32x4 o[kNT][kVTiles];  // O^T tiles: dims 256 hh + 16 mt + 4 g + i of row (nt, c)
+  f32x4 o[kRowTiles][kVTiles];  // O^T tiles: dims 64 w + 16 mt + 4 g + i of row 16 nt + c
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
+  for (int nt = 0; nt < kRowTiles; ++nt)
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -319,9 +310,8 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   int32_t win1 = j_begin + 64 + lane < j_end ? bt[j_begin + 64 + lane] : -1;
   int32_t slot_cur = __builtin_amdgcn_readlane(win0, 0);
   uint16_t sc_cur = 0, sc_nxt = 0;
-  // The page copy goes through registers: load i of page j + 1 is issued next to k-step i of
-  // page j's scores and written to the other LDS buffer next to the last M tiles of page j's
-  // PV, so both hide behind MFMAs.
+  // The page copy goes through registers: the loads of page j + 1 are issued between the
+  // score MFMAs of page j and written to the other LDS buffer between its PV MFMAs.
   const CopyPlan cp = copy_plan(wave, lane);
   if (j_begin < j_end && ok(slot_cur)) {
     const uint8_t* page = pool + (int64_t)slot_cur * p.page_bytes;
@@ -340,7 +330,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   int buf = 0;
   for (int jj = j_begin; jj < j_end; ++jj) {
     __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of page jj (and the prefetched words) have landed
-    __syncthreads();                // ... and everyone's; the other buffer and the swap area are free
+    __syncthreads();                // ... and everyone's; the other buffer and the exchange area are free
     if (jj + 1 - wbase == 64) {
       wbase += 64;
       win0 = win1;
@@ -381,154 +371,146 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
         }
         __syncthreads();
       }
+      // ---- the reference page scale moves (with a rescale) when the ratio leaves [1/4, 4]
+      if (ps * __builtin_amdgcn_rcpf(ps_ref) > 4.f || ps * __builtin_amdgcn_rcpf(ps_ref) < 0.25f) {
+        const float fo = ps_ref * __builtin_amdgcn_rcpf(ps);
+#pragma unroll
+        for (int nt = 0; nt < kRowTiles; ++nt)
+#pragma unroll
+          for (int mt = 0; mt < kVTiles; ++mt) scale_acc(o[nt][mt], fo);
+        ps_ref = ps;
+      }
+      const float lrat = __builtin_amdgcn_logf(ps * __builtin_amdgcn_rcpf(ps_ref));  // log2 of the ratio
+      const float inv_ratio = ps_ref * __builtin_amdgcn_rcpf(ps);
 
-      // ---- partial S^T = K Q^T over this half's dims
-      f32x4 s[kNT][4];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) s[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // ---- S^T = K Q^T for row tile rt, tokens 32 th + [0, 32)
+      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       // latent: A = 32 fp8 codes of token mla_tok(tt, c) (two 16-byte LDS reads), B = the
-      // row's hi and lo terms; rope: one f16 k-step as in the PV loop's operands
-      const uint8_t* klat = cur + kLatHalf * hh + 32 * g;
-      const uint8_t* krope = cur + kRope0 + kRopeHalf * hh + 8 * g;
+      // row's hi and lo terms; rope: A = 8 codes converted to fp16
+      const uint8_t* khalf = cur + 32 * th * kRawStride;
 #pragma unroll
       for (int ks = 0; ks < kLatSteps; ++ks) {
-        i32x8 a[4];
+        i32x8 a[2];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          const uint8_t* kp = klat + mla_tok(tt, c) * kRawStride + 128 * ks;
+        for (int tt = 0; tt < 2; ++tt) {
+          const uint8_t* kp = khalf + mla_tok(tt, c) * kRawStride + 128 * ks + 32 * g;
           const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
           const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
           a[tt] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+        if (ks < kEarlyLoads) ld(ks);
 #pragma unroll
-        for (int i = 0; i < kLoadIters / kLatSteps; ++i) ld(ks * (kLoadIters / kLatSteps) + i);
-        // each accumulator is touched every 8th MFMA: hi terms of all tiles, then lo terms
+        for (int tt = 0; tt < 2; ++tt)
+          s[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qhi[ks], s[tt], 0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            s[nt][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qhi[nt][ks], s[nt][tt], 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            s[nt][tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qlo[nt][ks], s[nt][tt], 0, 0, 0, 127, 0, 127);
+        for (int tt = 0; tt < 2; ++tt)
+          s[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qlo[ks], s[tt], 0, 0, 0, 127, 0, 127);
       }
 #pragma unroll
-      for (int i = kLatSteps * (kLoadIters / kLatSteps); i < kLoadIters; ++i) ld(i);
+      for (int ks = 0; ks < kRopeSteps; ++ks)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const f16x8 a = cvt8(*reinterpret_cast<const u32x2*>(krope + mla_tok(tt, c) * kRawStride));
+        for (int tt = 0; tt < 2; ++tt) {
+          const f16x8 a =
+              cvt8(*reinterpret_cast<const u32x2*>(khalf + mla_tok(tt, c) * kRawStride + kRope0 + 32 * ks + 8 * g));
+          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[ks], s[tt], 0, 0, 0);
+        }
+
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt)
-          s[nt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[nt], s[nt][tt], 0, 0, 0);
+      for (int i = kEarlyLoads; i < kLoadIters; ++i) ld(i);  // the rest, once the K operands are dead
+
+      // ---- this half's numerators (lane: row 16 rt + c, tokens 32 th + 8 g + [0, 8))
+      const float f = sl2 * ps;
+      if (!full) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (32 * th + mla_tok(tt, 4 * g + i) > lim - pos0) s[tt][i] = kNegInf;
       }
-      // ---- swap partials with the partner wavefront; both then hold the same full scores
+      float v_max = kNegInf;
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) s_x[wave][4 * nt + tt][lane] = __builtin_bit_cast(u32x4, s[nt][tt]);
+        for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, s[tt][i]);
+      const float lane_max = v_max * f;
+      float lr = ref_s;  // this half's offset for the page: raised only past the threshold
+      if (__any(lane_max > ref_s + kTau)) {
+        const float m_row = mgrp4_max(lane_max);
+        lr = m_row > ref_s + kTau ? m_row : ref_s;
+      }
+      const float off = lr == kNegInf ? 0.f : lr - lrat;  // -inf only while every score is masked
+      float psum = 0.f;
+      float x[8];
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[4 * tt + i] = __builtin_amdgcn_exp2f(fmaf(s[tt][i], f, -off));
+          psum += x[4 * tt + i];
+        }
+      s_p[rt][th][lane] = f16x8{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                                (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
+      if (g == 0) s_lr[th][16 * rt + c] = lr;
       // LDS writes done, then a bare barrier: a full __syncthreads would also wait for the
       // next page's copy, which is still in flight
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) s[nt][tt] += __builtin_bit_cast(f32x4, s_x[partner][4 * nt + tt][lane]);
 
-      // ---- row maxima in log2 units (lane: row (nt, c), tokens mla_tok(tt, 4g + i))
-      float f[kNT], mx[kNT];
-      bool move = false;
+      // ---- each row's offset for the page: the larger of its two halves'
+      float nref[kRowTiles];
+      bool mv = false;
 #pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        f[nt] = sl2[nt] * ps;
-        if (!full) {
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (mla_tok(tt, 4 * g + i) > lim[nt] - pos0) s[nt][tt][i] = kNegInf;
-        }
-        float v_max = kNegInf;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, s[nt][tt][i]);
-        mx[nt] = v_max * f[nt];  // this lane's 16 scores; the row maximum is formed only on a move
-        move = move || mx[nt] > mref[nt] + kTau;
+      for (int nt = 0; nt < kRowTiles; ++nt) {
+        nref[nt] = fmaxf(s_lr[0][16 * nt + c], s_lr[1][16 * nt + c]);
+        mv = mv || nref[nt] != ref[nt];
       }
-      // ---- move the references when a row's maximum outgrows its offset or the scale drifts
-      const float ratio = ps * __builtin_amdgcn_rcpf(ps_ref);  // page scales are normal bf16 values
-      if (__any(move) || ratio > 4.f || ratio < 0.25f) {
+      const bool move = __any(mv);  // the same in every wave of the workgroup
+      float own = 1.f;              // factor of this lane's numerators
+      if (move) {
 #pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          const float mn = fmaxf(mref[nt], mgrp4_max(mx[nt]));
-          const float a = mref[nt] == kNegInf ? 0.f : exp2f(mref[nt] - mn);
-          mref[nt] = mn;
-          l[nt] *= a;
-          const float fo = a * ps_ref * __builtin_amdgcn_rcpf(ps);
-          // the product goes back through an MFMA (adding 0 x 0) so the accumulator keeps one
-          // register class across the loop and the common path carries no copies
-          const f16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int nt = 0; nt < kRowTiles; ++nt) {
+          const float a = ref[nt] == kNegInf ? 0.f : exp2f(ref[nt] - nref[nt]);
 #pragma unroll
-          for (int mt = 0; mt < kVTiles; ++mt) {
-            asm volatile("" : "+a"(o[nt][mt]));  // read the accumulator here, not ahead of the branch
-            o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z, z, o[nt][mt] * fo, 0, 0, 0);
+          for (int mt = 0; mt < kVTiles; ++mt) scale_acc(o[nt][mt], a);
+          if (nt == rt) {
+            l_s *= a;
+            own = lr == nref[nt] ? 1.f : exp2f(lr - nref[nt]);
+            ref_s = nref[nt];
           }
+          ref[nt] = nref[nt];
         }
-        ps_ref = ps;
       }
-      // ---- P' = 2^(x - mref) * ps / ps_ref (fp16), l += sum 2^(x - mref)
-      const float lr = __builtin_amdgcn_logf(ps * __builtin_amdgcn_rcpf(ps_ref));
-      const float inv_ratio = ps_ref * __builtin_amdgcn_rcpf(ps);
-      f16x8 pb[kNT][2];
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        const float off = mref[nt] == kNegInf ? 0.f : mref[nt] - lr;  // -inf only if every score so far is masked
-        float psum = 0.f;
-        f16x4 ph[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          float x4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = __builtin_amdgcn_exp2f(fmaf(s[nt][tt][i], f[nt], -off));
-            psum += x;
-            x4[i] = x;
-          }
-          ph[tt] = f16x4{(_Float16)x4[0], (_Float16)x4[1], (_Float16)x4[2], (_Float16)x4[3]};
-        }
-        // k step ks: tokens 32ks + 8g + [0, 4) from tile 2ks, + [4, 8) from tile 2ks + 1
-        pb[nt][0] = __builtin_shufflevector(ph[0], ph[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        pb[nt][1] = __builtin_shufflevector(ph[2], ph[3], 0, 1, 2, 3, 4, 5, 6, 7);
-        l[nt] += psum * inv_ratio;  // this lane's part of the row's denominator
-      }
-      // ---- O^T += V^T P^T over this half's value dims
+      l_s += psum * own * inv_ratio;
+
+      // ---- O^T += V^T P^T over this wave's value dims
       // source lane (g, c) of the transposing read points at token 32ks + 8g + (c >> 1),
       // dims 16*mt + 8*(c & 1) .. +7; lane (g, j) then holds dim 16*mt + j of those 8 tokens
-      const uint8_t* vrow = cur + (8 * g + (c >> 1)) * kRawStride + 8 * (c & 1) + kHalfV * hh;
-      i32x2 vx[2][2];  // codes of M tiles mt (in use) and mt + 1 (in flight)
+      const uint8_t* vrow = cur + (8 * g + (c >> 1)) * kRawStride + 8 * (c & 1) + kWaveDv * wave;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        vx[0][ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 32 * ks * kRawStride));
+      for (int ks = 0; ks < 2; ++ks) {
+        f16x8 pk[kRowTiles];
 #pragma unroll
-      for (int mt = 0; mt < kVTiles; ++mt) {
-        if (mt >= kVTiles - kLoadIters) st(mt - (kVTiles - kLoadIters));
-        if (mt + 1 < kVTiles) {
+        for (int nt = 0; nt < kRowTiles; ++nt) pk[nt] = s_p[nt][ks][lane];
+        if (move) {  // operands of a half whose offset is below the row's
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            vx[(mt + 1) & 1][ks] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * (mt + 1)));
+          for (int nt = 0; nt < kRowTiles; ++nt) {
+            const float lt = s_lr[ks][16 * nt + c];
+            const float fct = lt == ref[nt] ? 1.f : exp2f(lt - ref[nt]);
+            pk[nt] = pk[nt] * (_Float16)fct;
+          }
         }
+        i32x2 vx[kVTiles];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 a = cvt8(__builtin_bit_cast(u32x2, vx[mt & 1][ks]));
+        for (int mt = 0; mt < kVTiles; ++mt)
+          vx[mt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * mt));
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt)
-            o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[nt][ks], o[nt][mt], 0, 0, 0);
+        for (int mt = 0; mt < kVTiles; ++mt) {
+          const int it = kVTiles * ks + mt;
+          if (it >= 2 * kVTiles - kLoadIters) st(it - (2 * kVTiles - kLoadIters));
+          const f16x8 a = cvt8(__builtin_bit_cast(u32x2, vx[mt]));
+#pragma unroll
+          for (int nt = 0; nt < kRowTiles; ++nt)
+            o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pk[nt], o[nt][mt], 0, 0, 0);
         }
       }
     }
@@ -537,27 +519,28 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
     buf ^= 1;
   }
 
-  // ---- write the (chunk) partial of the lane's two rows, this half's dims: O = ps_ref * O^T / l
+  // ---- write the (chunk) partial of rows 16 nt + c, this wave's dims: O = ps_ref * O^T / l
+  const float lh = mgrp4_sum(l_s);
+  if (g == 0) s_l[th][16 * rt + c] = lh;
+  __syncthreads();
   const bool direct = pp.k == 1;
   const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
   const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
-  float lrow[kNT];
 #pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) lrow[nt] = mgrp4_sum(l[nt]);
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt) {
-    if (rowq[nt] < 0) continue;
-    const int r = rowq[nt];
+  for (int nt = 0; nt < kRowTiles; ++nt) {
+    const int r = hb * kMlaRowsPerBlock + 16 * nt + c;
+    if (r >= p.rows) continue;
+    const float lrow = s_l[0][16 * nt + c] + s_l[1][16 * nt + c];
     float* dst = (direct ? p.partial_out + (pair_row0 + r) * kMlaDv : p.ws_o + (ws_row0 + r) * kMlaDv) +
-                 kHalfV * hh;
-    const float inv = lrow[nt] > 0.f ? ps_ref / lrow[nt] : 0.f;
+                 kWaveDv * wave;
+    const float inv = lrow > 0.f ? ps_ref / lrow : 0.f;
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) {
       const f32x4 v = o[nt][mt] * inv;
       *reinterpret_cast<float4*>(dst + 16 * mt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
     }
-    if (g == 0 && hh == 0) {
-      const float lse = lrow[nt] > 0.f ? (mref[nt] + log2f(lrow[nt])) * kLn2M : kNegInf;
+    if (g == 0 && wave == 0) {
+      const float lse = lrow > 0.f ? (ref[nt] + log2f(lrow)) * kLn2M : kNegInf;
       if (direct)
         p.partial_lse[pair_row0 + r] = lse;
       else
