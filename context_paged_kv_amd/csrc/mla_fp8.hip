@@ -146,12 +146,17 @@ __device__ __forceinline__ void split_e4m3(const float v[4], uint32_t& hi, uint3
   lo = (uint32_t)w;
 }
 
-// Token (within a 32-token half page) held by MFMA row m of S^T tile tt (0 or
-// 1): the two tiles give the lane of group g the tokens 8g + [0, 8) of the
-// half, the k slots of its P^T operand.
-__device__ __forceinline__ int mla_tok(int tt, int m) {
-  return 8 * (m >> 2) + 4 * tt + (m & 3);
+// Token order of a 32-token half page.  The PV contraction takes, in k-step
+// slot (g, k) of a lane (g = lane / 16), token mla_vtok(g, k); the score MFMA
+// row m of S^T tile tt reads token mla_tok(tt, m) = mla_vtok(m / 4, 4 tt + m % 4),
+// so the output lane of group g holds the eight scores of its P^T slots.  The
+// order makes both LDS access patterns bank-conflict free with 592-byte rows:
+// the 16 rows of a score tile and the 16 rows a transposing read touches in a
+// half wave are distinct modulo 16.
+__device__ __forceinline__ int mla_vtok(int g, int k) {
+  return 4 * g + k + (k < 4 ? (g < 2 ? 0 : 16) : 4);
 }
+__device__ __forceinline__ int mla_tok(int tt, int m) { return mla_vtok(m >> 2, 4 * tt + (m & 3)); }
 
 // LDS slot q (16 bytes) of a page buffer, row q / 37 and column q % 37, holds
 // page bytes 16 * (q - q / 37) onwards.  Per-lane source offsets of the page copy: load i of wave w moves the 64
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
 #pragma unroll
       for (int i = kEarlyLoads; i < kLoadIters; ++i) ld(i);  // the rest, once the K operands are dead
 
-      // ---- this half's numerators (lane: row 16 rt + c, tokens 32 th + 8 g + [0, 8))
+      // ---- this half's numerators (lane: row 16 rt + c, tokens 32 th + mla_vtok(g, [0, 8)))
       const float f = sl2 * ps;
       if (!full) {
 #pragma unroll
@@ -483,9 +488,9 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
       l_s += psum * own * inv_ratio;
 
       // ---- O^T += V^T P^T over this wave's value dims
-      // source lane (g, c) of the transposing read points at token 32ks + 8g + (c >> 1),
-      // dims 16*mt + 8*(c & 1) .. +7; lane (g, j) then holds dim 16*mt + j of those 8 tokens
-      const uint8_t* vrow = cur + (8 * g + (c >> 1)) * kRawStride + 8 * (c & 1) + kWaveDv * wave;
+      // source lane (g, c) of the transposing read points at token 32 ks + mla_vtok(g, c >> 1),
+      // dims 16 mt + 8 (c & 1) .. +7; lane (g, j) then holds dim 16 mt + j of those 8 tokens
+      const uint8_t* vrow = cur + mla_vtok(g, c >> 1) * kRawStride + 8 * (c & 1) + kWaveDv * wave;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         f16x8 pk[kRowTiles];
