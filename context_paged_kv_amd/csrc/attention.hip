@@ -26,75 +26,67 @@ namespace dcpkv {
 // Plan: chunks per (shard, request) pair and workspace slots (one workgroup)
 // ---------------------------------------------------------------------------
 
-constexpr int kPlanThreads = 256;
+constexpr int kPlanThreads = 64;  // one wavefront: shuffles instead of barriers
+
+// Inclusive prefix sum over the wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
-  __shared__ int32_t s_k[kPlanThreads];
-  __shared__ int32_t s_w[kPlanThreads];
-  __shared__ unsigned long long s_need, s_need_all;
-  __shared__ int32_t s_carry_k, s_carry_w;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x;
   const int num_pairs = p.shard_count * p.batch;
   const int C = p.chunk_pages;
-  if (tid == 0) {
-    s_need = 0;
-    s_need_all = 0;
-    s_carry_k = 0;
-    s_carry_w = 0;
-  }
-  __syncthreads();
-  unsigned long long mine = 0, mine_all = 0;
-  for (int i = tid; i < num_pairs; i += kPlanThreads) {
+  auto pair_pages = [&](int i) {
     const int d = p.shard_begin + i / p.batch, b = i % p.batch;
-    const int nl = local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
+    return local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
+  };
+  // chunk totals first: one chunk per pair when the split would not fit the workspace or
+  // the launched grid
+  long long need = 0, need_all = 0;
+  for (int i = lane; i < num_pairs; i += 64) {
+    const int nl = pair_pages(i);
     const int k = nl > C ? (nl + C - 1) / C : 1;
-    if (k >= 2) mine += k;
-    mine_all += k;
+    if (k >= 2) need += k;
+    need_all += k;
   }
-  atomicAdd(&s_need, mine);
-  atomicAdd(&s_need_all, mine_all);
-  __syncthreads();
-  // one chunk per pair when the split would not fit the workspace or the launched grid
-  const int fallback =
-      (s_need > (unsigned long long)p.ws_cap || s_need_all > (unsigned long long)p.max_chunks) ? 1 : 0;
-  for (int base = 0; base < num_pairs; base += kPlanThreads) {
-    const int i = base + tid;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    need += __shfl_xor(need, off, 64);
+    need_all += __shfl_xor(need_all, off, 64);
+  }
+  const int fallback = (need > (long long)p.ws_cap || need_all > (long long)p.max_chunks) ? 1 : 0;
+  // then exclusive prefix sums of the chunks and of the workspace slots, 64 pairs at a time
+  int carry_k = 0, carry_w = 0;
+  for (int base = 0; base < num_pairs; base += 64) {
+    const int i = base + lane;
     int k = 0, kw = 0, nl = 0;
     if (i < num_pairs) {
-      const int d = p.shard_begin + i / p.batch, b = i % p.batch;
-      nl = local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
+      nl = pair_pages(i);
       k = (!fallback && nl > C) ? (nl + C - 1) / C : 1;
       kw = k >= 2 ? k : 0;
     }
-    s_k[tid] = k;
-    s_w[tid] = kw;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {  // inclusive scan
-      const int a = tid >= off ? s_k[tid - off] : 0;
-      const int w = tid >= off ? s_w[tid - off] : 0;
-      __syncthreads();
-      s_k[tid] += a;
-      s_w[tid] += w;
-      __syncthreads();
-    }
+    const int sk = wave_incl_scan(k), sw = wave_incl_scan(kw);
     if (i < num_pairs) {
       PairPlan pp;
-      pp.chunk_begin = s_carry_k + s_k[tid] - k;
-      pp.ws_begin = kw ? s_carry_w + s_w[tid] - kw : -1;
+      pp.chunk_begin = carry_k + sk - k;
+      pp.ws_begin = kw ? carry_w + sw - kw : -1;
       pp.k = k;
       pp.n_local = nl;
       p.pairs[i] = pp;
     }
-    __syncthreads();
-    if (tid == kPlanThreads - 1) {
-      s_carry_k += s_k[tid];
-      s_carry_w += s_w[tid];
-    }
-    __syncthreads();
+    carry_k += __shfl(sk, 63, 64);
+    carry_w += __shfl(sw, 63, 64);
   }
-  if (tid == 0) {
-    p.hdr->total_chunks = s_carry_k;
-    p.hdr->ws_chunks = s_carry_w;
+  if (lane == 0) {
+    p.hdr->total_chunks = carry_k;
+    p.hdr->ws_chunks = carry_w;
     p.hdr->fallback = fallback;
   }
 }

@@ -89,10 +89,59 @@ __device__ __forceinline__ float wave_sum(float v) {
 //   m = max_i L_i, LSE = m + log sum_i exp(L_i - m), out = sum_i exp(L_i - LSE) O_i
 // ([2DR] section 5.2 for LSE; the O rule is the exact recombination of [SGL]).
 // Partial i's LSE is at lse[i * lse_stride], its output at o + i * o_stride.
+// Partials with LSE = -inf (no visible token) take no part, whatever their O holds.
+// Up to 64 partials, lane i holds L_i and its weight, and the O loads of four
+// partials are in flight together, so a row costs two memory round trips.
 __device__ inline void wave_merge_row(int count, const float* __restrict__ lse, int64_t lse_stride,
                                       const float* __restrict__ o, int64_t o_stride, int dv,
                                       float* __restrict__ out, float* __restrict__ out_lse) {
   const int lane = threadIdx.x & 63;
+  if (count <= 64) {
+    const float l = lane < count ? lse[lane * lse_stride] : kNegInf;
+    const float m = wave_max(l);
+    if (m == kNegInf) {
+      for (int c = lane; c < dv; c += 64) out[c] = 0.f;
+      if (lane == 0 && out_lse) *out_lse = kNegInf;
+      return;
+    }
+    const float tot = m + logf(wave_sum(l == kNegInf ? 0.f : expf(l - m)));
+    if (lane == 0 && out_lse) *out_lse = tot;
+    const float w = l == kNegInf ? 0.f : expf(l - tot);
+    if ((dv & 3) == 0 && (o_stride & 3) == 0) {
+      for (int c = lane * 4; c < dv; c += 256) {
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i0 = 0; i0 < count; i0 += 4) {
+          float4 x[4];
+          float wi[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = min(i0 + u, count - 1);
+            wi[u] = i0 + u < count ? __shfl(w, i, 64) : 0.f;
+            x[u] = *reinterpret_cast<const float4*>(o + i * o_stride + c);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (wi[u] == 0.f) continue;  // an empty partial's O may hold anything
+            acc.x += wi[u] * x[u].x;
+            acc.y += wi[u] * x[u].y;
+            acc.z += wi[u] * x[u].z;
+            acc.w += wi[u] * x[u].w;
+          }
+        }
+        *reinterpret_cast<float4*>(out + c) = acc;
+      }
+    } else {
+      for (int c = lane; c < dv; c += 64) {
+        float acc = 0.f;
+        for (int i = 0; i < count; ++i) {
+          const float wi = __shfl(w, i, 64);
+          if (wi != 0.f) acc += wi * o[i * o_stride + c];
+        }
+        out[c] = acc;
+      }
+    }
+    return;
+  }
   float m = kNegInf;
   for (int i = lane; i < count; i += 64) m = fmaxf(m, lse[i * lse_stride]);
   m = wave_max(m);
