@@ -45,7 +45,8 @@ Q_F32, Q_BF16 = 0, 1
 EXPORTED = (
     "dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
     "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
-    "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
+    "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_path_entries", "kv_pack_pages",
+    "kv_unpack_pages",
     "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge",
 )
 
@@ -90,6 +91,11 @@ _lib.dcp_pagemap_release.argtypes = [_P, _I64P, C.c_int64]
 _lib.dcp_build_block_tables.argtypes = [C.c_int32, C.c_int32, _I64P, _I64P, C.c_int32, _I32P, _I32P]
 _lib.kv_reshard_pages.argtypes = [C.POINTER(kv_reshard_desc), C.POINTER(_P), C.POINTER(_P),
                                   C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, C.c_int64, _P, _P]
+_lib.kv_path_entries.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, C.c_int64, C.c_int64, _P, _P, _P]
+_lib.kv_pack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, _P, _P, _P, C.c_int64, C.c_int64,
+                               _P, _P, _P, _P]
+_lib.kv_unpack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, C.c_int64,
+                                 C.c_int64, _P, _P, _P]
 _lib.dcp_decode_partial_workspace.argtypes = [C.POINTER(dcp_attn_desc), C.c_int64]
 _lib.dcp_decode_partial_workspace.restype = C.c_size_t
 _lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P,
@@ -97,6 +103,7 @@ _lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P),
 _lib.dcp_lse_merge.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P]
 for _f in ("cp_layersplit_layer_range", "dcp_filter_kv_indices", "dcp_pagemap_create",
            "dcp_pagemap_alloc", "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
+           "kv_path_entries", "kv_pack_pages", "kv_unpack_pages",
            "dcp_decode_partial", "dcp_lse_merge"):
     getattr(_lib, _f).restype = C.c_int
 
@@ -245,6 +252,43 @@ def kv_reshard_pages(*, num_layers: int, dcp_size: int, page_bytes: int, src_pag
                                  _ptr_array(src_scales), _ptr_array(dst_scales), _dptr(src_page_ids),
                                  _dptr(dst_global_pages), n, first_uncached, _dptr(bad_entries),
                                  _stream(stream)))
+
+
+def _path_desc(num_sources: int, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int,
+               dst_pages: int) -> kv_reshard_desc:
+    return kv_reshard_desc(num_sources, num_layers, dcp_size, -1, page_bytes, src_pages, dst_pages)
+
+
+def kv_path_entries(*, num_sources: int, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int,
+                    dst_pages: int, dest: int, src_page_ids, dst_global_pages, out_positions, out_count,
+                    first_uncached: int = 0, num_pages: Optional[int] = None, stream=None) -> None:
+    """Enqueue the entry list of the path to `dest` (see include/dcpkv.h)."""
+    desc = _path_desc(num_sources, num_layers, dcp_size, page_bytes, src_pages, dst_pages)
+    n = src_page_ids.numel() if num_pages is None else num_pages
+    _check(_lib.kv_path_entries(C.byref(desc), dest, _dptr(src_page_ids), _dptr(dst_global_pages), n,
+                                first_uncached, _dptr(out_positions), _dptr(out_count), _stream(stream)))
+
+
+def kv_pack_pages(*, num_sources: int, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int,
+                  dst_pages: int, source: int, src_pool, src_page_ids, positions, count, unit_begin: int,
+                  cap_units: int, staging, src_scales=None, staging_scales=None, out_units=None,
+                  stream=None) -> None:
+    """Enqueue the packing of one window of units of path (source, .) (see include/dcpkv.h)."""
+    desc = _path_desc(num_sources, num_layers, dcp_size, page_bytes, src_pages, dst_pages)
+    _check(_lib.kv_pack_pages(C.byref(desc), source, _dptr(src_pool), _dptr(src_scales), _dptr(src_page_ids),
+                              _dptr(positions), _dptr(count), unit_begin, cap_units, _dptr(staging),
+                              _dptr(staging_scales), _dptr(out_units), _stream(stream)))
+
+
+def kv_unpack_pages(*, num_sources: int, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int,
+                    dst_pages: int, source: int, dest: int, dst_pool, dst_global_pages, positions, count,
+                    unit_begin: int, cap_units: int, staging, dst_scales=None, staging_scales=None,
+                    stream=None) -> None:
+    """Enqueue the unpacking of one window of units into destination `dest` (see include/dcpkv.h)."""
+    desc = _path_desc(num_sources, num_layers, dcp_size, page_bytes, src_pages, dst_pages)
+    _check(_lib.kv_unpack_pages(C.byref(desc), source, dest, _dptr(dst_pool), _dptr(dst_scales),
+                                _dptr(dst_global_pages), _dptr(positions), _dptr(count), unit_begin, cap_units,
+                                _dptr(staging), _dptr(staging_scales), _stream(stream)))
 
 
 def make_attn_desc(*, kv_dtype: int, kv_layout: int, q_dtype: int, num_q_heads: int, num_kv_heads: int,

@@ -5,6 +5,8 @@
  * Sources of the operations (cited by short name):
  *   [2DR]  "Serving Macaron-V1 at Scale: Page-Level 2D KV Resharding"
  *   [SGL]  "SGLang's path" (serving-k3, module 05, the DCP paragraph)
+ *   [PR28] the fivechenxi/sglang pull request #28 thread (the bounded-pack
+ *          review and the address-translation comment)
  *
  * Conventions shared by every entry point
  *   - Status: 0 (DCPKV_OK) on success, a negative errno-style code on error.
@@ -174,6 +176,60 @@ DCPKV_API int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* s
                      void* const* dst_scales, const int32_t* src_page_ids,
                      const int64_t* dst_global_pages, int64_t num_pages,
                      int64_t first_uncached, int32_t* bad_entries, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * (1b) Bounded pack / unpack of one (source, destination) path              *
+ *      ([2DR] section 2: a path carries L_r x P_d pages; sections 6.2-6.3:   *
+ *      ownership by destination page value; [PR28]: a fixed-size pack       *
+ *      buffer reused in chunks when a transfer does not fit)                 *
+ * ------------------------------------------------------------------------ */
+
+/* Entries of the path to destination `dest`: the list positions
+ * i in [first_uncached, num_pages) whose ids are in range (src_page_ids[i] in
+ * [0, S), g = dst_global_pages[i] in [0, M*N)) and whose owner is dest
+ * (g mod N == dest; with N == 1 every entry), in list order.  Writes them to
+ * out_positions (device int32, capacity num_pages - first_uncached) and their
+ * number to out_count (device int64 [1]).  desc gives N, S and M (its
+ * dst_filter is ignored).  One workgroup reads each list once.
+ * EINVAL on a bad descriptor, dest outside [0, N), num_pages > INT32_MAX,
+ * first_uncached outside [0, num_pages] or NULL arrays. */
+DCPKV_API int kv_path_entries(const kv_reshard_desc* desc, int32_t dest, const int32_t* src_page_ids,
+                    const int64_t* dst_global_pages, int64_t num_pages, int64_t first_uncached,
+                    int32_t* out_positions, int64_t* out_count, void* stream);
+
+/* The path (source r, destination d) carries count * |L_r| units, count being
+ * the out_count of kv_path_entries (read on the device; no host wait).  Unit u
+ * is layer l_u = begin_r + (u mod |L_r|) of entry i_u = positions[u div |L_r|]
+ * (entry-major: one page's layers are consecutive).  kv_pack_pages copies the
+ * window of n = min(cap_units, count * |L_r| - unit_begin) units (none if that
+ * is negative) starting at unit_begin into a contiguous staging buffer:
+ *     staging[k] = src_pool[l_u - begin_r][src_page_ids[i_u]]   (page_bytes bytes)
+ *     staging_scales[k] = src_scales[l_u - begin_r][src_page_ids[i_u]]
+ * for k = u - unit_begin, and writes n to out_units (device int64 [1],
+ * nullable).  src_pool is source r's pool [|L_r|+1][S][page_bytes] (device),
+ * src_scales its bf16 scales [|L_r|+1][S] or NULL (then staging_scales must
+ * be NULL too).  staging holds cap_units pages (16-byte aligned),
+ * staging_scales cap_units bf16 values.  A caller packs windows
+ * unit_begin = 0, cap, 2 cap, ... until the unit count (read back once, or
+ * known on the host) is covered; the staging buffer is reused per window.
+ * EINVAL on a bad descriptor, source outside [0, N_cp), unit_begin < 0,
+ * cap_units < 1, NULL or misaligned pointers, scales given on one side only. */
+DCPKV_API int kv_pack_pages(const kv_reshard_desc* desc, int32_t source, const void* src_pool,
+                  const void* src_scales, const int32_t* src_page_ids, const int32_t* positions,
+                  const int64_t* count, int64_t unit_begin, int64_t cap_units, void* staging,
+                  void* staging_scales, int64_t* out_units, void* stream);
+
+/* The destination side of the same window:
+ *     dst_pool[l_u][g div N] = staging[k],   g = dst_global_pages[i_u]  (N == 1: slot g)
+ *     dst_scales[l_u][g div N] = staging_scales[k]
+ * dst_pool is destination `dest`'s pool [L][M][page_bytes], dst_scales its
+ * [L][M] bf16 scales or NULL (with staging_scales NULL).  Run over every window
+ * of every path (r, d), pack + unpack write exactly what kv_reshard_pages
+ * writes, byte for byte.  Errors as kv_pack_pages, plus dest outside [0, N). */
+DCPKV_API int kv_unpack_pages(const kv_reshard_desc* desc, int32_t source, int32_t dest, void* dst_pool,
+                    void* dst_scales, const int64_t* dst_global_pages, const int32_t* positions,
+                    const int64_t* count, int64_t unit_begin, int64_t cap_units, const void* staging,
+                    const void* staging_scales, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * (2) Per-shard partial decode attention ([2DR] sections 5.2, 8; [SGL])    *

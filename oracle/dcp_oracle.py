@@ -11,7 +11,7 @@ Sources (cited by short name below):
   [2DR]  "Serving Macaron-V1 at Scale: Page-Level 2D KV Resharding" (macaron.im)
   [SGL]  "SGLang's path" (serving-k3, module 05; the DCP paragraph)
   [PR28] the fivechenxi/sglang pull request #28 thread (address-translation
-         review comment)
+         review comment; the review of the bounded-pack commit)
 
 Readings where the pages are silent or garbled (each one is listed in the
 design notes as well):
@@ -41,6 +41,10 @@ design notes as well):
   R11 An empty shard yields (O, LSE) = (0, -inf) and gets zero weight.
   R12 The free list is a FIFO: allocation pops from the front, freeing
       appends to the back.
+  R17 Bounded pack: a path's pages are packed entry-major (one page's layers in
+      a row) into a staging buffer of a fixed number of pages, window after
+      window; the pages give the idea (a fixed pre-registered buffer reused in
+      chunks, the same bytes moved), not a layout, so the order is ours.
 
 Parity pins live in tests/test_oracle_pins.py; every function here has one.
 """
@@ -227,6 +231,79 @@ def reshard(src_pools: Sequence[np.ndarray], dst_pools: Sequence[np.ndarray],
         if r == 0 and ls == 0:
             sent[d] += 1
     return sent
+
+
+# --------------------------------------------------------------------------
+# Bounded pack / unpack of one (source, destination) path (reading R17)
+# --------------------------------------------------------------------------
+
+
+def path_entries(src_page_ids, dst_global_pages, first_uncached: int, dcp_size: int, dest: int,
+                 src_pages: int, dst_pages: int) -> List[int]:
+    """List positions the path to `dest` carries, in list order.
+
+    [2DR] section 2: a path moves P_d pages; section 6.3: ownership by the
+    destination page value (reading R6); reading R7: entries before
+    first_uncached are cached.  Entries with ids out of range carry nothing
+    (the reshard skips them too).
+    """
+    out = []
+    for i in range(first_uncached, len(dst_global_pages)):
+        g, sp = int(dst_global_pages[i]), int(src_page_ids[i])
+        if dcp_size > 1:
+            d, s = dcp_owner(g, dcp_size) if g >= 0 else -1, g // dcp_size if g >= 0 else -1
+        else:
+            d, s = 0, g
+        if g < 0 or s >= dst_pages or not (0 <= sp < src_pages):
+            continue
+        if d == dest:
+            out.append(i)
+    return out
+
+
+def path_units(num_layers: int, num_sources: int, r: int, entries: Sequence[int]) -> List[Tuple[int, int]]:
+    """Units (list position, layer) of path (r, .), entry-major: one page's |L_r| layers in a row
+    ([2DR] section 2: the path carries L_r x P_d pages)."""
+    a, b = layer_range(num_layers, num_sources, r)
+    return [(i, layer) for i in entries for layer in range(a, b)]
+
+
+def pack_pages(src_pool: np.ndarray, src_scale, src_page_ids, num_layers: int, num_sources: int, r: int,
+               entries: Sequence[int], unit_begin: int, cap_units: int, staging: np.ndarray,
+               staging_scales=None) -> int:
+    """Copy the window of units [unit_begin, unit_begin + n) of path (r, .) into staging (in place).
+
+    [PR28] bounded pack: a fixed buffer of cap_units pages is filled window by
+    window; n = min(cap_units, units - unit_begin), none past the end.
+    staging[k] = src_pool[layer - begin_r][src page of the entry], k = u - unit_begin.
+    """
+    units = path_units(num_layers, num_sources, r, entries)
+    a, _ = layer_range(num_layers, num_sources, r)
+    n = max(0, min(cap_units, len(units) - unit_begin))
+    for k in range(n):
+        i, layer = units[unit_begin + k]
+        sp = int(src_page_ids[i])
+        staging[k, :] = src_pool[layer - a, sp, :]
+        if src_scale is not None and staging_scales is not None:
+            staging_scales[k] = src_scale[layer - a, sp]
+    return n
+
+
+def unpack_pages(dst_pool: np.ndarray, dst_scale, dst_global_pages, num_layers: int, num_sources: int, r: int,
+                 dcp_size: int, entries: Sequence[int], unit_begin: int, cap_units: int, staging: np.ndarray,
+                 staging_scales=None) -> int:
+    """Scatter the same window from staging into the destination pool (in place):
+    dst_pool[layer][g div N] = staging[k] (N == 1: slot g), section 6.3's value-owned slot."""
+    units = path_units(num_layers, num_sources, r, entries)
+    n = max(0, min(cap_units, len(units) - unit_begin))
+    for k in range(n):
+        i, layer = units[unit_begin + k]
+        g = int(dst_global_pages[i])
+        s = dcp_local_slot(g, dcp_size) if dcp_size > 1 else g
+        dst_pool[layer, s, :] = staging[k, :]
+        if dst_scale is not None and staging_scales is not None:
+            dst_scale[layer, s] = staging_scales[k]
+    return n
 
 
 # --------------------------------------------------------------------------

@@ -318,6 +318,51 @@ def run_reshard(rc: ReshardCase, dst_filter=-1, bad=None, src_ids=None, dst_ids=
     return si, di
 
 
+def run_path_pack(rc: ReshardCase, cap_units: int, stream=None, src_ids=None, dst_ids=None, check_windows=None):
+    """The reshard done path by path through a staging buffer of cap_units pages: for every
+    destination d, kv_path_entries, then for every source r the windows of kv_pack_pages /
+    kv_unpack_pages.  check_windows(d, r, u0, staging, staging_scales, n) is called after each
+    pack (synchronised).  Returns the number of units moved."""
+    w = rc.w
+    dev = rc.src_pools[0].device
+    si = torch.from_numpy((rc.src_ids if src_ids is None else src_ids).astype(np.int32)).to(dev)
+    di = torch.from_numpy((rc.dst_ids if dst_ids is None else dst_ids).astype(np.int64)).to(dev)
+    P = si.numel()
+    geo = dict(num_sources=rc.num_sources, num_layers=rc.num_layers, dcp_size=w.dcp_size, page_bytes=w.page_bytes,
+               src_pages=rc.src_pages, dst_pages=w.pool_pages)
+    pos = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+    cnt = torch.empty(1, dtype=torch.int64, device=dev)
+    nout = torch.empty(1, dtype=torch.int64, device=dev)
+    stg = torch.empty((cap_units, w.page_bytes), dtype=torch.uint8, device=dev)
+    stg_sc = torch.empty(cap_units, dtype=torch.int16, device=dev) if rc.src_scales is not None else None
+    moved = 0
+    for d in range(w.dcp_size):
+        K.kv_path_entries(dest=d, src_page_ids=si, dst_global_pages=di, out_positions=pos, out_count=cnt,
+                          first_uncached=rc.first_uncached, stream=stream, **geo)
+        count = int(cnt.item())
+        for r in range(rc.num_sources):
+            a, b = K.cp_layersplit_layer_range(rc.num_layers, rc.num_sources, r)
+            total = count * (b - a)
+            for u0 in range(0, total, cap_units):
+                if check_windows is not None:
+                    gen.sentinel_fill_(stg, gen.DST_SENTINEL)
+                    if stg_sc is not None:
+                        stg_sc.fill_(gen.SCALE_SENTINEL)
+                K.kv_pack_pages(source=r, src_pool=rc.src_pools[r], src_page_ids=si, positions=pos, count=cnt,
+                                unit_begin=u0, cap_units=cap_units, staging=stg,
+                                src_scales=None if rc.src_scales is None else rc.src_scales[r],
+                                staging_scales=stg_sc, out_units=nout, stream=stream, **geo)
+                if check_windows is not None:
+                    torch.cuda.synchronize()
+                    check_windows(d, r, u0, stg, stg_sc, int(nout.item()), pos, count)
+                K.kv_unpack_pages(source=r, dest=d, dst_pool=rc.dst_pools[d], dst_global_pages=di, positions=pos,
+                                  count=cnt, unit_begin=u0, cap_units=cap_units, staging=stg,
+                                  dst_scales=None if rc.dst_scales is None else rc.dst_scales[d],
+                                  staging_scales=stg_sc, stream=stream, **geo)
+                moved += min(cap_units, total - u0)
+    return moved
+
+
 def check_reshard_by_plan(rc: ReshardCase, dst_filter=-1, sentinel=gen.DST_SENTINEL):
     """Bit-exact check of every destination page against the oracle's copy plan.
 

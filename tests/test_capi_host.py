@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTED)
-    assert K.dcpkv_abi_version() == 1
+    assert K.dcpkv_abi_version() == 2
 
 
 @pytest.mark.parametrize("L_,n", [(78, 8), (64, 4), (4, 4), (17, 5), (1, 1), (100, 7)])
@@ -145,3 +145,26 @@ def test_device_entry_points_reject_bad_arguments_on_host():
     rc = L._lib.dcp_decode_partial(C.byref(good), C.c_void_p(256), p, None, C.c_void_p(256), C.c_void_p(256), 0,
                                    2, 3, C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1 << 30, None)
     assert rc == L.DCPKV_EINVAL and "shard range" in K.dcpkv_last_error()
+
+
+def test_path_entry_points_reject_bad_arguments_on_host():
+    """The bounded-pack calls check their arguments before anything is enqueued."""
+    v = C.c_void_p(256)
+    good = L.kv_reshard_desc(2, 4, 2, -1, 64, 8, 8)
+    odd = L.kv_reshard_desc(2, 4, 2, -1, 72, 8, 8)  # page_bytes not a multiple of 16
+    E = L.DCPKV_EINVAL
+    assert L._lib.kv_path_entries(None, 0, v, v, 4, 0, v, v, None) == E
+    assert L._lib.kv_path_entries(C.byref(good), 2, v, v, 4, 0, v, v, None) == E  # dest outside [0, N)
+    assert L._lib.kv_path_entries(C.byref(good), 0, v, v, 4, 5, v, v, None) == E  # first_uncached > num_pages
+    assert L._lib.kv_path_entries(C.byref(good), 0, v, v, 4, 0, None, v, None) == E
+    assert L._lib.kv_path_entries(C.byref(good), 0, v, v, 1 << 31, 0, v, v, None) == E
+    assert L._lib.kv_pack_pages(C.byref(odd), 0, v, None, v, v, v, 0, 4, v, None, None, None) == E
+    assert L._lib.kv_pack_pages(C.byref(good), 2, v, None, v, v, v, 0, 4, v, None, None, None) == E  # source
+    assert L._lib.kv_pack_pages(C.byref(good), 0, v, None, v, v, v, 0, 0, v, None, None, None) == E  # cap 0
+    assert L._lib.kv_pack_pages(C.byref(good), 0, v, None, v, v, v, -1, 4, v, None, None, None) == E
+    assert L._lib.kv_pack_pages(C.byref(good), 0, v, v, v, v, v, 0, 4, v, None, None, None) == E  # one scale side
+    rc = L._lib.kv_pack_pages(C.byref(good), 0, C.c_void_p(264), None, v, v, v, 0, 4, v, None, None, None)
+    assert rc == E and "aligned" in K.dcpkv_last_error()
+    assert L._lib.kv_unpack_pages(C.byref(good), 0, 2, v, None, v, v, v, 0, 4, v, None, None) == E  # dest
+    assert L._lib.kv_unpack_pages(C.byref(good), 0, 0, v, v, v, v, v, 0, 4, v, None, None) == E  # one scale side
+    assert L._lib.kv_unpack_pages(C.byref(good), 0, 0, None, None, v, v, v, 0, 4, v, None, None) == E

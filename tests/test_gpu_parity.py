@@ -261,3 +261,79 @@ def test_reshard_out_of_range_entries_are_skipped_and_counted():
     O.reshard(_host_pools(rc.src_pools), dst_host, 3, 2, src[keep], dst[keep], 0)
     for d in range(2):
         assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
+# --------------------------------------------------------------------------- bounded pack / unpack
+
+
+@pytest.mark.parametrize("cap", [1, 3, 22, 4096])
+def test_path_pack_unpack_windows_vs_oracle(cap):
+    """Entries, every staging window (pages, scales, unit count) and the final destination pools
+    of the path-by-path transfer, bit for bit against the oracle; the pools also equal what the
+    oracle's reshard writes."""
+    base = get_workload("reshard_mla_128k")
+    w = scaled(base, seed=base.seed + 110, seq_segments=((1, 64 * 37 + 13, 64 * 37 + 13),), num_layers=7,
+               num_sources=3, pool_pages=16, dcp_size=4)
+    H.log(f"path pack/unpack 3 sources x 7 layers N=4 cached=5 cap={cap}")
+    rc = H.make_reshard_case(w, DEV, first_uncached=5)
+    src_host = _host_pools(rc.src_pools)
+    ssc_host = _host_pools(rc.src_scales)
+    dst_host = _host_pools(rc.dst_pools)
+    dsc_host = _host_pools(rc.dst_scales)
+    ref_dst = [a.copy() for a in dst_host]
+    ref_dsc = [a.copy() for a in dsc_host]
+    O.reshard(src_host, ref_dst, rc.num_layers, w.dcp_size, rc.src_ids, rc.dst_ids, 5, -1, ssc_host, ref_dsc)
+    seen = []
+
+    def check(d, r, u0, stg, stg_sc, n, pos, count):
+        ent = O.path_entries(rc.src_ids, rc.dst_ids, 5, w.dcp_size, d, rc.src_pages, w.pool_pages)
+        assert count == len(ent) and pos[:count].cpu().numpy().tolist() == ent
+        ostg = np.full((cap, w.page_bytes), gen.DST_SENTINEL, dtype=np.uint8)
+        osc = np.full(cap, gen.SCALE_SENTINEL, dtype=np.int16)
+        k = O.pack_pages(src_host[r], ssc_host[r], rc.src_ids, rc.num_layers, rc.num_sources, r, ent, u0, cap,
+                         ostg, osc)
+        assert n == k
+        assert np.array_equal(stg.cpu().numpy(), ostg) and np.array_equal(stg_sc.cpu().numpy(), osc)
+        O.unpack_pages(dst_host[d], dsc_host[d], rc.dst_ids, rc.num_layers, rc.num_sources, r, w.dcp_size, ent,
+                       u0, cap, ostg, osc)
+        seen.append(k)
+
+    moved = H.run_path_pack(rc, cap, check_windows=check)
+    _sync()
+    assert moved == sum(seen) == (len(rc.dst_ids) - 5) * rc.num_layers
+    for d in range(w.dcp_size):
+        got = rc.dst_pools[d].cpu().numpy()
+        assert np.array_equal(got, dst_host[d]) and np.array_equal(got, ref_dst[d])
+        got_sc = rc.dst_scales[d].cpu().numpy()
+        assert np.array_equal(got_sc, dsc_host[d]) and np.array_equal(got_sc, ref_dsc[d])
+
+
+def test_path_entries_value_owned_and_bad_ids_excluded():
+    base = get_workload("reshard_mla_128k")
+    w = scaled(base, seed=base.seed + 111, seq_segments=((1, 64 * 8, 64 * 8),), num_layers=2, num_sources=1,
+               pool_pages=8, dcp_size=4)
+    rc = H.make_reshard_case(w, DEV, first_uncached=0)
+    rc.dst_ids = np.array([7, 2, 4, 13, 0, 9, 30, 17], dtype=np.int64)  # residues differ from positions
+    src = rc.src_ids.copy()
+    dst = rc.dst_ids.copy()
+    src[1] = rc.src_pages + 5
+    dst[4] = w.pool_pages * 4 + 3
+    dst[5] = -1
+    si = torch.from_numpy(src.astype(np.int32)).to(DEV)
+    di = torch.from_numpy(dst).to(DEV)
+    pos = torch.empty(8, dtype=torch.int32, device=DEV)
+    cnt = torch.empty(1, dtype=torch.int64, device=DEV)
+    for d in range(4):
+        K.kv_path_entries(num_sources=1, num_layers=2, dcp_size=4, page_bytes=w.page_bytes, src_pages=rc.src_pages,
+                          dst_pages=w.pool_pages, dest=d, src_page_ids=si, dst_global_pages=di, out_positions=pos,
+                          out_count=cnt)
+        _sync()
+        want = O.path_entries(src, dst, 0, 4, d, rc.src_pages, w.pool_pages)
+        assert pos[: int(cnt.item())].cpu().numpy().tolist() == want
+    dst_host = _host_pools([torch.full_like(t, gen.DST_SENTINEL) for t in rc.dst_pools])
+    keep = [i for i in range(8) if i not in (1, 4, 5)]
+    O.reshard(_host_pools(rc.src_pools), dst_host, 2, 4, src[keep], dst[keep], 0)
+    H.run_path_pack(rc, 3, src_ids=src, dst_ids=dst)
+    _sync()
+    for d in range(4):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])

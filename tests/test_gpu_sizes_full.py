@@ -98,3 +98,18 @@ def test_full_longmix_verify_pipeline():
             H.check_rows(f"L{layer} merged b={b}", outs.out[b][:, heads].cpu().numpy(),
                          outs.lse[b][:, heads].cpu().numpy(), uo[:, heads], ul[:, heads], tol_o, tol_l)
         H.log(f"  layer {layer}: sampled rows match")
+
+
+def test_full_path_pack_unpack_mla_128k():
+    """The full 128K reshard done path by path through a 256-page (9 MiB) staging buffer, checked
+    bit for bit against the oracle's copy plan like the direct reshard."""
+    w = get_workload("reshard_mla_128k")
+    H.log("full path pack/unpack: 4 sources x 16 of 64 layers, 2048 pages, 40% cached, N=8, 256-page windows")
+    rc = H.make_reshard_case(w, DEV)
+    chk = [t.view(torch.int64).sum().item() for t in rc.src_pools]
+    moved = H.run_path_pack(rc, 256)
+    torch.cuda.synchronize()
+    assert moved == 64 * (2048 - 819)
+    assert H.check_reshard_by_plan(rc) == 64 * (2048 - 819)
+    assert chk == [t.view(torch.int64).sum().item() for t in rc.src_pools]
+    H.log(f"  {moved} units verified")

@@ -227,6 +227,116 @@ def test_reshard_moves_scales():
             assert (dst[gg % n][layer, gg // n] == src[0][layer, sp[i]]).all()
 
 
+# --------------------------------------------------------------------------- bounded pack / unpack
+
+
+def _pack_all(srcp, ssc, src_ids, g, L, n, cached, S, M, cap, page_bytes, dst, dsc=None):
+    """Every path (r, d), window after window through a staging buffer of `cap` pages."""
+    ncp = len(srcp)
+    packed = 0
+    for d in range(n):
+        ent = O.path_entries(src_ids, g, cached, n, d, S, M)
+        for r in range(ncp):
+            u0 = 0
+            while True:
+                stg = np.full((cap, page_bytes), 0x5A, dtype=np.uint8)
+                stg_sc = np.zeros(cap, np.uint16) if ssc is not None else None
+                k = O.pack_pages(srcp[r], None if ssc is None else ssc[r], src_ids, L, ncp, r, ent, u0, cap, stg,
+                                 stg_sc)
+                if k == 0:
+                    break
+                O.unpack_pages(dst[d], None if dsc is None else dsc[d], g, L, ncp, r, n, ent, u0, cap, stg, stg_sc)
+                packed += k
+                u0 += k
+    return packed
+
+
+@pytest.mark.parametrize("n,cached,cap", [(1, 0, 1), (2, 0, 3), (4, 3, 2), (3, 5, 7), (4, 2, 1000)])
+def test_pack_unpack_round_trip_pull_view(n, cached, cap):
+    """Window after window, pack + unpack over every path leaves each destination page exactly
+    what the 2D target says ([2DR] section 2; ownership by value, section 6.3), checked page by
+    page from the tags, and exactly what the reshard writes."""
+    L, ncp, S, M, psz, page_bytes = 7, 3, 30, 20, 16, 32
+    rng = np.random.default_rng(11 + n)
+    pm = O.PageMap(n, psz, M, rng.permutation(M))
+    g = pm.alloc(19 * psz - 5)
+    P = len(g)
+    src = rng.permutation(S)[:P]
+    srcp = _tagged_sources(L, ncp, S, page_bytes)
+    dst = [np.full((L, M, page_bytes), 0xA5, dtype=np.uint8) for _ in range(n)]
+    packed = _pack_all(srcp, None, src, g, L, n, cached, S, M, cap, page_bytes, dst)
+    assert packed == (P - cached) * L  # the same pages move, only in windows
+    where = {int(gg): i for i, gg in enumerate(g)}
+    for d in range(n):
+        for layer in range(L):
+            owner = next(r for r in range(ncp) if O.layer_range(L, ncp, r)[0] <= layer < O.layer_range(L, ncp, r)[1])
+            for s_ in range(M):
+                i = where.get(s_ * n + d)
+                page = dst[d][layer, s_]
+                if i is None or i < cached:
+                    assert (page == 0xA5).all()
+                else:
+                    tag = page[:16].view(np.int32)
+                    assert tag.tolist() == [owner, layer - O.layer_range(L, ncp, owner)[0], int(src[i]), 0xC0FFEE]
+    ref = [np.full((L, M, page_bytes), 0xA5, dtype=np.uint8) for _ in range(n)]
+    O.reshard(srcp, ref, L, n, src, g, cached)
+    for d in range(n):
+        assert np.array_equal(dst[d], ref[d])
+
+
+def test_pack_windows_hand_example():
+    """A window layout worked by hand from the definition: L = 4 over 2 sources (layers 0-1, 2-3),
+    N = 2, g = [5, 2, 3, 0, 6], one cached page.  Path to d = 0 takes positions 1, 3, 4 (values
+    2, 0, 6); source 1's units are (1,2) (1,3) (3,2) (3,3) (4,2) (4,3); four-page windows."""
+    L, ncp, n, S, M, pb = 4, 2, 2, 16, 8, 16
+    g = [5, 2, 3, 0, 6]
+    src = [10, 11, 12, 13, 14]
+    ent = O.path_entries(src, g, 1, n, 0, S, M)
+    assert ent == [1, 3, 4]
+    assert O.path_entries(src, g, 1, n, 1, S, M) == [2]
+    assert O.path_units(L, ncp, 1, ent) == [(1, 2), (1, 3), (3, 2), (3, 3), (4, 2), (4, 3)]
+    pool = np.zeros((3, S, pb), dtype=np.uint8)
+    for ls in range(3):
+        for sp in range(S):
+            pool[ls, sp] = 16 * ls + sp
+    stg = np.zeros((4, pb), dtype=np.uint8)
+    assert O.pack_pages(pool, None, src, L, ncp, 1, ent, 0, 4, stg) == 4
+    assert stg[:, 0].tolist() == [11, 16 + 11, 13, 16 + 13]
+    stg[:] = 0
+    assert O.pack_pages(pool, None, src, L, ncp, 1, ent, 4, 4, stg) == 2
+    assert stg[:, 0].tolist() == [14, 16 + 14, 0, 0]
+    assert O.pack_pages(pool, None, src, L, ncp, 1, ent, 6, 4, stg) == 0
+    dst = np.zeros((L, M, pb), dtype=np.uint8)
+    stg[:] = 0
+    O.pack_pages(pool, None, src, L, ncp, 1, ent, 0, 4, stg)
+    assert O.unpack_pages(dst, None, g, L, ncp, 1, n, ent, 0, 4, stg) == 4
+    # value 2 -> slot 1, value 0 -> slot 0, layers 2 and 3
+    assert dst[2, 1, 0] == 11 and dst[3, 1, 0] == 16 + 11 and dst[2, 0, 0] == 13 and dst[3, 0, 0] == 16 + 13
+    assert int(dst.astype(np.int64).sum()) == pb * (11 + 27 + 13 + 29)
+
+
+def test_pack_excludes_bad_ids_and_scales_ride_along():
+    """Entries whose ids fall outside the pools carry nothing (the reshard skips them too); page
+    scales travel with their pages through the staging buffer."""
+    L, ncp, n, S, M, pb = 2, 1, 2, 6, 4, 8
+    g = [4, 1, 9, 2, -3, 7]   # 9 >= M*N and -3 are out of range
+    src = [5, 0, 3, 6, 1, 2]  # 6 >= S is out of range
+    assert O.path_entries(src, g, 0, n, 0, S, M) == [0]
+    assert O.path_entries(src, g, 0, n, 1, S, M) == [1, 5]
+    pool = np.arange(3 * S * pb, dtype=np.uint8).reshape(3, S, pb)
+    ssc = [np.arange(3 * S, dtype=np.uint16).reshape(3, S) + 1000]
+    dst = [np.zeros((L, M, pb), np.uint8) for _ in range(n)]
+    dsc = [np.zeros((L, M), np.uint16) for _ in range(n)]
+    _pack_all([pool], ssc, src, g, L, n, 0, S, M, 3, pb, dst, dsc)
+    ref = [np.zeros((L, M, pb), np.uint8) for _ in range(n)]
+    rsc = [np.zeros((L, M), np.uint16) for _ in range(n)]
+    keep = [i for i in range(len(g)) if 0 <= g[i] < M * n and 0 <= src[i] < S]
+    O.reshard([pool], ref, L, n, [src[i] for i in keep], [g[i] for i in keep], 0, src_scales=ssc, dst_scales=rsc)
+    for d in range(n):
+        assert np.array_equal(dst[d], ref[d]) and np.array_equal(dsc[d], rsc[d])
+    assert dsc[1][0, 0] == ssc[0][0, 0] and dsc[1][1, 3] == ssc[0][1, 2]  # values 1 and 7 -> slots 0 and 3
+
+
 # --------------------------------------------------------------------------- page map
 
 
