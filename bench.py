@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", default="gqa_bf16_16x4k-32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--pack-cap-mib", type=int, default=64,
+                    help="staging buffer of the path-by-path (bounded pack/unpack) transfer timed after the "
+                         "steps; 0 skips it")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this many MiB (torch bitwise_not, int32) before timing: a "
                          "known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -158,6 +161,47 @@ class Step:
                                 dst_pools=self.pools, src_page_ids=self.src_ids, dst_global_pages=self.dst_ids,
                                 first_uncached=self.first_uncached, src_scales=self.src_scales,
                                 dst_scales=self.scales)
+
+    def prepare_paths(self, cap_pages: int):
+        """Entry lists of every destination's path (device) and their sizes (read back once), and a
+        staging buffer of cap_pages pages, for the path-by-path transfer."""
+        import torch
+        w, K = self.w, self.K
+        self.geo = dict(num_sources=w.num_sources, num_layers=w.num_layers, dcp_size=w.dcp_size,
+                        page_bytes=w.page_bytes, src_pages=self.src_pages, dst_pages=w.pool_pages)
+        self.cap = cap_pages
+        self.pos, self.cnt = [], []
+        for d in range(w.dcp_size):
+            pos = torch.empty(max(1, self.num_pages), dtype=torch.int32, device=self.dev)
+            cnt = torch.empty(1, dtype=torch.int64, device=self.dev)
+            K.kv_path_entries(dest=d, src_page_ids=self.src_ids, dst_global_pages=self.dst_ids, out_positions=pos,
+                              out_count=cnt, first_uncached=self.first_uncached, **self.geo)
+            self.pos.append(pos)
+            self.cnt.append(cnt)
+        self.counts = [int(c.item()) for c in self.cnt]
+        self.stg = torch.empty((cap_pages, w.page_bytes), dtype=torch.uint8, device=self.dev)
+        self.stg_sc = torch.empty(cap_pages, dtype=torch.int16, device=self.dev) if w.has_scales else None
+        self.windows = 0
+        for d in range(w.dcp_size):
+            for r in range(w.num_sources):
+                a, b = K.cp_layersplit_layer_range(w.num_layers, w.num_sources, r)
+                self.windows += -(-self.counts[d] * (b - a) // cap_pages)
+
+    def path_transfer(self):
+        """The reshard done path by path through the staging buffer (pack, then unpack, per window)."""
+        w, K = self.w, self.K
+        for d in range(w.dcp_size):
+            for r in range(w.num_sources):
+                a, b = K.cp_layersplit_layer_range(w.num_layers, w.num_sources, r)
+                for u0 in range(0, self.counts[d] * (b - a), self.cap):
+                    K.kv_pack_pages(source=r, src_pool=self.src[r], src_page_ids=self.src_ids, positions=self.pos[d],
+                                    count=self.cnt[d], unit_begin=u0, cap_units=self.cap, staging=self.stg,
+                                    src_scales=None if self.src_scales is None else self.src_scales[r],
+                                    staging_scales=self.stg_sc, **self.geo)
+                    K.kv_unpack_pages(source=r, dest=d, dst_pool=self.pools[d], dst_global_pages=self.dst_ids,
+                                      positions=self.pos[d], count=self.cnt[d], unit_begin=u0, cap_units=self.cap,
+                                      staging=self.stg, dst_scales=None if self.scales is None else self.scales[d],
+                                      staging_scales=self.stg_sc, **self.geo)
 
     def partial(self):
         if not self.has_attention:
@@ -429,6 +473,25 @@ def main():
                       "reshard_us": round(t_rs.mean() * 1e6, 2),
                       "plain_copy_GBps": round(copy_gbps, 1),
                       "reshard_frac_of_plain_copy": round(rs_gbps / copy_gbps, 4)})
+        if a.pack_cap_mib > 0 and st.num_pages > st.first_uncached:
+            # the same pages path by path through a fixed staging buffer: every page is read and
+            # written twice (source -> staging -> pool)
+            cap = max(1, (a.pack_cap_mib << 20) // w.page_bytes)
+            st.prepare_paths(cap)
+            st.path_transfer()
+            ts = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                st.path_transfer()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e-3)
+            t_pk = float(np.median(ts))
+            pk_gbps = 2 * b_rs / t_pk / 1e9
+            parts.update({"pack_cap_pages": cap, "pack_windows": st.windows, "pack_unpack_us": round(t_pk * 1e6, 2),
+                          "pack_unpack_GBps": round(pk_gbps, 1), "pack_unpack_frac_hbm": round(pk_gbps / HBM_PEAK_GBPS, 4),
+                          "pack_unpack_time_vs_reshard": round(t_pk / t_rs.mean(), 3)})
     if st.has_attention:
         t_attn = t_pa.mean() + t_mg.mean()
         kv_gbps = b_kv / t_attn / 1e9
