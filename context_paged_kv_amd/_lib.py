@@ -41,6 +41,7 @@ DCPKV_ENOTSUP = -95
 KV_F32, KV_BF16, KV_FP8E4M3 = 0, 1, 2
 LAYOUT_SPLIT, LAYOUT_MLA = 0, 1
 Q_F32, Q_BF16 = 0, 1
+OWN_PAGE, OWN_TOKEN = 0, 1
 
 EXPORTED = (
     "dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
@@ -69,7 +70,7 @@ class dcp_attn_desc(C.Structure):
                 ("head_dim_qk", C.c_int32), ("head_dim_v", C.c_int32), ("page_size", C.c_int32),
                 ("dcp_size", C.c_int32), ("batch", C.c_int32), ("q_len", C.c_int32),
                 ("max_local_pages", C.c_int32), ("layer", C.c_int32), ("num_layers", C.c_int32),
-                ("pages_per_layer", C.c_int64), ("softmax_scale", C.c_float), ("pad2_", C.c_float)]
+                ("pages_per_layer", C.c_int64), ("softmax_scale", C.c_float), ("token_interleave", C.c_int32)]
 
 
 _P = C.c_void_p
@@ -88,7 +89,7 @@ _lib.dcp_pagemap_num_free.argtypes = [_P]
 _lib.dcp_pagemap_num_free.restype = C.c_int64
 _lib.dcp_pagemap_alloc.argtypes = [_P, C.c_int64, _I64P, C.c_int64]
 _lib.dcp_pagemap_release.argtypes = [_P, _I64P, C.c_int64]
-_lib.dcp_build_block_tables.argtypes = [C.c_int32, C.c_int32, _I64P, _I64P, C.c_int32, _I32P, _I32P]
+_lib.dcp_build_block_tables.argtypes = [C.c_int32, C.c_int32, _I64P, _I64P, C.c_int32, C.c_int32, _I32P, _I32P]
 _lib.kv_reshard_pages.argtypes = [C.POINTER(kv_reshard_desc), C.POINTER(_P), C.POINTER(_P),
                                   C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, C.c_int64, _P, _P]
 _lib.kv_path_entries.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, C.c_int64, C.c_int64, _P, _P, _P]
@@ -226,7 +227,8 @@ class PageMap:
             pass
 
 
-def dcp_build_block_tables(dcp_size: int, pages_per_request: Sequence[Sequence[int]], max_local_pages: int):
+def dcp_build_block_tables(dcp_size: int, pages_per_request: Sequence[Sequence[int]], max_local_pages: int,
+                           token_interleave: int = 0):
     """Returns (tables int32 [N][B][max_local_pages], counts int32 [N][B])."""
     batch = len(pages_per_request)
     offs = np.zeros(batch + 1, dtype=np.int64)
@@ -237,7 +239,7 @@ def dcp_build_block_tables(dcp_size: int, pages_per_request: Sequence[Sequence[i
     tables = np.empty((dcp_size, batch, max_local_pages), dtype=np.int32)
     counts = np.empty((dcp_size, batch), dtype=np.int32)
     _check(_lib.dcp_build_block_tables(dcp_size, batch, _ptr64(flat) if flat.size else None, _ptr64(offs),
-                                       max_local_pages, _ptr32(tables), _ptr32(counts)))
+                                       max_local_pages, token_interleave, _ptr32(tables), _ptr32(counts)))
     return tables, counts
 
 
@@ -294,10 +296,10 @@ def kv_unpack_pages(*, num_sources: int, num_layers: int, dcp_size: int, page_by
 def make_attn_desc(*, kv_dtype: int, kv_layout: int, q_dtype: int, num_q_heads: int, num_kv_heads: int,
                    head_dim_qk: int, head_dim_v: int, page_size: int, dcp_size: int, batch: int,
                    q_len: int, max_local_pages: int, layer: int, num_layers: int, pages_per_layer: int,
-                   softmax_scale: float) -> dcp_attn_desc:
+                   softmax_scale: float, token_interleave: int = 0) -> dcp_attn_desc:
     return dcp_attn_desc(kv_dtype, kv_layout, q_dtype, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
                          page_size, dcp_size, batch, q_len, max_local_pages, layer, num_layers, pages_per_layer,
-                         softmax_scale, 0.0)
+                         softmax_scale, token_interleave)
 
 
 def dcp_decode_partial_workspace(desc: dcp_attn_desc, total_tokens: int) -> int:

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
   const int C = p.chunk_pages;
   auto pair_pages = [&](int i) {
     const int d = p.shard_begin + i / p.batch, b = i % p.batch;
-    return local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local);
+    return local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local, p.tok_il);
   };
   // chunk totals first: one chunk per pair when the split would not fit the workspace or
   // the launched grid
@@ -189,15 +189,13 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
           p.pools[d] + ((int64_t)p.layer * p.pages_per_layer + slot) * p.page_bytes;
       float pscale = 1.f;
       if (KIND == 2) pscale = bf16_to_float(p.scales[d][(int64_t)p.layer * p.pages_per_layer + slot]);
-      const int64_t seq_page = (int64_t)jj * p.n + d;
       for (int off = 0; off < p.page_size; off += TT) {
-        const int64_t pos0 = seq_page * p.page_size + off;
         const int ntok = min(TT, p.page_size - off);
         __syncthreads();  // previous tile consumed
         for (int e = tid; e < TT * DQ; e += kGenThreads) {
           const int j = e / DQ, k = e - j * DQ;
           float kv = 0.f;
-          if (j < ntok && pos0 + j < T) {
+          if (j < ntok && token_position(jj, off + j, p.page_size, p.n, d, p.tok_il) < T) {
             const int tok = off + j;
             if (KIND == 2) {
               kv = e4m3fn_to_float(page[(int64_t)tok * 576 + k]) * pscale;
@@ -215,7 +213,7 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
           for (int e = tid; e < TT * DV; e += kGenThreads) {
             const int j = e / DV, c = e - j * DV;
             float vv = 0.f;
-            if (j < ntok && pos0 + j < T) {
+            if (j < ntok && token_position(jj, off + j, p.page_size, p.n, d, p.tok_il) < T) {
               const int tok = off + j;
               const int64_t vi = (((int64_t)p.hkv + hk) * p.page_size + tok) * DV + c;
               if (KIND == 1)
@@ -234,7 +232,7 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
           if (r < RB) {
             const int rr = r0 + r;
             const int t = rr / p.group;
-            const int64_t pos = pos0 + j;
+            const int64_t pos = token_position(jj, off + j, p.page_size, p.n, d, p.tok_il);
             if (r < nrows && j < ntok && pos < T && pos <= (int64_t)T - p.q_len + t) {
               float dot = 0.f;
               const float* qr = sQ + r * (DQ + 1);
@@ -383,6 +381,8 @@ static int validate(const dcp_attn_desc& D) {
       D.q_len < 1 || D.max_local_pages < 1 || D.layer < 0 || D.layer >= D.num_layers ||
       D.pages_per_layer < 1 || !(D.softmax_scale == D.softmax_scale))
     return set_error(DCPKV_EINVAL, "attn: bad geometry");
+  if (D.token_interleave != DCPKV_OWN_PAGE && D.token_interleave != DCPKV_OWN_TOKEN)
+    return set_error(DCPKV_EINVAL, "attn: token_interleave must be %d or %d", DCPKV_OWN_PAGE, DCPKV_OWN_TOKEN);
   if ((int64_t)D.q_len * D.num_q_heads > (1 << 20) || (int64_t)D.batch * D.dcp_size > (1 << 24))
     return set_error(DCPKV_EINVAL, "attn: batch too large");
   return DCPKV_OK;
@@ -411,7 +411,9 @@ static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus,
   g.hb_count = D.num_kv_heads * g.rb_per_head;
   g.rows = D.q_len * D.num_q_heads;
   const int64_t tot = std::max<int64_t>(total_tokens, 0);
-  const int64_t est_pages = tot / D.page_size + D.batch;  // >= sum of ceil(T_b / page)
+  // >= the local pages over all shards: sum of ceil(T_b / page) (page ownership), at most
+  // T_b / page + N per request (token ownership: every shard may end on a partial page)
+  const int64_t est_pages = tot / D.page_size + (int64_t)D.batch * (D.token_interleave ? D.dcp_size : 1);
   const int64_t target_items = (int64_t)cus * kernel_items_per_cu(g.kind);
   int64_t c = (est_pages * g.hb_count + target_items - 1) / std::max<int64_t>(target_items, 1);
   c = std::max<int64_t>(c, kernel_min_chunk_pages(g.kind, D));
@@ -506,6 +508,7 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   p.rb_rows = g.rb_rows;
   p.rb_per_head = g.rb_per_head;
   p.scale = D.softmax_scale;
+  p.tok_il = D.token_interleave;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int cus = device_cus();
 
@@ -513,7 +516,8 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   // max_chunks chunks and the planner never produces more (it falls back to one
   // chunk per pair, which pairs <= max_chunks always allows)
   const int64_t pairs = (int64_t)shard_count * D.batch;
-  const int64_t est_pages = std::max<int64_t>(total_tokens, 0) / D.page_size + D.batch;
+  const int64_t est_pages = std::max<int64_t>(total_tokens, 0) / D.page_size +
+                            (int64_t)D.batch * (D.token_interleave ? D.dcp_size : 1);
   p.max_chunks = pairs + est_pages / g.chunk_pages + 1;
   const int64_t item_bound = p.max_chunks * g.hb_count;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);

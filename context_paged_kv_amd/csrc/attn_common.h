@@ -64,13 +64,38 @@ struct AttnParams {
   int32_t rb_rows;      // rows per head block
   int32_t rb_per_head;  // head blocks per KV head
   float scale;
+  int32_t tok_il;       // 1: token t on shard t mod N; 0: page ownership
 };
 
+// Tokens of (request with seq_len tokens) held by shard d, and its local pages.
+// Page ownership ([2DR] section 5.1): sequence page i on shard i mod N.  Token
+// ownership ([SGL]): token t on shard t mod N, local token t div N.
 __device__ __forceinline__ int32_t local_pages_of(int32_t seq_len, int32_t page_size, int32_t n,
-                                                  int32_t d, int32_t max_local) {
-  const int32_t pages = (seq_len + page_size - 1) / page_size;
-  const int32_t nl = pages > d ? (pages - 1 - d) / n + 1 : 0;
+                                                  int32_t d, int32_t max_local, int32_t tok_il) {
+  int32_t nl;
+  if (tok_il) {
+    const int32_t toks = seq_len > d ? (seq_len - 1 - d) / n + 1 : 0;
+    nl = (toks + page_size - 1) / page_size;
+  } else {
+    const int32_t pages = (seq_len + page_size - 1) / page_size;
+    nl = pages > d ? (pages - 1 - d) / n + 1 : 0;
+  }
   return nl < max_local ? nl : max_local;
+}
+
+// Position of token x of shard d's local page j.
+__device__ __forceinline__ int64_t token_position(int32_t j, int32_t x, int32_t page_size, int32_t n, int32_t d,
+                                                  int32_t tok_il) {
+  return tok_il ? ((int64_t)j * page_size + x) * n + d : ((int64_t)j * n + d) * page_size + x;
+}
+
+// Largest x whose token_position(j, x) <= pos (pos >= -1); tokens of local page j
+// past it are later than pos.  Page ownership: pos - first position of the page;
+// token ownership: the local index of the last position <= pos, minus j * page_size.
+__device__ __forceinline__ int64_t local_limit(int64_t pos, int32_t j, int32_t page_size, int32_t n, int32_t d,
+                                               int32_t tok_il) {
+  if (tok_il) return (pos >= d ? (pos - d) / n : -1) - (int64_t)j * page_size;
+  return pos - ((int64_t)j * n + d) * page_size;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -140,9 +140,10 @@ __global__ __launch_bounds__(256) void gqa_bf16_kernel(AttnParams p) {
   }
 
   while (jj < j_end) {
-    const int64_t pos0 = ((int64_t)jj * p.n + d) * kGqaPage;
-    const int64_t rem = (int64_t)T - pos0;
-    const int valid = rem < kGqaPage ? (int)rem : kGqaPage;  // tokens of this page before T
+    // tokens of this page before T, and the last one this lane's row sees
+    const int64_t vlast = local_limit((int64_t)T - 1, jj, kGqaPage, p.n, d, p.tok_il);
+    const int valid = vlast + 1 < kGqaPage ? (int)(vlast + 1) : kGqaPage;
+    const int64_t thr = local_limit(lim, jj, kGqaPage, p.n, d, p.tok_il);
     // ---- stage the current page into LDS
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -200,8 +201,7 @@ __global__ __launch_bounds__(256) void gqa_bf16_kernel(AttnParams p) {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t pos = pos0 + tok_of(tt, 4 * g + i);
-        const float v = pos <= lim ? s[tt][i] * sl2 : kNegInf;
+        const float v = tok_of(tt, 4 * g + i) <= thr ? s[tt][i] * sl2 : kNegInf;
         s[tt][i] = v;
         mx = fmaxf(mx, v);
       }

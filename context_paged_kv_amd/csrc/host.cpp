@@ -31,7 +31,7 @@ using namespace dcpkv;
 
 extern "C" const char* dcpkv_last_error(void) { return g_err; }
 
-extern "C" int dcpkv_abi_version(void) { return 2; }
+extern "C" int dcpkv_abi_version(void) { return 3; }
 
 // [2DR] section 4.1: start_r = r*floor(L/N) + min(r, L mod N), end_r = start_{r+1}.
 extern "C" int cp_layersplit_layer_range(int32_t num_layers, int32_t num_sources, int32_t r,
@@ -167,9 +167,10 @@ extern "C" int dcp_pagemap_release(dcp_pagemap* pm, const int64_t* global_pages,
 
 extern "C" int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int64_t* global_pages,
                                       const int64_t* page_offsets, int32_t max_local_pages,
-                                      int32_t* out_tables, int32_t* out_counts) {
+                                      int32_t token_interleave, int32_t* out_tables, int32_t* out_counts) {
   if (dcp_size < 1 || dcp_size > kMaxShards || batch < 0 || max_local_pages < 0 || !page_offsets ||
-      !out_tables || (!global_pages && batch > 0 && page_offsets[batch] > 0))
+      !out_tables || (!global_pages && batch > 0 && page_offsets[batch] > 0) ||
+      (token_interleave != DCPKV_OWN_PAGE && token_interleave != DCPKV_OWN_TOKEN))
     return set_error(DCPKV_EINVAL, "block_tables: bad arguments");
   const size_t total = (size_t)dcp_size * batch * max_local_pages;
   for (size_t i = 0; i < total; ++i) out_tables[i] = -1;
@@ -191,8 +192,19 @@ extern "C" int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int
       if (cnt[d] >= max_local_pages)
         return set_error(DCPKV_EINVAL, "block_tables: request %d needs more than %d local pages",
                          b, max_local_pages);
-      out_tables[((size_t)d * batch + b) * max_local_pages + cnt[d]] = (int32_t)slot;
+      if (!token_interleave) out_tables[((size_t)d * batch + b) * max_local_pages + cnt[d]] = (int32_t)slot;
       ++cnt[d];
+    }
+    if (token_interleave) {  // local page j of every shard sits at virtual page j's slot
+      const int64_t nv = (e - a + dcp_size - 1) / dcp_size;
+      if (nv > max_local_pages)
+        return set_error(DCPKV_EINVAL, "block_tables: request %d needs more than %d local pages", b,
+                         max_local_pages);
+      for (int32_t d = 0; d < dcp_size; ++d) {
+        for (int64_t j = 0; j < nv; ++j)
+          out_tables[((size_t)d * batch + b) * max_local_pages + j] = (int32_t)(global_pages[a + j * dcp_size] / dcp_size);
+        cnt[d] = (int32_t)nv;
+      }
     }
     if (out_counts)
       for (int32_t d = 0; d < dcp_size; ++d) out_counts[(size_t)d * batch + b] = cnt[d];

@@ -310,6 +310,11 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   // and the next page's copies.  Entries outside [0, pages_per_layer) are skipped.
   const uint32_t slots = (uint32_t)min<int64_t>(p.pages_per_layer, INT32_MAX);
   auto ok = [&](int32_t sl) { return (uint32_t)sl < slots; };
+  // largest token x of local page j at a position <= pos (local_limit in 32 bits: positions are
+  // below T <= INT32_MAX)
+  auto llim = [&](int pos, int j) {
+    return p.tok_il ? (pos >= d ? (pos - d) / p.n : -1) - j * kMlaPage : pos - (j * p.n + d) * kMlaPage;
+  };
   int wbase = j_begin;
   int32_t win0 = j_begin + lane < j_end ? bt[j_begin + lane] : -1;
   int32_t win1 = j_begin + 64 + lane < j_end ? bt[j_begin + 64 + lane] : -1;
@@ -364,9 +369,10 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
       for (int i = 0; i < kLoadIters; ++i) st(i);
     }
     if (ok(slot_cur)) {
-      const int pos0 = (jj * p.n + d) * kMlaPage;  // local page jj holds positions below T
-      const int valid = min(T - pos0, kMlaPage);
-      const bool full = pos0 <= T - p.q_len - (kMlaPage - 1);  // no row masks a token of this page
+      // tokens of local page jj before T; no row masks a token of the page when even the
+      // first query position sees all 64
+      const int valid = min(llim(T - 1, jj) + 1, kMlaPage);
+      const bool full = llim(T - p.q_len, jj) >= kMlaPage - 1;
       const float ps = fmaxf(bf16_to_float(sc_cur), 1e-30f);
       uint8_t* cur = s_raw[buf];
       if (valid < kMlaPage) {  // tail of the last page: no code past T reaches a product
@@ -426,11 +432,12 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
       // ---- this half's numerators (lane: row 16 rt + c, tokens 32 th + mla_vtok(g, [0, 8)))
       const float f = sl2 * ps;
       if (!full) {
+        const int thr = llim(lim, jj);  // this row's last visible token
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (32 * th + mla_tok(tt, 4 * g + i) > lim - pos0) s[tt][i] = kNegInf;
+            if (32 * th + mla_tok(tt, 4 * g + i) > thr) s[tt][i] = kNegInf;
       }
       float v_max = kNegInf;
 #pragma unroll

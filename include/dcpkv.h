@@ -57,6 +57,9 @@ enum {
 enum { DCPKV_KV_F32 = 0, DCPKV_KV_BF16 = 1, DCPKV_KV_FP8E4M3 = 2 };
 enum { DCPKV_LAYOUT_SPLIT = 0, DCPKV_LAYOUT_MLA = 1 };
 enum { DCPKV_Q_F32 = 0, DCPKV_Q_BF16 = 1 };
+/* Which shard holds a token: its page's owner (page p on rank p mod N, [2DR]
+ * section 5.1) or the token's own residue (token t on rank t mod N, [SGL]). */
+enum { DCPKV_OWN_PAGE = 0, DCPKV_OWN_TOKEN = 1 };
 
 /* Thread-local text describing the last non-OK status returned on this thread. */
 DCPKV_API const char* dcpkv_last_error(void);
@@ -120,15 +123,19 @@ DCPKV_API int dcp_pagemap_release(dcp_pagemap* pm, const int64_t* global_pages, 
 /* Per-shard block tables for a batch ([2DR] section 5.1).  Request b's
  * global pages are global_pages[page_offsets[b] .. page_offsets[b+1]) (host).
  * out_tables (host, int32 [N][batch][max_local_pages]) receives, for shard d
- * and request b, the local slots of the pages d owns in sequence order; unused
- * entries are -1.  out_counts (host, int32 [N][batch], nullable) receives the
- * number of pages per (d, b).  Requires the allocator's canonical placement:
- * sequence page i must be owned by rank i mod N (EINVAL otherwise), which is
- * what the attention kernels assume when they turn a local page index j of
- * shard d back into sequence page j*N + d.  EINVAL if a count exceeds
- * max_local_pages. */
+ * and request b, the local slots of its local pages in order; unused entries
+ * are -1.  out_counts (host, int32 [N][batch], nullable) receives the number
+ * of entries per (d, b).  Requires the allocator's canonical placement:
+ * sequence page i must be owned by rank i mod N (EINVAL otherwise), so that
+ * virtual page j of the request is slot v_j = g_{jN} div N on every rank.
+ *   token_interleave = DCPKV_OWN_PAGE: shard d's local page j is sequence page
+ *     j*N + d (the pages d owns, in sequence order);
+ *   token_interleave = DCPKV_OWN_TOKEN ([SGL]: token t on rank t mod N): local
+ *     page j of every shard holds that shard's tokens of virtual page j, so every
+ *     shard lists v_0 .. v_{ceil(P/N)-1}.
+ * EINVAL if a count exceeds max_local_pages or token_interleave is neither. */
 DCPKV_API int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int64_t* global_pages,
-                           const int64_t* page_offsets, int32_t max_local_pages,
+                           const int64_t* page_offsets, int32_t max_local_pages, int32_t token_interleave,
                            int32_t* out_tables, int32_t* out_counts);
 
 /* ------------------------------------------------------------------------ *
@@ -252,7 +259,11 @@ typedef struct {
   int32_t num_layers;      /* L: layers in each pool */
   int64_t pages_per_layer; /* M: local slots per layer in each pool */
   float softmax_scale;     /* scores are softmax_scale * q . k */
-  float pad2_;
+  int32_t token_interleave; /* DCPKV_OWN_PAGE (0): page p of a sequence lives on shard
+                               p mod N ([2DR] section 5.1).  DCPKV_OWN_TOKEN (1): token t
+                               lives on shard t mod N, local token t div N ([SGL]: rank i
+                               holds tokens i, i+N, i+2N, ...).  The block tables are the
+                               same for both: entry j of (d, b) is the slot of local page j. */
 } dcp_attn_desc;
 
 /* Workspace bytes dcp_decode_partial needs for this batch.  total_tokens is
@@ -264,7 +275,8 @@ DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t
  * query t < q_len and head h:
  *     pos_t = T_b - q_len + t  (T_b counts the q_len draft tokens, whose KV
  *                               is already in the pools)
- *     J     = { j <= pos_t : the page of token j is owned by shard d }
+ *     J     = { j <= pos_t : token j is owned by shard d }  (through its page, or
+ *                               itself under DCPKV_OWN_TOKEN)
  *     s_j   = softmax_scale * q[b][t][h] . k_j   (k, v of KV head h / (Hq/Hkv))
  *     LSE_d = log sum_{j in J} exp(s_j)
  *     O_d   = sum_{j in J} exp(s_j - LSE_d) v_j
@@ -277,7 +289,9 @@ DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t
  * device pointers to DCP pools; kv_scales: host array [N] of device pointers
  * to bf16 [L][M] page scales (MLA), else NULL.  block_tables: device int32
  * [N][B][max_local_pages] as built by dcp_build_block_tables: entry j of
- * (d, b) is the local slot of sequence page j*N + d.  seq_lens: device int32
+ * (d, b) is the slot of shard d's local page j, which holds sequence page
+ * j*N + d (DCPKV_OWN_PAGE) or the tokens (j*page_size + x)*N + d, x < page_size
+ * (DCPKV_OWN_TOKEN).  seq_lens: device int32
  * [B], each T_b >= q_len.  Out: partial_out fp32 [N][B][q_len][Hq][head_dim_v],
  * partial_lse fp32 [N][B][q_len][Hq] (natural log); only the requested shards'
  * slices are written.  workspace: device, >= dcp_decode_partial_workspace()

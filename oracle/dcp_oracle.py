@@ -45,6 +45,11 @@ design notes as well):
       a row) into a staging buffer of a fixed number of pages, window after
       window; the pages give the idea (a fixed pre-registered buffer reused in
       chunks, the same bytes moved), not a layout, so the order is ours.
+  R18 Token ownership ([SGL]: rank i holds tokens i, i+N, ...): token t is the
+      (t div N)-th token of shard t mod N; shard d's local page j holds its
+      tokens j*page_size .. j*page_size + page_size - 1 and sits at the slot of
+      the request's j-th virtual page (the allocator's unit of N pages), the
+      same slot page ownership gives it.
 
 Parity pins live in tests/test_oracle_pins.py; every function here has one.
 """
@@ -170,13 +175,38 @@ class PageMap:
             self.free.append(v)
 
 
-def block_tables(global_pages: Sequence[Sequence[int]], n: int) -> List[List[List[int]]]:
-    """Per shard d and request b: the local slots of the pages d owns, in sequence order."""
+def block_tables(global_pages: Sequence[Sequence[int]], n: int, own: str = "page") -> List[List[List[int]]]:
+    """Per shard d and request b: the slots of d's local pages, in order.
+
+    own == "page": the pages d owns, in sequence order ([2DR] section 5.1).
+    own == "token" (reading R18): local page j of every shard holds that shard's
+    tokens of the request's j-th virtual page, whose slot is g_{jN} div N.
+    """
     out = [[[] for _ in global_pages] for _ in range(n)]
     for b, pages in enumerate(global_pages):
+        if own == "token":
+            for j in range(0, len(pages), n):
+                for d in range(n):
+                    out[d][b].append(dcp_local_slot(int(pages[j]), n))
+            continue
         for g in pages:
             out[dcp_owner(int(g), n)][b].append(dcp_local_slot(int(g), n))
     return out
+
+
+def token_owner(t: int, n: int) -> int:
+    """[SGL]: rank i holds tokens i, i+N, i+2N, ... of the sequence."""
+    return t % n
+
+
+def token_place(t: int, n: int, page_size: int, global_pages: Sequence[int]) -> Tuple[int, int, int]:
+    """(shard, slot, row) of token t under token ownership (reading R18): shard t mod N holds it
+    as its (t div N)-th token, row (t div N) mod page_size of its local page (t div N) div page_size,
+    which sits at the slot of the request's virtual page of that index."""
+    d = token_owner(t, n)
+    u = t // n
+    j = u // page_size
+    return d, dcp_local_slot(int(global_pages[j * n]), n), u % page_size
 
 
 # --------------------------------------------------------------------------
@@ -410,21 +440,27 @@ def request_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_len: int,
     return out, lse
 
 
-def shard_token_mask(global_pages: Sequence[int], page_size: int, seq_len: int, n: int, d: int) -> np.ndarray:
-    """Tokens held by shard d: those whose page's global id is owned by d ([2DR] 5.1)."""
+def shard_token_mask(global_pages: Sequence[int], page_size: int, seq_len: int, n: int, d: int,
+                     own: str = "page") -> np.ndarray:
+    """Tokens held by shard d: those whose page's global id is owned by d ([2DR] 5.1), or, with
+    own == "token", those with t mod N == d ([SGL])."""
     mask = np.zeros(seq_len, dtype=bool)
+    if own == "token":
+        for t in range(seq_len):
+            mask[t] = token_owner(t, n) == d
+        return mask
     for i, g in enumerate(global_pages):
         if dcp_owner(int(g), n) == d:
             mask[i * page_size:min(seq_len, (i + 1) * page_size)] = True
     return mask
 
 
-def request_partials(q, k, v, seq_len, scale, global_pages, page_size, n, heads=None):
+def request_partials(q, k, v, seq_len, scale, global_pages, page_size, n, heads=None, own="page"):
     """Per-shard partials of one request: O [N][q_len][Hq][Dv], LSE [N][q_len][Hq]."""
     outs, lses = [], []
     for d in range(n):
-        o, l = request_attention(q, k, v, seq_len, scale, shard_token_mask(global_pages, page_size, seq_len, n, d),
-                                 heads)
+        o, l = request_attention(q, k, v, seq_len, scale,
+                                 shard_token_mask(global_pages, page_size, seq_len, n, d, own), heads)
         outs.append(o)
         lses.append(l)
     return np.stack(outs), np.stack(lses)
@@ -475,4 +511,33 @@ def logical_kv_mla(page_and_scale_of, global_pages, n, page_size, seq_len, dv=51
         page, sbits = page_and_scale_of(dcp_owner(int(g), n), dcp_local_slot(int(g), n))
         lat.append(decode_mla_page(page, sbits, page_size))
     x = np.concatenate(lat, axis=0)[:seq_len]
+    return x[None], x[None, :, :dv]
+
+
+def logical_kv_split_tokens(pool_pages_of, global_pages, n, dtype, num_kv_heads, page_size, head_dim, seq_len):
+    """Logical (K, V) [Hkv][T][D] of one request from split-layout pools under token ownership."""
+    cache = {}
+    k = np.zeros((num_kv_heads, seq_len, head_dim))
+    v = np.zeros((num_kv_heads, seq_len, head_dim))
+    for t in range(seq_len):
+        d, slot, row = token_place(t, n, page_size, global_pages)
+        if (d, slot) not in cache:
+            cache[(d, slot)] = decode_split_page(pool_pages_of(d, slot), dtype, num_kv_heads, page_size, head_dim)
+        pk, pv = cache[(d, slot)]
+        k[:, t] = pk[:, row]
+        v[:, t] = pv[:, row]
+    return k, v
+
+
+def logical_kv_mla_tokens(page_and_scale_of, global_pages, n, page_size, seq_len, dv=512):
+    """Logical (K, V) [1][T][576], [1][T][512] from fp8 latent pools under token ownership; each
+    token is dequantised with the scale of the page that holds it."""
+    cache = {}
+    x = np.zeros((seq_len, 576))
+    for t in range(seq_len):
+        d, slot, row = token_place(t, n, page_size, global_pages)
+        if (d, slot) not in cache:
+            page, sbits = page_and_scale_of(d, slot)
+            cache[(d, slot)] = decode_mla_page(page, sbits, page_size)
+        x[t] = cache[(d, slot)][row]
     return x[None], x[None, :, :dv]

@@ -47,6 +47,7 @@ class DecodeCase:
     bt_dev: torch.Tensor
     sl_dev: torch.Tensor
     layer: int = 0
+    own: int = 0                       # K.OWN_PAGE or K.OWN_TOKEN
 
     @property
     def total_tokens(self) -> int:
@@ -83,18 +84,18 @@ def alloc_pools(w: Workload, device, fill: str = "random", tag: str = "pool"):
     return pools, scales
 
 
-def make_decode_case(w: Workload, device="cuda", seq_lens=None, pools=None, scales=None) -> DecodeCase:
+def make_decode_case(w: Workload, device="cuda", seq_lens=None, pools=None, scales=None, own: int = 0) -> DecodeCase:
     sl = gen.draw_seq_lens(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int64)
     assert len(sl) == w.num_requests
     pages = page_map_pages(w, sl)
     max_local = max(1, max(-(-len(p) // w.dcp_size) for p in pages))
-    tables, counts = K.dcp_build_block_tables(w.dcp_size, pages, max_local)
+    tables, counts = K.dcp_build_block_tables(w.dcp_size, pages, max_local, token_interleave=own)
     if pools is None:
         pools, scales = alloc_pools(w, device)
     q = gen.draw_q(w, device)
     return DecodeCase(w=w, seq_lens=sl, pages=pages, max_local=max_local, tables=tables, pools=pools,
                       scales=scales, q=q, bt_dev=torch.from_numpy(tables).to(device),
-                      sl_dev=torch.from_numpy(sl.astype(np.int32)).to(device), layer=w.attn_layer)
+                      sl_dev=torch.from_numpy(sl.astype(np.int32)).to(device), layer=w.attn_layer, own=own)
 
 
 def attn_desc(case: DecodeCase, layer: Optional[int] = None):
@@ -105,7 +106,7 @@ def attn_desc(case: DecodeCase, layer: Optional[int] = None):
         num_kv_heads=w.num_kv_heads, head_dim_qk=w.head_dim_qk, head_dim_v=w.head_dim_v,
         page_size=w.page_size, dcp_size=w.dcp_size, batch=w.num_requests, q_len=w.q_len,
         max_local_pages=case.max_local, layer=case.layer if layer is None else layer, num_layers=w.num_layers,
-        pages_per_layer=w.pool_pages, softmax_scale=w.softmax_scale)
+        pages_per_layer=w.pool_pages, softmax_scale=w.softmax_scale, token_interleave=case.own)
 
 
 @dataclass
@@ -180,6 +181,28 @@ def oracle_logical_kv(w: Workload, page_bytes: np.ndarray, page_scales, seq_len:
     return np.concatenate(ks, axis=1)[:, :seq_len], np.concatenate(vs, axis=1)[:, :seq_len]
 
 
+def gather_token_layout_kv(case: DecodeCase, b: int, layer: int):
+    """Logical K, V of request b under token ownership: host copies of every shard's pages at the
+    request's virtual slots, read back token by token by the oracle."""
+    w = case.w
+    n = w.dcp_size
+    pages = case.pages[b]
+    vslots = [O.dcp_local_slot(int(pages[j]), n) for j in range(0, len(pages), n)]
+    sl = torch.tensor(vslots, dtype=torch.int64, device=case.pools[0].device)
+    host = {}
+    for d in range(n):
+        pb = case.pools[d][layer].index_select(0, sl).cpu().numpy()
+        sc = (case.scales[d][layer].index_select(0, sl).cpu().numpy().astype(np.int64) & 0xFFFF
+              if case.scales is not None else None)
+        for i, s_ in enumerate(vslots):
+            host[(d, s_)] = (pb[i], None if sc is None else int(sc[i]))
+    T = int(case.seq_lens[b])
+    if w.layout == "mla":
+        return O.logical_kv_mla_tokens(lambda d, s_: host[(d, s_)], pages, n, w.page_size, T, w.head_dim_v)
+    return O.logical_kv_split_tokens(lambda d, s_: host[(d, s_)][0], pages, n, w.kv_dtype, w.num_kv_heads,
+                                     w.page_size, w.head_dim_qk, T)
+
+
 def q_host(case: DecodeCase, b: int) -> np.ndarray:
     return case.q[b].float().cpu().numpy().astype(np.float64)
 
@@ -188,13 +211,16 @@ def oracle_request(case: DecodeCase, b: int, heads=None, kv=None, layer=None):
     """(partials O [N][q_len][Hq][Dv], LSE [N][q_len][Hq]), (unsharded O, LSE) for request b."""
     w = case.w
     lay = case.layer if layer is None else layer
+    if kv is None and case.own:
+        kv = gather_token_layout_kv(case, b, lay)
     if kv is None:
         pb, ps = gather_request_pages(case.pools, case.scales, case.pages[b], w.dcp_size, lay)
         kv = oracle_logical_kv(w, pb, ps, int(case.seq_lens[b]))
     k, v = kv
     q = q_host(case, b)
     T = int(case.seq_lens[b])
-    po, pl = O.request_partials(q, k, v, T, w.softmax_scale, case.pages[b], w.page_size, w.dcp_size, heads)
+    po, pl = O.request_partials(q, k, v, T, w.softmax_scale, case.pages[b], w.page_size, w.dcp_size, heads,
+                                own="token" if case.own else "page")
     uo, ul = O.request_attention(q, k, v, T, w.softmax_scale, None, heads)
     return (po, pl), (uo, ul)
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTED)
-    assert K.dcpkv_abi_version() == 2
+    assert K.dcpkv_abi_version() == 3
 
 
 @pytest.mark.parametrize("L_,n", [(78, 8), (64, 4), (4, 4), (17, 5), (1, 1), (100, 7)])
@@ -99,14 +99,15 @@ def test_pagemap_errors():
         pm.alloc(0)
 
 
-def test_block_tables_match_oracle():
+@pytest.mark.parametrize("own", [0, 1])
+def test_block_tables_match_oracle(own):
     rng = np.random.default_rng(5)
     n, page, M = 4, 16, 200
     om = O.PageMap(n, page, M, rng.permutation(M))
     pages = [om.alloc(int(t)) for t in rng.integers(1, 600, size=9)]
     mx = max(-(-len(p) // n) for p in pages) + 2
-    tables, counts = K.dcp_build_block_tables(n, pages, mx)
-    want = O.block_tables(pages, n)
+    tables, counts = K.dcp_build_block_tables(n, pages, mx, token_interleave=own)
+    want = O.block_tables(pages, n, "token" if own else "page")
     for d in range(n):
         for b in range(len(pages)):
             c = counts[d, b]
@@ -116,7 +117,9 @@ def test_block_tables_match_oracle():
     with pytest.raises(L.DcpkvError):
         K.dcp_build_block_tables(4, [[1, 0, 2, 3]], 4)
     with pytest.raises(L.DcpkvError):  # too narrow
-        K.dcp_build_block_tables(n, pages, 1)
+        K.dcp_build_block_tables(n, pages, 1, token_interleave=own)
+    with pytest.raises(L.DcpkvError):  # unknown ownership mode
+        K.dcp_build_block_tables(n, pages, mx, token_interleave=2)
 
 
 def test_device_entry_points_reject_bad_arguments_on_host():

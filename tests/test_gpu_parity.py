@@ -263,6 +263,62 @@ def test_reshard_out_of_range_entries_are_skipped_and_counted():
         assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
 
 
+# --------------------------------------------------------------------------- token ownership
+
+
+_TOKEN_CASES = {
+    "tiny_fp32": dict(seq_segments=((1, 1000, 1000),)),
+    "gqa_bf16_16x4k-32k": dict(seq_segments=((5, 70, 3000),), pool_pages=256),
+    "mla_fp8_48x100k": dict(seq_segments=((3, 200, 5000),), pool_pages=512),
+    "mla_fp8_longmix_verify": dict(seq_segments=((2, 3000, 9000), (3, 2048, 2048)), pool_pages=512,
+                                   num_layers=2, attn_layer=1),
+}
+
+
+@pytest.mark.parametrize("name", list(_TOKEN_CASES))
+def test_decode_token_ownership(name):
+    """Token t on shard t mod N ([SGL]): every kernel (generic fp32, bf16 GQA, fp8 MLA with q_len 1
+    and causal q_len 4) against the oracle under token ownership."""
+    base = get_workload(name)
+    w = scaled(base, seed=base.seed + 300, **_TOKEN_CASES[name])
+    H.log(f"decode token ownership {name}")
+    case = H.make_decode_case(w, DEV, own=K.OWN_TOKEN)
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs)
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+def test_decode_token_ownership_generic_kernel(monkeypatch):
+    base = get_workload("gqa_bf16_16x4k-32k")
+    w = scaled(base, seed=base.seed + 301, seq_segments=((3, 70, 2000),), pool_pages=128, q_len=2)
+    case = H.make_decode_case(w, DEV, own=K.OWN_TOKEN)
+    monkeypatch.setenv("DCPKV_FORCE_GENERIC", "1")
+    outs = H.run_decode(case)
+    _sync()
+    monkeypatch.delenv("DCPKV_FORCE_GENERIC")
+    H.check_decode(case, outs)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "gqa_bf16_16x4k-32k", "mla_fp8_longmix_verify"])
+def test_decode_token_ownership_edge_lengths(name):
+    """T = q_len, just over one page, and fewer tokens than shards: shards holding no token give
+    (0, -inf); a shard whose page ownership would hold nothing now holds tokens."""
+    base = get_workload(name)
+    ql = base.q_len
+    lens = [max(ql, t) for t in (ql, base.page_size + 1, 2 * base.page_size - 1, 3)]
+    w = scaled(base, seed=base.seed + 302, seq_segments=tuple((1, t, t) for t in lens), pool_pages=64,
+               num_layers=1, attn_layer=0)
+    case = H.make_decode_case(w, DEV, own=K.OWN_TOKEN)
+    outs = H.run_decode(case)
+    _sync()
+    H.check_decode(case, outs)
+    for b, t in enumerate(lens):
+        for d in range(w.dcp_size):
+            empty = d >= t
+            assert bool(torch.isneginf(outs.partial_lse[d, b]).all()) == empty
+
+
 # --------------------------------------------------------------------------- bounded pack / unpack
 
 

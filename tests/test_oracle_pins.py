@@ -227,6 +227,97 @@ def test_reshard_moves_scales():
             assert (dst[gg % n][layer, gg // n] == src[0][layer, sp[i]]).all()
 
 
+# --------------------------------------------------------------------------- token ownership
+
+
+def test_token_ownership_fixture():
+    """[SGL]: rank i holds tokens i, i+N, i+2N, ... (tests/golden/token_ownership_10_over_4.txt)."""
+    for row in _rows("token_ownership_10_over_4.txt"):
+        d, toks = int(row[0]), [int(x) for x in row[1:]]
+        mask = O.shard_token_mask([0, 1, 2, 3], 16, 10, 4, d, own="token")
+        assert np.nonzero(mask)[0].tolist() == toks
+        assert all(O.token_owner(t, 4) == d for t in toks)
+
+
+@pytest.mark.parametrize("own", ["page", "token"])
+@pytest.mark.parametrize("n,T", [(1, 37), (2, 65), (4, 65), (4, 300), (3, 7), (8, 1000)])
+def test_shard_masks_partition_the_sequence(own, n, T):
+    pm = O.PageMap(n, 16, 64, list(range(64)))
+    g = pm.alloc(T)
+    masks = np.stack([O.shard_token_mask(g, 16, T, n, d, own) for d in range(n)])
+    assert (masks.sum(axis=0) == 1).all()
+
+
+def test_token_layout_hand_example():
+    """N = 2, page 4, T = 11 tokens on virtual pages 5 and 9 (global pages 10, 11, 18), worked by
+    hand: rank 0 holds tokens 0, 2, 4, 6 in rows 0-3 of slot 5 and 8, 10 in rows 0-1 of slot 9;
+    rank 1 holds 1, 3, 5, 7 in slot 5 and 9 in row 0 of slot 9.  Block tables: page ownership
+    gives rank 0 slots [5, 9] and rank 1 [5]; token ownership gives both [5, 9]."""
+    g = [10, 11, 18]
+    want = {0: (0, 5, 0), 2: (0, 5, 1), 4: (0, 5, 2), 6: (0, 5, 3), 8: (0, 9, 0), 10: (0, 9, 1),
+            1: (1, 5, 0), 3: (1, 5, 1), 5: (1, 5, 2), 7: (1, 5, 3), 9: (1, 9, 0)}
+    for t, place in want.items():
+        assert O.token_place(t, 2, 4, g) == place
+    assert O.block_tables([g], 2, "page") == [[[5, 9]], [[5]]]
+    assert O.block_tables([g], 2, "token") == [[[5, 9]], [[5, 9]]]
+
+
+@pytest.mark.parametrize("n,T,psz", [(2, 11, 4), (4, 65, 16), (4, 301, 16), (3, 50, 8), (8, 129, 4)])
+def test_token_layout_places_every_token_once_within_its_table(n, T, psz):
+    """Every token gets its own (shard, slot, row); each slot is in its shard's token block-table
+    row; rows fill local pages in order; a shard holds ceil((T - d) / N) tokens."""
+    M = 4 * (T // (psz * n) + 2)
+    pm = O.PageMap(n, psz, M, list(reversed(range(M))))
+    g = pm.alloc(T)
+    places = [O.token_place(t, n, psz, g) for t in range(T)]
+    assert len(set(places)) == T
+    tab = O.block_tables([g], n, "token")
+    for d in range(n):
+        mine = [p for p in places if p[0] == d]
+        assert len(mine) == max(0, -(-(T - d) // n))
+        for u, (_, slot, row) in enumerate(mine):
+            assert tab[d][0][u // psz] == slot and row == u % psz
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 8])
+def test_merge_equals_unsharded_token_ownership(n):
+    """Any partition of the tokens merges back exactly ([SGL]: exact across ranks); here the
+    token-residue partition."""
+    rng = np.random.default_rng(40 + n)
+    T, q_len, hq, hkv, d_ = 301, 2, 4, 2, 8
+    q, k, v = _rand_req(rng, T, q_len, hq, hkv, d_, d_)
+    pm = O.PageMap(n, 16, 64, list(range(64)))
+    g = pm.alloc(T)
+    po, pl = O.request_partials(q, k, v, T, 0.3, g, 16, n, own="token")
+    mo, ml = O.lse_merge(po, pl)
+    uo, ul = O.request_attention(q, k, v, T, 0.3, None)
+    assert np.allclose(mo, uo, rtol=1e-12, atol=1e-12) and np.allclose(ml, ul, rtol=1e-12, atol=1e-12)
+
+
+def test_logical_kv_gather_token_ownership():
+    """Pools written token by token under token ownership (tagged rows) read back into the logical
+    sequence, for the split and the latent layouts."""
+    n, psz, T, hkv, D = 4, 8, 70, 2, 4
+    M = 16
+    pm = O.PageMap(n, psz, M, list(range(M)))
+    g = pm.alloc(T)
+    pools = np.zeros((n, M, 2, hkv, psz, D), dtype=np.float32)
+    for t in range(T):
+        d, slot, row = O.token_place(t, n, psz, g)
+        pools[d, slot, 0, :, row, :] = t + 0.25
+        pools[d, slot, 1, :, row, :] = -t
+    k, v = O.logical_kv_split_tokens(lambda d, s: pools[d, s].reshape(-1).view(np.uint8), g, n, "f32", hkv, psz,
+                                     D, T)
+    assert (k[:, :, 0] == np.arange(T) + 0.25).all() and (v[:, :, 0] == -np.arange(T)).all()
+    lat = np.zeros((n, M, psz, 576), dtype=np.uint8)
+    for t in range(T):
+        d, slot, row = O.token_place(t, n, psz, g)
+        lat[d, slot, row, :] = 0x38  # e4m3 1.0
+        lat[d, slot, row, 0] = 0x38 + (t % 8)  # 1.0 .. 1.875
+    kk, vv = O.logical_kv_mla_tokens(lambda d, s: (lat[d, s].reshape(-1), 0x4000), g, n, psz, T)  # scale 2.0
+    assert np.allclose(kk[0, :, 0], 2.0 * (1.0 + (np.arange(T) % 8) / 8.0)) and vv.shape == (1, T, 512)
+
+
 # --------------------------------------------------------------------------- bounded pack / unpack
 
 
