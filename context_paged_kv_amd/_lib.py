@@ -47,7 +47,7 @@ EXPORTED = (
     "dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
     "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
     "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_path_entries", "kv_pack_pages",
-    "kv_unpack_pages",
+    "kv_unpack_pages", "kv_reshard_tokens",
     "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge",
 )
 
@@ -62,6 +62,12 @@ class kv_reshard_desc(C.Structure):
     _fields_ = [("num_sources", C.c_int32), ("num_layers", C.c_int32), ("dcp_size", C.c_int32),
                 ("dst_filter", C.c_int32), ("page_bytes", C.c_int64), ("src_pages", C.c_int64),
                 ("dst_pages", C.c_int64)]
+
+
+class kv_token_reshard_desc(C.Structure):
+    _fields_ = [("num_sources", C.c_int32), ("num_layers", C.c_int32), ("dcp_size", C.c_int32),
+                ("page_size", C.c_int32), ("token_rows", C.c_int32), ("row_bytes", C.c_int32),
+                ("src_pages", C.c_int64), ("dst_pages", C.c_int64)]
 
 
 class dcp_attn_desc(C.Structure):
@@ -97,6 +103,8 @@ _lib.kv_pack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, _P
                                _P, _P, _P, _P]
 _lib.kv_unpack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, C.c_int64,
                                  C.c_int64, _P, _P, _P]
+_lib.kv_reshard_tokens.argtypes = [C.POINTER(kv_token_reshard_desc), C.POINTER(_P), C.POINTER(_P), _P, _P,
+                                   C.c_int64, C.c_int64, _P, _P]
 _lib.dcp_decode_partial_workspace.argtypes = [C.POINTER(dcp_attn_desc), C.c_int64]
 _lib.dcp_decode_partial_workspace.restype = C.c_size_t
 _lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P,
@@ -104,7 +112,7 @@ _lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P),
 _lib.dcp_lse_merge.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P]
 for _f in ("cp_layersplit_layer_range", "dcp_filter_kv_indices", "dcp_pagemap_create",
            "dcp_pagemap_alloc", "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
-           "kv_path_entries", "kv_pack_pages", "kv_unpack_pages",
+           "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
            "dcp_decode_partial", "dcp_lse_merge"):
     getattr(_lib, _f).restype = C.c_int
 
@@ -254,6 +262,18 @@ def kv_reshard_pages(*, num_layers: int, dcp_size: int, page_bytes: int, src_pag
                                  _ptr_array(src_scales), _ptr_array(dst_scales), _dptr(src_page_ids),
                                  _dptr(dst_global_pages), n, first_uncached, _dptr(bad_entries),
                                  _stream(stream)))
+
+
+def kv_reshard_tokens(*, num_layers: int, dcp_size: int, page_size: int, token_rows: int, row_bytes: int,
+                      src_pages: int, dst_pages: int, src_pools, dst_pools, src_page_ids, dst_global_pages,
+                      first_uncached: int = 0, bad_entries=None, num_pages: Optional[int] = None,
+                      stream=None) -> None:
+    """Enqueue the token scatter reshard for pools under token ownership (see include/dcpkv.h)."""
+    desc = kv_token_reshard_desc(len(src_pools), num_layers, dcp_size, page_size, token_rows, row_bytes,
+                                 src_pages, dst_pages)
+    n = src_page_ids.numel() if num_pages is None else num_pages
+    _check(_lib.kv_reshard_tokens(C.byref(desc), _ptr_array(src_pools), _ptr_array(dst_pools), _dptr(src_page_ids),
+                                  _dptr(dst_global_pages), n, first_uncached, _dptr(bad_entries), _stream(stream)))
 
 
 def _path_desc(num_sources: int, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int,

@@ -139,6 +139,71 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a)
   }
 }
 
+// ---------------------------------------------------------------------------
+// Token scatter under token ownership ([SGL]: token t on shard t mod N)
+// ---------------------------------------------------------------------------
+
+struct TokenReshardArgs {
+  const uint8_t* src[kMaxSources];
+  uint8_t* dst[kMaxShards];
+  const int32_t* src_ids;
+  const int64_t* dst_ids;
+  int32_t* bad;
+  int64_t page_bytes, seg_bytes, src_pages, dst_pages, first, work, items;
+  int32_t segs, num_layers, num_sources, n, page_size, row_bytes;
+};
+
+// Item (layer, sequence page i, segment): the page's tokens x land on shard (i*P + x) mod N
+// as local token u = (i*P + x) div N, row u mod P of the request's virtual page i div N, whose
+// slot is g_{(i div N) N} div N on every shard.  A page is token_rows blocks of P rows of
+// row_bytes; token x is row x of each block, and so is its destination row.
+__global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenReshardArgs a) {
+  const int64_t per_layer = a.work * a.segs;
+  const int block_bytes = a.page_size * a.row_bytes;
+  for (int64_t it = blockIdx.x; it < a.items; it += gridDim.x) {
+    const int layer = (int)(it / per_layer);
+    const int64_t rest = it - (int64_t)layer * per_layer;
+    const int64_t i = a.first + rest / a.segs;
+    const int sg = (int)(rest % a.segs);
+    const int32_t sp = a.src_ids[i];
+    const int64_t j = i / a.n;
+    const int64_t g = a.dst_ids[j * a.n];
+    const int64_t slot = a.n > 1 ? g / a.n : g;
+    if (sp < 0 || sp >= a.src_pages || g < 0 || slot >= a.dst_pages) {
+      if (sg == 0 && threadIdx.x == 0 && a.bad) atomicAdd(a.bad, 1);
+      continue;
+    }
+    int r, begin;
+    layer_owner(layer, a.num_layers, a.num_sources, r, begin);
+    const int64_t off0 = (int64_t)sg * a.seg_bytes;
+    const uint8_t* src = a.src[r] + ((int64_t)(layer - begin) * a.src_pages + sp) * a.page_bytes;
+    const int64_t dst_page = ((int64_t)layer * a.dst_pages + slot) * a.page_bytes;
+    const int64_t len = (a.page_bytes - off0) < a.seg_bytes ? (a.page_bytes - off0) : a.seg_bytes;
+    const int chunks = (int)(len >> 4);
+    const int64_t t0 = i * a.page_size;  // first token of the page
+    u32x4 v[kReshardUnroll];
+#pragma unroll
+    for (int q = 0; q < kReshardUnroll; ++q) {
+      const int c = q * kReshardThreads + threadIdx.x;
+      if (c < chunks) v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off0) + c);
+    }
+#pragma unroll
+    for (int q = 0; q < kReshardUnroll; ++q) {
+      const int c = q * kReshardThreads + threadIdx.x;
+      if (c < chunks) {
+        const int o = (int)(off0 + 16 * (int64_t)c);  // byte offset in the page (< 2^31)
+        const int blk = o / block_bytes, rem = o - blk * block_bytes;
+        const int x = rem / a.row_bytes, off = rem - x * a.row_bytes;
+        const int64_t t = t0 + x;
+        const int d = (int)(t % a.n);
+        const int y = (int)((t / a.n) % a.page_size);
+        __builtin_nontemporal_store(
+            v[q], reinterpret_cast<u32x4*>(a.dst[d] + dst_page + ((int64_t)blk * a.page_size + y) * a.row_bytes + off));
+      }
+    }
+  }
+}
+
 static int device_cus_reshard() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -200,7 +265,7 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   a.dst_ids = dst_global_pages;
   a.bad = bad_entries;
   a.page_bytes = D.page_bytes;
-  {  // near-equal segments of at most 16 KB, 16-byte multiples, covering the page exactly
+  {  // near-equal segments of at most 36 KB, 16-byte multiples, covering the page exactly
     const int64_t nseg = (D.page_bytes + kReshardSegMax - 1) / kReshardSegMax;
     a.seg_bytes = (((D.page_bytes + nseg - 1) / nseg + 15) / 16) * 16;
     a.segs = (int32_t)((D.page_bytes + a.seg_bytes - 1) / a.seg_bytes);
@@ -220,5 +285,64 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
                      static_cast<hipStream_t>(stream), a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "reshard: launch failed: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}
+
+extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* const* src_pools,
+                                 void* const* dst_pools, const int32_t* src_page_ids,
+                                 const int64_t* dst_global_pages, int64_t num_pages, int64_t first_uncached,
+                                 int32_t* bad_entries, void* stream) {
+  if (!desc || !src_pools || !dst_pools) return set_error(DCPKV_EINVAL, "token reshard: NULL argument");
+  const kv_token_reshard_desc& D = *desc;
+  const int64_t page_bytes = (int64_t)D.token_rows * D.page_size * D.row_bytes;
+  if (D.num_sources < 1 || D.num_sources > kMaxSources || D.num_layers < D.num_sources ||
+      D.num_layers > kMaxLayers || D.dcp_size < 1 || D.dcp_size > kMaxShards || D.page_size < 1 ||
+      D.token_rows < 1 || D.row_bytes < 16 || D.row_bytes % 16 != 0 || page_bytes > INT32_MAX ||
+      D.src_pages < 1 || D.dst_pages < 1)
+    return set_error(DCPKV_EINVAL,
+                     "token reshard: bad descriptor (N_cp=%d L=%d N=%d page=%d rows=%d row_bytes=%d S=%lld M=%lld)",
+                     D.num_sources, D.num_layers, D.dcp_size, D.page_size, D.token_rows, D.row_bytes,
+                     (long long)D.src_pages, (long long)D.dst_pages);
+  if (num_pages < 0 || first_uncached < 0 || first_uncached > num_pages)
+    return set_error(DCPKV_EINVAL, "token reshard: first_uncached %lld outside [0, %lld]",
+                     (long long)first_uncached, (long long)num_pages);
+  const int64_t work = num_pages - first_uncached;
+  if (work == 0) return DCPKV_OK;
+  if (!src_page_ids || !dst_global_pages) return set_error(DCPKV_EINVAL, "token reshard: NULL page id arrays");
+  TokenReshardArgs a = {};
+  for (int r = 0; r < D.num_sources; ++r) {
+    if (!src_pools[r] || !aligned16(src_pools[r]))
+      return set_error(DCPKV_EINVAL, "token reshard: source pool %d is NULL or not 16-byte aligned", r);
+    a.src[r] = static_cast<const uint8_t*>(src_pools[r]);
+  }
+  for (int d = 0; d < D.dcp_size; ++d) {
+    if (!dst_pools[d] || !aligned16(dst_pools[d]))
+      return set_error(DCPKV_EINVAL, "token reshard: destination pool %d is NULL or not 16-byte aligned", d);
+    a.dst[d] = static_cast<uint8_t*>(dst_pools[d]);
+  }
+  a.src_ids = src_page_ids;
+  a.dst_ids = dst_global_pages;
+  a.bad = bad_entries;
+  a.page_bytes = page_bytes;
+  {
+    const int64_t nseg = (page_bytes + kReshardSegMax - 1) / kReshardSegMax;
+    a.seg_bytes = (((page_bytes + nseg - 1) / nseg + 15) / 16) * 16;
+    a.segs = (int32_t)((page_bytes + a.seg_bytes - 1) / a.seg_bytes);
+  }
+  a.src_pages = D.src_pages;
+  a.dst_pages = D.dst_pages;
+  a.first = first_uncached;
+  a.work = work;
+  a.items = (int64_t)D.num_layers * work * a.segs;
+  a.num_layers = D.num_layers;
+  a.num_sources = D.num_sources;
+  a.n = D.dcp_size;
+  a.page_size = D.page_size;
+  a.row_bytes = D.row_bytes;
+  const int64_t grid = std::min<int64_t>(a.items, (int64_t)device_cus_reshard() * kReshardBlocksPerCU);
+  hipLaunchKernelGGL(reshard_tokens_kernel, dim3((unsigned)grid), dim3(kReshardThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "token reshard: launch failed: %s", hipGetErrorString(e));
   return DCPKV_OK;
 }

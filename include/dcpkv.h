@@ -185,6 +185,43 @@ DCPKV_API int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* s
                      int64_t first_uncached, int32_t* bad_entries, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * (1c) Token scatter reshard for pools under token ownership                *
+ *      ([2DR] section 2 per path; [SGL]: token t on rank t mod N)           *
+ * ------------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t num_sources;  /* N_cp layer-split sources, >= 1 */
+  int32_t num_layers;   /* L, >= num_sources */
+  int32_t dcp_size;     /* N destination pools, >= 1 */
+  int32_t page_size;    /* tokens per page */
+  int32_t token_rows;   /* R: a page is R blocks of page_size rows (SPLIT: 2 * Hkv; MLA: 1) */
+  int32_t row_bytes;    /* bytes per row, a multiple of 16 (SPLIT: head_dim * elem; MLA: 576) */
+  int64_t src_pages;    /* S: page slots per layer slot in each source pool */
+  int64_t dst_pages;    /* M: local page slots per layer in each destination */
+} kv_token_reshard_desc;
+
+/* One request's transfer into pools that hold tokens under token ownership
+ * (DCPKV_OWN_TOKEN).  Entry i of the lists is sequence page i: its source page
+ * src_page_ids[i] (device int32) and its global page dst_global_pages[i]
+ * (device int64, the allocator's canonical placement).  For every layer l (from
+ * its owner r, as in kv_reshard_pages), every page i in [first_uncached,
+ * num_pages) and every token x < page_size of it, with t = i*page_size + x:
+ *     d = t mod N,  u = t div N,  slot = g_{(i div N) N} div N  (N == 1: g_i)
+ *     dst[d][l][slot] row (u mod page_size) of block b  =  src[r][l - begin_r]
+ *         [src_page_ids[i]] row x of block b,   for every block b < token_rows
+ * i.e. a source page's tokens land on every shard, in the request's virtual page
+ * i div N.  Whole uncached pages move, tail rows included.  Page scales cannot
+ * follow tokens that leave their page, so this call takes no scales (pools with
+ * per-page fp8 scales under token ownership are out of its scope).
+ * bad_entries (device int32 [1], nullable): incremented once per (layer, page)
+ * whose source id is outside [0, S) or whose virtual page slot is outside
+ * [0, M); such pages are skipped.  EINVAL on a bad descriptor, NULL or
+ * misaligned pools, first_uncached outside [0, num_pages]. */
+DCPKV_API int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* const* src_pools,
+                      void* const* dst_pools, const int32_t* src_page_ids, const int64_t* dst_global_pages,
+                      int64_t num_pages, int64_t first_uncached, int32_t* bad_entries, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * (1b) Bounded pack / unpack of one (source, destination) path              *
  *      ([2DR] section 2: a path carries L_r x P_d pages; sections 6.2-6.3:   *
  *      ownership by destination page value; [PR28]: a fixed-size pack       *

@@ -50,6 +50,10 @@ design notes as well):
       tokens j*page_size .. j*page_size + page_size - 1 and sits at the slot of
       the request's j-th virtual page (the allocator's unit of N pages), the
       same slot page ownership gives it.
+  R19 Per-page fp8 scales under token ownership: a destination page gathers
+      tokens of N source pages, each quantised with its own page's scale, so a
+      byte copy cannot keep one scale per page; the token reshard moves only
+      pools without scales.
 
 Parity pins live in tests/test_oracle_pins.py; every function here has one.
 """
@@ -261,6 +265,39 @@ def reshard(src_pools: Sequence[np.ndarray], dst_pools: Sequence[np.ndarray],
         if r == 0 and ls == 0:
             sent[d] += 1
     return sent
+
+
+# --------------------------------------------------------------------------
+# Token scatter reshard under token ownership (readings R18, R19)
+# --------------------------------------------------------------------------
+
+
+def reshard_tokens(src_pools: Sequence[np.ndarray], dst_pools: Sequence[np.ndarray], num_layers: int,
+                   dcp_size: int, page_size: int, token_rows: int, row_bytes: int, src_page_ids,
+                   dst_global_pages, first_uncached: int) -> int:
+    """Token-granular version of the 2D reshard for pools under token ownership; returns rows moved.
+
+    [2DR] section 2 moves L_r x P_d per path; with token ownership ([SGL]) a
+    source page's tokens land on every rank (reading R18: token t is row
+    (t div N) mod page_size of local page (t div N) div page_size of shard t mod N,
+    at the slot of that virtual page).  A page holds token_rows blocks of
+    page_size rows of row_bytes bytes; token x of a page is row x of every block.
+    Whole uncached source pages move, tail rows included (reading R8).  Entry i
+    of the lists is sequence page i.  Pools are uint8 [.][S or M][page_bytes].
+    """
+    num_sources = len(src_pools)
+    moved = 0
+    for r in range(num_sources):
+        a, b = layer_range(num_layers, num_sources, r)
+        for layer in range(a, b):
+            for i in range(first_uncached, len(dst_global_pages)):
+                src = src_pools[r][layer - a, int(src_page_ids[i])].reshape(token_rows, page_size, row_bytes)
+                for x in range(page_size):
+                    d, slot, y = token_place(i * page_size + x, dcp_size, page_size, dst_global_pages)
+                    dst = dst_pools[d][layer, slot].reshape(token_rows, page_size, row_bytes)
+                    dst[:, y, :] = src[:, x, :]
+                    moved += 1
+    return moved
 
 
 # --------------------------------------------------------------------------

@@ -389,6 +389,26 @@ def run_path_pack(rc: ReshardCase, cap_units: int, stream=None, src_ids=None, ds
     return moved
 
 
+def token_geometry(w: Workload):
+    """(token_rows, row_bytes) of the workload's page layout for the token reshard."""
+    if w.layout == "mla":
+        return 1, 576
+    return 2 * w.num_kv_heads, w.head_dim_qk * w.elem_bytes
+
+
+def run_reshard_tokens(rc: ReshardCase, bad=None, src_ids=None, dst_ids=None, stream=None):
+    w = rc.w
+    dev = rc.src_pools[0].device
+    si = torch.from_numpy((rc.src_ids if src_ids is None else src_ids).astype(np.int32)).to(dev)
+    di = torch.from_numpy((rc.dst_ids if dst_ids is None else dst_ids).astype(np.int64)).to(dev)
+    R, rb = token_geometry(w)
+    K.kv_reshard_tokens(num_layers=rc.num_layers, dcp_size=w.dcp_size, page_size=w.page_size, token_rows=R,
+                        row_bytes=rb, src_pages=rc.src_pages, dst_pages=w.pool_pages, src_pools=rc.src_pools,
+                        dst_pools=rc.dst_pools, src_page_ids=si, dst_global_pages=di,
+                        first_uncached=rc.first_uncached, bad_entries=bad, stream=stream)
+    return si, di
+
+
 def check_reshard_by_plan(rc: ReshardCase, dst_filter=-1, sentinel=gen.DST_SENTINEL):
     """Bit-exact check of every destination page against the oracle's copy plan.
 

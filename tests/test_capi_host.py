@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTED)
-    assert K.dcpkv_abi_version() == 3
+    assert K.dcpkv_abi_version() == 4
 
 
 @pytest.mark.parametrize("L_,n", [(78, 8), (64, 4), (4, 4), (17, 5), (1, 1), (100, 7)])
@@ -171,3 +171,19 @@ def test_path_entry_points_reject_bad_arguments_on_host():
     assert L._lib.kv_unpack_pages(C.byref(good), 0, 2, v, None, v, v, v, 0, 4, v, None, None) == E  # dest
     assert L._lib.kv_unpack_pages(C.byref(good), 0, 0, v, v, v, v, v, 0, 4, v, None, None) == E  # one scale side
     assert L._lib.kv_unpack_pages(C.byref(good), 0, 0, None, None, v, v, v, 0, 4, v, None, None) == E
+
+
+def test_token_reshard_rejects_bad_arguments_on_host():
+    p = (C.c_void_p * 4)(256, 256, 256, 256)
+    v = C.c_void_p(256)
+    E = L.DCPKV_EINVAL
+    bad_rows = L.kv_token_reshard_desc(1, 2, 2, 64, 2, 72, 8, 8)     # row_bytes not a multiple of 16
+    assert L._lib.kv_reshard_tokens(C.byref(bad_rows), p, p, v, v, 4, 0, None, None) == E
+    few_layers = L.kv_token_reshard_desc(2, 1, 2, 64, 1, 576, 8, 8)  # fewer layers than sources
+    assert L._lib.kv_reshard_tokens(C.byref(few_layers), p, p, v, v, 4, 0, None, None) == E
+    good = L.kv_token_reshard_desc(1, 2, 2, 64, 1, 576, 8, 8)
+    assert L._lib.kv_reshard_tokens(C.byref(good), p, p, v, v, 4, 5, None, None) == E  # first_uncached
+    assert L._lib.kv_reshard_tokens(C.byref(good), p, p, None, None, 4, 0, None, None) == E
+    assert L._lib.kv_reshard_tokens(C.byref(good), p, p, None, None, 4, 4, None, None) == 0  # nothing to move
+    mis = (C.c_void_p * 2)(264, 256)
+    assert L._lib.kv_reshard_tokens(C.byref(good), mis, p, v, v, 4, 0, None, None) == E

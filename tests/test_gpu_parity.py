@@ -393,3 +393,79 @@ def test_path_entries_value_owned_and_bad_ids_excluded():
     _sync()
     for d in range(4):
         assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
+# --------------------------------------------------------------------------- token scatter reshard
+
+
+@pytest.mark.parametrize("name,n,cached", [("gqa_bf16_16x4k-32k", 4, 3), ("tiny_fp32", 2, 0),
+                                           ("gqa_bf16_16x4k-32k", 3, 0), ("gqa_bf16_16x4k-32k", 1, 2)])
+def test_reshard_tokens_vs_oracle(name, n, cached):
+    """Layer-split sources into token-owned pools, bit for bit against the oracle (several sources
+    and layers, cached pages, a partial last page, N that does not divide the page)."""
+    base = get_workload(name)
+    w = scaled(base, seed=base.seed + 120, seq_segments=((1, base.page_size * 23 + 5, base.page_size * 23 + 5),),
+               num_layers=5, num_sources=2, pool_pages=32, dcp_size=n)
+    H.log(f"token reshard {name} N={n} cached={cached}")
+    rc = H.make_reshard_case(w, DEV, first_uncached=cached)
+    dst_host = _host_pools(rc.dst_pools)
+    R, rb = H.token_geometry(w)
+    O.reshard_tokens(_host_pools(rc.src_pools), dst_host, rc.num_layers, n, w.page_size, R, rb, rc.src_ids,
+                     rc.dst_ids, cached)
+    H.run_reshard_tokens(rc)
+    _sync()
+    for d in range(n):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
+def test_reshard_tokens_bad_pages_skipped_and_counted():
+    base = get_workload("gqa_bf16_16x4k-32k")
+    w = scaled(base, seed=base.seed + 121, seq_segments=((1, 64 * 9, 64 * 9),), num_layers=2, num_sources=1,
+               pool_pages=8, dcp_size=4)
+    rc = H.make_reshard_case(w, DEV, first_uncached=0)
+    src = rc.src_ids.copy()
+    src[2] = rc.src_pages + 1  # page 2: source id out of range
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.run_reshard_tokens(rc, bad=bad, src_ids=src)
+    _sync()
+    assert int(bad.item()) == 2  # one per layer
+    dst_host = _host_pools([torch.full_like(t, gen.DST_SENTINEL) for t in rc.dst_pools])
+    R, rb = H.token_geometry(w)
+    keep_src = src.copy()
+    src_host = _host_pools(rc.src_pools)
+    # the oracle moves every page; page 2's rows are then put back to the sentinel
+    O.reshard_tokens(src_host, dst_host, 2, 4, w.page_size, R, rb, np.where(keep_src >= rc.src_pages, 0, keep_src),
+                     rc.dst_ids, 0)
+    for x in range(w.page_size):
+        d, slot, y = O.token_place(2 * w.page_size + x, 4, w.page_size, rc.dst_ids)
+        for layer in range(2):
+            pg = dst_host[d][layer, slot].reshape(R, w.page_size, rb)
+            pg[:, y, :] = gen.DST_SENTINEL
+    for d in range(4):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_token_pipeline_reshard_then_decode(q_len):
+    """Token reshard into token-owned pools, then decode under token ownership: every partial and
+    the merged output against the oracle's attention over the source pages' logical sequence."""
+    base = get_workload("gqa_bf16_16x4k-32k")
+    lens = (64 * 20 + 7, 64 * 7 + 63)
+    w = scaled(base, seed=base.seed + 122 + q_len, seq_segments=tuple((1, t, t) for t in lens), num_layers=1,
+               num_sources=1, pool_pages=64, dcp_size=4, q_len=q_len)
+    case = H.make_decode_case(w, DEV, seq_lens=lens, own=K.OWN_TOKEN)
+    for b in range(len(lens)):
+        rc = H.make_reshard_case(w, DEV, seq_lens=lens, requests=[b], first_uncached=0, dst_pools=case.pools,
+                                 dst_scales=case.scales)
+        H.run_reshard_tokens(rc)
+        _sync()
+        srcp = rc.src_pools[0][0].index_select(0, torch.from_numpy(rc.src_ids).to(DEV)).cpu().numpy()
+        kv = H.oracle_logical_kv(w, srcp, None, lens[b])
+        (po, pl), (uo, ul) = H.oracle_request(case, b, kv=kv)
+        outs = H.run_decode(case)
+        _sync()
+        tol_o, tol_l = H.tolerance(w)
+        for d in range(4):
+            H.check_rows(f"partial d={d}", outs.partial_out[d, b].cpu().numpy(), outs.partial_lse[d, b].cpu().numpy(),
+                         po[d], pl[d], tol_o, tol_l)
+        H.check_rows("merged", outs.out[b].cpu().numpy(), outs.lse[b].cpu().numpy(), uo, ul, tol_o, tol_l)

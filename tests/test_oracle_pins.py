@@ -318,6 +318,95 @@ def test_logical_kv_gather_token_ownership():
     assert np.allclose(kk[0, :, 0], 2.0 * (1.0 + (np.arange(T) % 8) / 8.0)) and vv.shape == (1, T, 512)
 
 
+def _token_tagged_sources(L, ncp, S, R, psz, rb):
+    """Sources whose every row carries (source, layer slot, page, block, row) as int32s."""
+    pools = []
+    for r in range(ncp):
+        n_slots = O.local_layer_count(L, ncp, r)
+        p = np.zeros((n_slots + 1, S, R, psz, rb), dtype=np.uint8)
+        for ls in range(n_slots):
+            for sp in range(S):
+                for blk in range(R):
+                    for x in range(psz):
+                        tag = np.array([r, ls, sp, blk, x, 0x70C], dtype=np.int32).view(np.uint8)
+                        p[ls, sp, blk, x] = np.resize(tag, rb)
+        p[-1] = 0xEE
+        pools.append(p.reshape(n_slots + 1, S, R * psz * rb))
+    return pools
+
+
+@pytest.mark.parametrize("n,cached,T", [(1, 0, 70), (2, 0, 70), (4, 1, 150), (3, 2, 130), (8, 0, 64)])
+def test_reshard_tokens_pull_view(n, cached, T):
+    """Every destination row, checked from its tag: under token ownership row y of shard d's local
+    page j (slot of virtual page j) holds token t = (j * page + y) * N + d of the sequence, from
+    the source owning the layer; rows of cached or missing tokens keep the sentinel."""
+    L, ncp, psz, R, rb, M = 5, 2, 8, 2, 32, 12
+    rng = np.random.default_rng(60 + n)
+    pm = O.PageMap(n, psz, M, rng.permutation(M))
+    g = pm.alloc(T)
+    P = len(g)
+    S = P + 3
+    src = rng.permutation(S)[:P]
+    srcp = _token_tagged_sources(L, ncp, S, R, psz, rb)
+    dst = [np.full((L, M, R * psz * rb), 0xA5, dtype=np.uint8) for _ in range(n)]
+    moved = O.reshard_tokens(srcp, dst, L, n, psz, R, rb, src, g, cached)
+    assert moved == L * (P - cached) * psz
+    vslot = {j: O.dcp_local_slot(int(g[j * n]), n) for j in range(-(-P // n))}
+    for d in range(n):
+        for layer in range(L):
+            owner = next(r for r in range(ncp) if O.layer_range(L, ncp, r)[0] <= layer < O.layer_range(L, ncp, r)[1])
+            for s_ in range(M):
+                page = dst[d][layer, s_].reshape(R, psz, rb)
+                js = [j for j, v in vslot.items() if v == s_]
+                for y in range(psz):
+                    t = (js[0] * psz + y) * n + d if js else None
+                    for blk in range(R):
+                        row = page[blk, y]
+                        if t is None or t // psz >= P or t // psz < cached:
+                            assert (row == 0xA5).all()
+                        else:
+                            want = [owner, layer - O.layer_range(L, ncp, owner)[0], int(src[t // psz]), blk,
+                                    t % psz, 0x70C]
+                            assert row[:24].view(np.int32).tolist() == want
+
+
+def test_reshard_tokens_one_shard_is_the_page_reshard():
+    """With N = 1 token and page ownership coincide: the token reshard writes what the page
+    reshard writes."""
+    L, ncp, psz, R, rb, M = 4, 2, 8, 2, 16, 6
+    rng = np.random.default_rng(70)
+    pm = O.PageMap(1, psz, M, rng.permutation(M))
+    g = pm.alloc(37)
+    src = rng.permutation(len(g) + 2)[:len(g)]
+    srcp = _token_tagged_sources(L, ncp, len(g) + 2, R, psz, rb)
+    a = [np.full((L, M, R * psz * rb), 0xA5, dtype=np.uint8)]
+    b = [np.full((L, M, R * psz * rb), 0xA5, dtype=np.uint8)]
+    O.reshard_tokens(srcp, a, L, 1, psz, R, rb, src, g, 1)
+    O.reshard(srcp, b, L, 1, src, g, 1)
+    assert np.array_equal(a[0], b[0])
+
+
+def test_reshard_tokens_gives_the_page_reshards_logical_sequence():
+    """Same sources, either ownership: the token reshard read back under token ownership gives
+    the same logical K/V as the page reshard read back under page ownership."""
+    n, psz, hkv, D, T, M = 4, 8, 2, 4, 70, 16
+    rng = np.random.default_rng(80)
+    pm = O.PageMap(n, psz, M, rng.permutation(M))
+    g = pm.alloc(T)
+    P = len(g)
+    src_ids = rng.permutation(P)
+    pb = 2 * hkv * psz * D * 4
+    srcp = [np.concatenate([rng.standard_normal((1, P, pb // 4)).astype(np.float32).view(np.uint8),
+                            np.zeros((1, P, pb), np.uint8)])]
+    dp = [np.zeros((1, M, pb), np.uint8) for _ in range(n)]
+    dt = [np.zeros((1, M, pb), np.uint8) for _ in range(n)]
+    O.reshard(srcp, dp, 1, n, src_ids, g, 0)
+    O.reshard_tokens(srcp, dt, 1, n, psz, 2 * hkv, D * 4, src_ids, g, 0)
+    kp, vp = O.logical_kv_split(lambda d, s_: dp[d][0, s_], g, n, "f32", hkv, psz, D, T)
+    kt, vt = O.logical_kv_split_tokens(lambda d, s_: dt[d][0, s_], g, n, "f32", hkv, psz, D, T)
+    assert np.array_equal(kp, kt) and np.array_equal(vp, vt)
+
+
 # --------------------------------------------------------------------------- bounded pack / unpack
 
 
