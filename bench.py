@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="gqa_bf16_16x4k-32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--own", choices=["page", "token"], default="page",
+                    help="DCP ownership: page p on shard p mod N (default) or token t on shard t mod N")
     ap.add_argument("--pack-cap-mib", type=int, default=64,
                     help="staging buffer of the path-by-path (bounded pack/unpack) transfer timed after the "
                          "steps; 0 skips it")
@@ -78,12 +80,13 @@ def load_traffic(kernel_key: str, src_hash: str, launches_bytes: float):
 class Step:
     """Device state of one workload: inputs, outputs and the three calls."""
 
-    def __init__(self, w, dev):
+    def __init__(self, w, dev, own: str = "page"):
         import torch
         import context_paged_kv_amd as K
         from workloads import gen
 
         self.w, self.dev, self.K = w, dev, K
+        self.own = 1 if own == "token" else 0
         N, M, pb = w.dcp_size, w.pool_pages, w.page_bytes
         self.seq_lens = gen.draw_seq_lens(w)
         self.total_tokens = int(self.seq_lens.sum())
@@ -91,7 +94,7 @@ class Step:
         self.pages = [pm.alloc(int(t)) for t in self.seq_lens]
         pm.close()
         self.max_local = max(-(-len(p) // N) for p in self.pages)
-        tables, _ = K.dcp_build_block_tables(N, self.pages, self.max_local)
+        tables, _ = K.dcp_build_block_tables(N, self.pages, self.max_local, token_interleave=self.own)
         # the transfer: every request's pages (or only the long ones), from the layer-split sources
         self.has_reshard = w.num_sources > 0
         self.has_attention = w.has_attention
@@ -143,7 +146,7 @@ class Step:
             q_dtype=K.Q_BF16 if w.q_dtype == "bf16" else K.Q_F32, num_q_heads=hq, num_kv_heads=w.num_kv_heads,
             head_dim_qk=w.head_dim_qk, head_dim_v=dv, page_size=w.page_size, dcp_size=N, batch=B, q_len=ql,
             max_local_pages=self.max_local, layer=w.attn_layer, num_layers=w.num_layers, pages_per_layer=M,
-            softmax_scale=w.softmax_scale)
+            softmax_scale=w.softmax_scale, token_interleave=self.own)
         self.ws = torch.empty(K.dcp_decode_partial_workspace(self.desc, self.total_tokens), dtype=torch.uint8,
                               device=dev)
         self.po = torch.empty((N, B, ql, hq, dv), dtype=torch.float32, device=dev)
@@ -156,6 +159,14 @@ class Step:
         if not self.has_reshard:
             return
         w = self.w
+        if self.own:  # token ownership: the token scatter (pools without page scales)
+            rows, row_bytes = (1, 576) if w.layout == "mla" else (2 * w.num_kv_heads, w.head_dim_qk * w.elem_bytes)
+            self.K.kv_reshard_tokens(num_layers=w.num_layers, dcp_size=w.dcp_size, page_size=w.page_size,
+                                     token_rows=rows, row_bytes=row_bytes, src_pages=self.src_pages,
+                                     dst_pages=w.pool_pages, src_pools=self.src, dst_pools=self.pools,
+                                     src_page_ids=self.src_ids, dst_global_pages=self.dst_ids,
+                                     first_uncached=self.first_uncached)
+            return
         self.K.kv_reshard_pages(num_layers=w.num_layers, dcp_size=w.dcp_size, page_bytes=w.page_bytes,
                                 src_pages=self.src_pages, dst_pages=w.pool_pages, src_pools=self.src,
                                 dst_pools=self.pools, src_page_ids=self.src_ids, dst_global_pages=self.dst_ids,
@@ -282,24 +293,36 @@ def cpu_baseline(st, budget_s: float):
             g = st.dst_ids[sel].cpu().numpy()
             g2 = np.arange(n) * w.dcp_size + (g % w.dcp_size)
             dst_h = [np.zeros((w.num_sources, n, w.page_bytes), np.uint8) for _ in range(w.dcp_size)]
+            if st.own:  # token scatter: sequence pages 0..n-1 of one request, virtual page i div N at slot i div N
+                rows, row_bytes = (1, 576) if w.layout == "mla" else (2 * w.num_kv_heads,
+                                                                       w.head_dim_qk * w.elem_bytes)
             reps, t0 = 0, time.perf_counter()
             while time.perf_counter() - t0 < budget:
-                O.reshard(src_h, dst_h, w.num_sources, w.dcp_size, np.arange(n), g2, 0)
+                if st.own:
+                    O.reshard_tokens(src_h, dst_h, w.num_sources, w.dcp_size, w.page_size, rows, row_bytes,
+                                     np.arange(n), np.arange(n), 0)
+                else:
+                    O.reshard(src_h, dst_h, w.num_sources, w.dcp_size, np.arange(n), g2, 0)
                 reps += 1
             t_rs = time.perf_counter() - t0
             rate = 2.0 * reps * n * w.num_sources * w.page_bytes / t_rs
             rs_time_full = st.bytes_reshard() / rate
-            notes.append(f"scalar reshard of {n} pages x {w.num_sources} layer(s), {reps} passes in {t_rs:.1f}s")
+            kind = "token scatter" if st.own else "page"
+            notes.append(f"scalar {kind} reshard of {n} pages x {w.num_sources} layer(s), {reps} passes in {t_rs:.1f}s")
         if st.has_attention:
             done, t0, rows = 0, time.perf_counter(), 0
             b = 0
             while time.perf_counter() - t0 < budget and b < w.num_requests:
-                pb, ps = Hn.gather_request_pages(st.pools, st.scales, st.pages[b], w.dcp_size, w.attn_layer)
-                kv = Hn.oracle_logical_kv(w, pb, ps, int(st.seq_lens[b]))
+                if st.own:
+                    kv = Hn.gather_token_layout_kv(st, b, w.attn_layer)
+                else:
+                    pb, ps = Hn.gather_request_pages(st.pools, st.scales, st.pages[b], w.dcp_size, w.attn_layer)
+                    kv = Hn.oracle_logical_kv(w, pb, ps, int(st.seq_lens[b]))
                 q = st.q[b].float().cpu().numpy().astype(np.float64)
                 for h in range(w.num_q_heads):
                     po, pl = O.request_partials(q, kv[0], kv[1], int(st.seq_lens[b]), w.softmax_scale,
-                                                st.pages[b], w.page_size, w.dcp_size, heads=[h])
+                                                st.pages[b], w.page_size, w.dcp_size, heads=[h],
+                                                own="token" if st.own else "page")
                     O.lse_merge(po[:, :, [h]], pl[:, :, [h]])
                     rows += 1
                     done += int(st.seq_lens[b]) * w.q_len
@@ -338,7 +361,7 @@ def plain_copy_gbps(torch, dev, nbytes: int, reps: int = 5) -> float:
 
 
 # kernels of each timed call, as rocprofv3 names them
-CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",),
+CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",), "reshard_tokens_kernel": ("reshard_tokens_kernel",),
                 "dcp_decode_partial": ("plan_kernel", "gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
                                        "chunk_reduce_kernel")}
 
@@ -386,7 +409,7 @@ def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: in
         out[counter] = {"kib_per_launch": sum(v for _, v in mine) / launches, "scale": scale,
                         "calib_kib": calib[0], "launches": launches}
     hbm = sum(out[c]["kib_per_launch"] * 1024.0 * out[c]["scale"] for c in out)
-    key = f"{wl}:{call}"
+    key = f"{wl}:{call}" + (":token" if line["config"].get("ownership") == "token" else "")
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
@@ -424,7 +447,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
-    st = Step(w, dev)
+    if a.own == "token" and w.has_scales and w.num_sources > 0:
+        print(f"{w.name}: its pools carry per-page fp8 scales, which the token reshard does not move",
+              file=sys.stderr)
+        sys.exit(2)
+    st = Step(w, dev, a.own)
     torch.cuda.synchronize()
     if a.calib_copy_mib:  # one elementwise kernel reading and writing exactly this many bytes
         n = a.calib_copy_mib * (1 << 20) // 4
@@ -473,7 +500,7 @@ def main():
                       "reshard_us": round(t_rs.mean() * 1e6, 2),
                       "plain_copy_GBps": round(copy_gbps, 1),
                       "reshard_frac_of_plain_copy": round(rs_gbps / copy_gbps, 4)})
-        if a.pack_cap_mib > 0 and st.num_pages > st.first_uncached:
+        if a.pack_cap_mib > 0 and not st.own and st.num_pages > st.first_uncached:
             # the same pages path by path through a fixed staging buffer: every page is read and
             # written twice (source -> staging -> pool)
             cap = max(1, (a.pack_cap_mib << 20) // w.page_bytes)
@@ -502,7 +529,8 @@ def main():
                       "decode_tokens_per_s": round(w.num_requests * w.q_len / t_attn, 1)})
     # roofline of the dominant call of the step
     if st.has_reshard and (not st.has_attention or t_rs.mean() >= t_pa.mean()):
-        dom, src_files = "reshard_kernel", ["reshard.hip", "common.h"]
+        dom = "reshard_tokens_kernel" if st.own else "reshard_kernel"
+        src_files = ["reshard.hip", "common.h"]
         achieved = b_rs / t_rs.mean() / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4)}
@@ -521,7 +549,8 @@ def main():
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4)}
     src_hash = kernel_source_hash(src_files)
-    roof.update({"traffic": load_traffic(f"{w.name}:{dom.split()[0]}", src_hash, dom_bytes), "kernel": dom,
+    tkey = f"{w.name}:{dom.split()[0]}" + (":token" if st.own else "")
+    roof.update({"traffic": load_traffic(tkey, src_hash, dom_bytes), "kernel": dom,
                  "algorithmic_bytes": int(dom_bytes), "source_hash": src_hash})
     cpu = None
     if not a.no_cpu_baseline:
@@ -537,7 +566,7 @@ def main():
         "config": {"workload": w.name, "requests": w.num_requests, "total_tokens": st.total_tokens,
                    "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_qk,
                    "page_size": w.page_size, "dcp_size": w.dcp_size, "q_len": w.q_len,
-                   "layers": w.num_layers, "step": steps_desc},
+                   "layers": w.num_layers, "ownership": a.own, "step": steps_desc},
         "parts": parts,
         "roofline": roof,
         "cpu_baseline": cpu,
