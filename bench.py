@@ -133,6 +133,9 @@ class Step:
         self.dst_ids = torch.from_numpy(np.concatenate([self.pages[b] for b in self.reshard_reqs] or [np.zeros(0)])
                                         .astype(np.int64)).to(dev)
         self.first_uncached = int(np.floor(w.cached_frac * self.num_pages)) if self.has_reshard else 0
+        # where each request's entries start in the lists (the token reshard restarts positions there)
+        self.req_offsets = torch.from_numpy(np.cumsum([0] + [len(self.pages[b]) for b in self.reshard_reqs])
+                                            .astype(np.int64)).to(dev)
         if not self.has_attention:
             return
         self.q = gen.draw_q(w, dev)
@@ -165,7 +168,7 @@ class Step:
                                      token_rows=rows, row_bytes=row_bytes, src_pages=self.src_pages,
                                      dst_pages=w.pool_pages, src_pools=self.src, dst_pools=self.pools,
                                      src_page_ids=self.src_ids, dst_global_pages=self.dst_ids,
-                                     first_uncached=self.first_uncached)
+                                     request_offsets=self.req_offsets, first_uncached=self.first_uncached)
             return
         self.K.kv_reshard_pages(num_layers=w.num_layers, dcp_size=w.dcp_size, page_bytes=w.page_bytes,
                                 src_pages=self.src_pages, dst_pages=w.pool_pages, src_pools=self.src,

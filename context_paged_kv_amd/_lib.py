@@ -32,6 +32,13 @@ import torch  # noqa: E402,F401
 
 _lib = C.CDLL(LIB_PATH)
 
+# the include/dcpkv.h revision these signatures follow; a library of another revision is refused
+ABI_VERSION = 5
+_lib.dcpkv_abi_version.restype = C.c_int
+if _lib.dcpkv_abi_version() != ABI_VERSION:
+    raise ImportError(f"{LIB_PATH} has ABI version {_lib.dcpkv_abi_version()}, this binding needs {ABI_VERSION}: "
+                      "rebuild it with `python -m context_paged_kv_amd.build`")
+
 DCPKV_OK = 0
 DCPKV_EDEVICE = -5
 DCPKV_ENOMEM = -12
@@ -104,7 +111,7 @@ _lib.kv_pack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, _P
 _lib.kv_unpack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, C.c_int64,
                                  C.c_int64, _P, _P, _P]
 _lib.kv_reshard_tokens.argtypes = [C.POINTER(kv_token_reshard_desc), C.POINTER(_P), C.POINTER(_P), _P, _P,
-                                   C.c_int64, C.c_int64, _P, _P]
+                                   C.c_int64, _P, C.c_int32, C.c_int64, _P, _P]
 _lib.dcp_decode_partial_workspace.argtypes = [C.POINTER(dcp_attn_desc), C.c_int64]
 _lib.dcp_decode_partial_workspace.restype = C.c_size_t
 _lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P,
@@ -266,14 +273,18 @@ def kv_reshard_pages(*, num_layers: int, dcp_size: int, page_bytes: int, src_pag
 
 def kv_reshard_tokens(*, num_layers: int, dcp_size: int, page_size: int, token_rows: int, row_bytes: int,
                       src_pages: int, dst_pages: int, src_pools, dst_pools, src_page_ids, dst_global_pages,
-                      first_uncached: int = 0, bad_entries=None, num_pages: Optional[int] = None,
-                      stream=None) -> None:
-    """Enqueue the token scatter reshard for pools under token ownership (see include/dcpkv.h)."""
+                      first_uncached: int = 0, request_offsets=None, num_requests: Optional[int] = None,
+                      bad_entries=None, num_pages: Optional[int] = None, stream=None) -> None:
+    """Enqueue the token scatter reshard for pools under token ownership (see include/dcpkv.h).
+    request_offsets: device int64 [B + 1] delimiting the requests in the lists (None: one request)."""
     desc = kv_token_reshard_desc(len(src_pools), num_layers, dcp_size, page_size, token_rows, row_bytes,
                                  src_pages, dst_pages)
     n = src_page_ids.numel() if num_pages is None else num_pages
+    if num_requests is None:
+        num_requests = request_offsets.numel() - 1 if request_offsets is not None else 1
     _check(_lib.kv_reshard_tokens(C.byref(desc), _ptr_array(src_pools), _ptr_array(dst_pools), _dptr(src_page_ids),
-                                  _dptr(dst_global_pages), n, first_uncached, _dptr(bad_entries), _stream(stream)))
+                                  _dptr(dst_global_pages), n, _dptr(request_offsets), num_requests, first_uncached,
+                                  _dptr(bad_entries), _stream(stream)))
 
 
 def _path_desc(num_sources: int, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int,

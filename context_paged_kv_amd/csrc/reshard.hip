@@ -148,15 +148,33 @@ struct TokenReshardArgs {
   uint8_t* dst[kMaxShards];
   const int32_t* src_ids;
   const int64_t* dst_ids;
+  const int64_t* req_off;  // request b owns list entries [req_off[b], req_off[b+1]); NULL: one request
   int32_t* bad;
-  int64_t page_bytes, seg_bytes, src_pages, dst_pages, first, work, items;
-  int32_t segs, num_layers, num_sources, n, page_size, row_bytes;
+  int64_t page_bytes, seg_bytes, src_pages, dst_pages, first, work, items, num_pages;
+  int32_t segs, num_layers, num_sources, n, page_size, row_bytes, num_req;
 };
 
-// Item (layer, sequence page i, segment): the page's tokens x land on shard (i*P + x) mod N
-// as local token u = (i*P + x) div N, row u mod P of the request's virtual page i div N, whose
-// slot is g_{(i div N) N} div N on every shard.  A page is token_rows blocks of P rows of
-// row_bytes; token x is row x of each block, and so is its destination row.
+// First list entry of the request that holds entry i (i < num_pages), or -1 when the offsets
+// name no request that contains i (offsets out of order or out of range).
+__device__ __forceinline__ int64_t token_request_base(const TokenReshardArgs& a, int64_t i) {
+  if (!a.req_off) return 0;
+  int lo = 0, hi = a.num_req - 1;
+  while (lo < hi) {  // last request whose first entry is <= i
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.req_off[mid] <= i)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const int64_t b0 = a.req_off[lo], b1 = a.req_off[lo + 1];
+  return (b0 >= 0 && b0 <= i && i < b1 && b1 <= a.num_pages) ? b0 : -1;
+}
+
+// Item (layer, list entry i, segment): entry i is sequence page k = i - o of the request whose
+// entries start at o.  The page's tokens x land on shard (k*P + x) mod N as local token
+// u = (k*P + x) div N, row u mod P of the request's virtual page k div N, whose slot is
+// g_{o + (k div N) N} div N on every shard.  A page is token_rows blocks of P rows of row_bytes;
+// token x is row x of each block, and so is its destination row.
 __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenReshardArgs a) {
   const int64_t per_layer = a.work * a.segs;
   const int block_bytes = a.page_size * a.row_bytes;
@@ -166,10 +184,11 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenRe
     const int64_t i = a.first + rest / a.segs;
     const int sg = (int)(rest % a.segs);
     const int32_t sp = a.src_ids[i];
-    const int64_t j = i / a.n;
-    const int64_t g = a.dst_ids[j * a.n];
+    const int64_t o = token_request_base(a, i);
+    const int64_t k = i - o;  // sequence page within the request (o >= 0 keeps o + (k/N)*N in [o, i])
+    const int64_t g = o >= 0 ? a.dst_ids[o + (k / a.n) * a.n] : -1;
     const int64_t slot = a.n > 1 ? g / a.n : g;
-    if (sp < 0 || sp >= a.src_pages || g < 0 || slot >= a.dst_pages) {
+    if (o < 0 || sp < 0 || sp >= a.src_pages || g < 0 || slot >= a.dst_pages) {
       if (sg == 0 && threadIdx.x == 0 && a.bad) atomicAdd(a.bad, 1);
       continue;
     }
@@ -180,7 +199,7 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenRe
     const int64_t dst_page = ((int64_t)layer * a.dst_pages + slot) * a.page_bytes;
     const int64_t len = (a.page_bytes - off0) < a.seg_bytes ? (a.page_bytes - off0) : a.seg_bytes;
     const int chunks = (int)(len >> 4);
-    const int64_t t0 = i * a.page_size;  // first token of the page
+    const int64_t t0 = k * a.page_size;  // first token of the page in its request
     u32x4 v[kReshardUnroll];
 #pragma unroll
     for (int q = 0; q < kReshardUnroll; ++q) {
@@ -290,7 +309,8 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
 
 extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* const* src_pools,
                                  void* const* dst_pools, const int32_t* src_page_ids,
-                                 const int64_t* dst_global_pages, int64_t num_pages, int64_t first_uncached,
+                                 const int64_t* dst_global_pages, int64_t num_pages,
+                                 const int64_t* request_offsets, int32_t num_requests, int64_t first_uncached,
                                  int32_t* bad_entries, void* stream) {
   if (!desc || !src_pools || !dst_pools) return set_error(DCPKV_EINVAL, "token reshard: NULL argument");
   const kv_token_reshard_desc& D = *desc;
@@ -306,10 +326,16 @@ extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* 
   if (num_pages < 0 || first_uncached < 0 || first_uncached > num_pages)
     return set_error(DCPKV_EINVAL, "token reshard: first_uncached %lld outside [0, %lld]",
                      (long long)first_uncached, (long long)num_pages);
+  if (num_requests < 0 || (num_requests > 1 && !request_offsets) || (request_offsets && num_requests < 1))
+    return set_error(DCPKV_EINVAL, "token reshard: %d requests with%s request_offsets", num_requests,
+                     request_offsets ? "" : "out");
   const int64_t work = num_pages - first_uncached;
   if (work == 0) return DCPKV_OK;
   if (!src_page_ids || !dst_global_pages) return set_error(DCPKV_EINVAL, "token reshard: NULL page id arrays");
   TokenReshardArgs a = {};
+  a.req_off = request_offsets;
+  a.num_req = request_offsets ? num_requests : 1;
+  a.num_pages = num_pages;
   for (int r = 0; r < D.num_sources; ++r) {
     if (!src_pools[r] || !aligned16(src_pools[r]))
       return set_error(DCPKV_EINVAL, "token reshard: source pool %d is NULL or not 16-byte aligned", r);

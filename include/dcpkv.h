@@ -200,26 +200,37 @@ typedef struct {
   int64_t dst_pages;    /* M: local page slots per layer in each destination */
 } kv_token_reshard_desc;
 
-/* One request's transfer into pools that hold tokens under token ownership
- * (DCPKV_OWN_TOKEN).  Entry i of the lists is sequence page i: its source page
- * src_page_ids[i] (device int32) and its global page dst_global_pages[i]
- * (device int64, the allocator's canonical placement).  For every layer l (from
- * its owner r, as in kv_reshard_pages), every page i in [first_uncached,
- * num_pages) and every token x < page_size of it, with t = i*page_size + x:
- *     d = t mod N,  u = t div N,  slot = g_{(i div N) N} div N  (N == 1: g_i)
- *     dst[d][l][slot] row (u mod page_size) of block b  =  src[r][l - begin_r]
- *         [src_page_ids[i]] row x of block b,   for every block b < token_rows
- * i.e. a source page's tokens land on every shard, in the request's virtual page
- * i div N.  Whole uncached pages move, tail rows included.  Page scales cannot
- * follow tokens that leave their page, so this call takes no scales (pools with
+/* A batch of requests' transfers into pools that hold tokens under token
+ * ownership (DCPKV_OWN_TOKEN), in one launch.  The lists concatenate the
+ * requests: request b owns entries [request_offsets[b], request_offsets[b+1])
+ * (device int64 [num_requests + 1], non-decreasing, from 0 to num_pages), and
+ * its entry i is its sequence page k = i - request_offsets[b]: source page
+ * src_page_ids[i] (device int32) and global page dst_global_pages[i] (device
+ * int64, the allocator's canonical placement).  request_offsets == NULL with
+ * num_requests <= 1 is one request over the whole list.  For every layer l
+ * (from its owner r, as in kv_reshard_pages), every entry i in
+ * [first_uncached, num_pages) and every token x < page_size of its page, with
+ * t = k*page_size + x the token's position in its request:
+ *     d = t mod N,  u = t div N,
+ *     slot = g_{o_b + (k div N) N} div N        (N == 1: g_i)
+ *     dst[d][l][slot] row (u mod page_size) of block b'  =  src[r][l - begin_r]
+ *         [src_page_ids[i]] row x of block b',   for every block b' < token_rows
+ * i.e. a source page's tokens land on every shard, in its request's virtual
+ * page k div N.  Whole uncached pages move, tail rows included.  first_uncached
+ * counts list entries, as in kv_reshard_pages.  Page scales cannot follow
+ * tokens that leave their page, so this call takes no scales (pools with
  * per-page fp8 scales under token ownership are out of its scope).
- * bad_entries (device int32 [1], nullable): incremented once per (layer, page)
- * whose source id is outside [0, S) or whose virtual page slot is outside
- * [0, M); such pages are skipped.  EINVAL on a bad descriptor, NULL or
- * misaligned pools, first_uncached outside [0, num_pages]. */
+ * bad_entries (device int32 [1], nullable): incremented once per (layer, entry)
+ * whose source id is outside [0, S), whose virtual page slot is outside
+ * [0, M), or that no request of request_offsets contains consistently; such
+ * entries are skipped.  Every access stays in bounds whatever the id arrays
+ * and offsets hold.  EINVAL on a bad descriptor, NULL or misaligned pools,
+ * first_uncached outside [0, num_pages], num_requests < 0, num_requests > 1
+ * without offsets, or offsets with num_requests < 1. */
 DCPKV_API int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* const* src_pools,
                       void* const* dst_pools, const int32_t* src_page_ids, const int64_t* dst_global_pages,
-                      int64_t num_pages, int64_t first_uncached, int32_t* bad_entries, void* stream);
+                      int64_t num_pages, const int64_t* request_offsets, int32_t num_requests,
+                      int64_t first_uncached, int32_t* bad_entries, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * (1b) Bounded pack / unpack of one (source, destination) path              *

@@ -274,7 +274,7 @@ def reshard(src_pools: Sequence[np.ndarray], dst_pools: Sequence[np.ndarray],
 
 def reshard_tokens(src_pools: Sequence[np.ndarray], dst_pools: Sequence[np.ndarray], num_layers: int,
                    dcp_size: int, page_size: int, token_rows: int, row_bytes: int, src_page_ids,
-                   dst_global_pages, first_uncached: int) -> int:
+                   dst_global_pages, first_uncached: int, request_offsets=None) -> int:
     """Token-granular version of the 2D reshard for pools under token ownership; returns rows moved.
 
     [2DR] section 2 moves L_r x P_d per path; with token ownership ([SGL]) a
@@ -282,18 +282,24 @@ def reshard_tokens(src_pools: Sequence[np.ndarray], dst_pools: Sequence[np.ndarr
     (t div N) mod page_size of local page (t div N) div page_size of shard t mod N,
     at the slot of that virtual page).  A page holds token_rows blocks of
     page_size rows of row_bytes bytes; token x of a page is row x of every block.
-    Whole uncached source pages move, tail rows included (reading R8).  Entry i
-    of the lists is sequence page i.  Pools are uint8 [.][S or M][page_bytes].
+    Whole uncached source pages move, tail rows included (reading R8).  The
+    lists concatenate requests: request b holds entries [o_b, o_{b+1}) of
+    request_offsets (None: one request), and its entry i is its sequence page
+    i - o_b.  first_uncached counts list entries.  Pools are uint8
+    [.][S or M][page_bytes].
     """
     num_sources = len(src_pools)
+    offs = [0, len(dst_global_pages)] if request_offsets is None else [int(o) for o in request_offsets]
     moved = 0
     for r in range(num_sources):
         a, b = layer_range(num_layers, num_sources, r)
         for layer in range(a, b):
             for i in range(first_uncached, len(dst_global_pages)):
+                q = max(k for k in range(len(offs) - 1) if offs[k] <= i < offs[k + 1])
+                req_pages = dst_global_pages[offs[q]:offs[q + 1]]
                 src = src_pools[r][layer - a, int(src_page_ids[i])].reshape(token_rows, page_size, row_bytes)
                 for x in range(page_size):
-                    d, slot, y = token_place(i * page_size + x, dcp_size, page_size, dst_global_pages)
+                    d, slot, y = token_place((i - offs[q]) * page_size + x, dcp_size, page_size, req_pages)
                     dst = dst_pools[d][layer, slot].reshape(token_rows, page_size, row_bytes)
                     dst[:, y, :] = src[:, x, :]
                     moved += 1

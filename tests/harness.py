@@ -396,16 +396,20 @@ def token_geometry(w: Workload):
     return 2 * w.num_kv_heads, w.head_dim_qk * w.elem_bytes
 
 
-def run_reshard_tokens(rc: ReshardCase, bad=None, src_ids=None, dst_ids=None, stream=None):
+def run_reshard_tokens(rc: ReshardCase, bad=None, src_ids=None, dst_ids=None, request_offsets=None, stream=None):
+    """kv_reshard_tokens over the case's lists; request_offsets (host ints, B + 1) splits them into
+    requests, None passes one request."""
     w = rc.w
     dev = rc.src_pools[0].device
     si = torch.from_numpy((rc.src_ids if src_ids is None else src_ids).astype(np.int32)).to(dev)
     di = torch.from_numpy((rc.dst_ids if dst_ids is None else dst_ids).astype(np.int64)).to(dev)
+    ro = (torch.tensor(np.asarray(request_offsets, dtype=np.int64), device=dev)
+          if request_offsets is not None else None)
     R, rb = token_geometry(w)
     K.kv_reshard_tokens(num_layers=rc.num_layers, dcp_size=w.dcp_size, page_size=w.page_size, token_rows=R,
                         row_bytes=rb, src_pages=rc.src_pages, dst_pages=w.pool_pages, src_pools=rc.src_pools,
                         dst_pools=rc.dst_pools, src_page_ids=si, dst_global_pages=di,
-                        first_uncached=rc.first_uncached, bad_entries=bad, stream=stream)
+                        first_uncached=rc.first_uncached, request_offsets=ro, bad_entries=bad, stream=stream)
     return si, di
 
 

@@ -27,7 +27,17 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTED)
-    assert K.dcpkv_abi_version() == 4
+    assert K.dcpkv_abi_version() == 5 == L.ABI_VERSION
+
+
+def test_graft_build_entry_accepts_the_built_library(monkeypatch):
+    """build() compiles and then checks the library's ABI; with the compile step stubbed the
+    check runs against the library already built."""
+    import __graft_entry__ as G
+    from context_paged_kv_amd import build as B
+
+    monkeypatch.setattr(B, "build", lambda *a, **k: None)
+    G.build()
 
 
 @pytest.mark.parametrize("L_,n", [(78, 8), (64, 4), (4, 4), (17, 5), (1, 1), (100, 7)])
@@ -177,13 +187,17 @@ def test_token_reshard_rejects_bad_arguments_on_host():
     p = (C.c_void_p * 4)(256, 256, 256, 256)
     v = C.c_void_p(256)
     E = L.DCPKV_EINVAL
+    call = L._lib.kv_reshard_tokens
     bad_rows = L.kv_token_reshard_desc(1, 2, 2, 64, 2, 72, 8, 8)     # row_bytes not a multiple of 16
-    assert L._lib.kv_reshard_tokens(C.byref(bad_rows), p, p, v, v, 4, 0, None, None) == E
+    assert call(C.byref(bad_rows), p, p, v, v, 4, None, 1, 0, None, None) == E
     few_layers = L.kv_token_reshard_desc(2, 1, 2, 64, 1, 576, 8, 8)  # fewer layers than sources
-    assert L._lib.kv_reshard_tokens(C.byref(few_layers), p, p, v, v, 4, 0, None, None) == E
+    assert call(C.byref(few_layers), p, p, v, v, 4, None, 1, 0, None, None) == E
     good = L.kv_token_reshard_desc(1, 2, 2, 64, 1, 576, 8, 8)
-    assert L._lib.kv_reshard_tokens(C.byref(good), p, p, v, v, 4, 5, None, None) == E  # first_uncached
-    assert L._lib.kv_reshard_tokens(C.byref(good), p, p, None, None, 4, 0, None, None) == E
-    assert L._lib.kv_reshard_tokens(C.byref(good), p, p, None, None, 4, 4, None, None) == 0  # nothing to move
+    assert call(C.byref(good), p, p, v, v, 4, None, 1, 5, None, None) == E  # first_uncached
+    assert call(C.byref(good), p, p, None, None, 4, None, 1, 0, None, None) == E
+    assert call(C.byref(good), p, p, None, None, 4, None, 1, 4, None, None) == 0  # nothing to move
+    assert call(C.byref(good), p, p, v, v, 4, None, 2, 0, None, None) == E  # two requests, no offsets
+    assert call(C.byref(good), p, p, v, v, 4, v, 0, 0, None, None) == E     # offsets, no request
+    assert call(C.byref(good), p, p, v, v, 4, None, -1, 0, None, None) == E
     mis = (C.c_void_p * 2)(264, 256)
-    assert L._lib.kv_reshard_tokens(C.byref(good), mis, p, v, v, 4, 0, None, None) == E
+    assert call(C.byref(good), mis, p, v, v, 4, None, 1, 0, None, None) == E

@@ -418,6 +418,54 @@ def test_reshard_tokens_vs_oracle(name, n, cached):
         assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
 
 
+@pytest.mark.parametrize("name,n,cached", [("gqa_bf16_16x4k-32k", 4, 3), ("reshard_mla_128k", 8, 0),
+                                           ("tiny_fp32", 3, 1)])
+def test_reshard_tokens_batch_vs_oracle(name, n, cached):
+    """Several requests in one launch, delimited by offsets: each request's tokens restart at
+    position 0 and land in its own virtual pages (the MLA case: 576-byte rows over N = 8, the
+    pools' scales not passed).  Bit for bit against the oracle."""
+    base = get_workload(name)
+    ps = base.page_size
+    lens = (ps * 9 + 5, ps * 2, 3, ps * 13 + 1)
+    w = scaled(base, seed=base.seed + 130, seq_segments=tuple((1, t, t) for t in lens), num_layers=3,
+               num_sources=2, pool_pages=32, dcp_size=n)
+    H.log(f"token reshard batch {name} N={n} cached={cached}")
+    rc = H.make_reshard_case(w, DEV, seq_lens=lens, first_uncached=cached)
+    offs = np.cumsum([0] + [-(-t // ps) for t in lens])
+    assert offs[-1] == len(rc.dst_ids)
+    dst_host = _host_pools(rc.dst_pools)
+    R, rb = H.token_geometry(w)
+    O.reshard_tokens(_host_pools(rc.src_pools), dst_host, 3, n, ps, R, rb, rc.src_ids, rc.dst_ids, cached,
+                     request_offsets=offs)
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.run_reshard_tokens(rc, bad=bad, request_offsets=offs)
+    _sync()
+    assert int(bad.item()) == 0
+    for d in range(n):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
+def test_reshard_tokens_bad_request_offsets_skipped_and_counted():
+    """Entries that no request of the offsets contains (a last offset past the list, a negative
+    first offset) are skipped and counted once per layer; the rest move as for a good split."""
+    base = get_workload("gqa_bf16_16x4k-32k")
+    lens = (64 * 5 + 3, 64 * 4)
+    w = scaled(base, seed=base.seed + 131, seq_segments=tuple((1, t, t) for t in lens), num_layers=2,
+               num_sources=1, pool_pages=8, dcp_size=4)
+    R, rb = H.token_geometry(w)
+    for offs, keep in (([0, 6, 14], slice(0, 6)), ([-1, 6, 10], slice(6, 10))):
+        rc = H.make_reshard_case(w, DEV, seq_lens=lens, first_uncached=0)
+        dst_host = _host_pools(rc.dst_pools)
+        bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+        H.run_reshard_tokens(rc, bad=bad, request_offsets=offs)
+        _sync()
+        assert int(bad.item()) == 2 * (10 - (keep.stop - keep.start))
+        O.reshard_tokens(_host_pools(rc.src_pools), dst_host, 2, 4, w.page_size, R, rb, rc.src_ids[keep],
+                         rc.dst_ids[keep], 0)
+        for d in range(4):
+            assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
+
+
 def test_reshard_tokens_bad_pages_skipped_and_counted():
     base = get_workload("gqa_bf16_16x4k-32k")
     w = scaled(base, seed=base.seed + 121, seq_segments=((1, 64 * 9, 64 * 9),), num_layers=2, num_sources=1,

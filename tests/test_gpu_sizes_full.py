@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import context_paged_kv_amd as K
 from tests import harness as H
 from workloads.configs import get_workload
 
@@ -48,6 +49,38 @@ def test_full_mla_fp8_48x100k():
     assert torch.isfinite(outs.out).all()
     worst = H.check_decode(case, outs, requests=[0, 47], heads=[0, 77, 127])
     H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
+def test_full_gqa_token_ownership_reshard_then_decode():
+    """The token-ownership step the bench times: all 16 requests scattered from the source in one
+    launch (offsets per request), then decode under token ownership; sampled rows of every shard
+    and the merged output against the oracle's attention over the source pages."""
+    w = get_workload("gqa_bf16_16x4k-32k")
+    H.log("full token ownership: gqa bf16 16 x U[4K,32K], N=4, token reshard then decode")
+    sl = np.asarray(H.gen.draw_seq_lens(w))
+    case = H.make_decode_case(w, DEV, seq_lens=sl, own=K.OWN_TOKEN)
+    rc = H.make_reshard_case(w, DEV, seq_lens=sl, first_uncached=0, dst_pools=case.pools, dst_scales=case.scales)
+    offs = np.cumsum([0] + [len(p) for p in case.pages])
+    bad = torch.zeros(1, dtype=torch.int32, device=DEV)
+    H.run_reshard_tokens(rc, bad=bad, request_offsets=offs)
+    torch.cuda.synchronize()
+    assert int(bad.item()) == 0
+    outs = H.run_decode(case)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs.out).all()
+    tol_o, tol_l = H.tolerance(w)
+    heads = [0, 13, 31]
+    for b in (0, 7, 15):
+        sids = torch.from_numpy(rc.src_ids[offs[b]:offs[b + 1]]).to(DEV)
+        kv = H.oracle_logical_kv(w, rc.src_pools[0][0].index_select(0, sids).cpu().numpy(), None, int(sl[b]))
+        (po, pl), (uo, ul) = H.oracle_request(case, b, heads=heads, kv=kv)
+        for d in range(w.dcp_size):
+            H.check_rows(f"partial d={d} b={b}", outs.partial_out[d, b][:, heads].cpu().numpy(),
+                         outs.partial_lse[d, b][:, heads].cpu().numpy(), po[d][:, heads], pl[d][:, heads],
+                         tol_o, tol_l)
+        H.check_rows(f"merged b={b}", outs.out[b][:, heads].cpu().numpy(), outs.lse[b][:, heads].cpu().numpy(),
+                     uo[:, heads], ul[:, heads], tol_o, tol_l)
+    H.log("  sampled rows match")
 
 
 @pytest.mark.timeout(400)

@@ -370,6 +370,47 @@ def test_reshard_tokens_pull_view(n, cached, T):
                             assert row[:24].view(np.int32).tolist() == want
 
 
+@pytest.mark.parametrize("n,cached,lens", [(4, 0, (70, 9, 33)), (3, 5, (20, 64, 1)), (2, 0, (8, 8))])
+def test_reshard_tokens_pull_view_batch(n, cached, lens):
+    """Several requests in one list, delimited by offsets: each request's tokens restart at
+    position 0 and land in its own virtual pages; rows are checked from their tags as above."""
+    L, ncp, psz, R, rb, M = 3, 2, 8, 1, 32, 24
+    rng = np.random.default_rng(90 + n)
+    pm = O.PageMap(n, psz, M, rng.permutation(M))
+    reqs = [pm.alloc(T) for T in lens]
+    offs = np.cumsum([0] + [len(g) for g in reqs])
+    g_all = np.concatenate(reqs)
+    P = len(g_all)
+    S = P + 2
+    src = rng.permutation(S)[:P]
+    srcp = _token_tagged_sources(L, ncp, S, R, psz, rb)
+    dst = [np.full((L, M, R * psz * rb), 0xA5, dtype=np.uint8) for _ in range(n)]
+    moved = O.reshard_tokens(srcp, dst, L, n, psz, R, rb, src, g_all, cached, request_offsets=offs)
+    assert moved == L * (P - cached) * psz
+    owner_slot = {}  # slot -> (request, virtual page)
+    for q, g in enumerate(reqs):
+        for j in range(-(-len(g) // n)):
+            owner_slot[O.dcp_local_slot(int(g[j * n]), n)] = (q, j)
+    for d in range(n):
+        for layer in range(L):
+            owner = next(r for r in range(ncp) if O.layer_range(L, ncp, r)[0] <= layer < O.layer_range(L, ncp, r)[1])
+            for s_ in range(M):
+                page = dst[d][layer, s_].reshape(R, psz, rb)
+                for y in range(psz):
+                    row = page[0, y]
+                    if s_ not in owner_slot:
+                        assert (row == 0xA5).all()
+                        continue
+                    q, j = owner_slot[s_]
+                    t = (j * psz + y) * n + d
+                    e = offs[q] + t // psz  # list entry of the token's source page
+                    if t // psz >= len(reqs[q]) or e < cached:
+                        assert (row == 0xA5).all()
+                    else:
+                        want = [owner, layer - O.layer_range(L, ncp, owner)[0], int(src[e]), 0, t % psz, 0x70C]
+                        assert row[:24].view(np.int32).tolist() == want
+
+
 def test_reshard_tokens_one_shard_is_the_page_reshard():
     """With N = 1 token and page ownership coincide: the token reshard writes what the page
     reshard writes."""
