@@ -145,6 +145,56 @@ def test_decode_edge_lengths(name):
             assert (outs.partial_out[d, b] == 0).all()
 
 
+@pytest.mark.parametrize("name,force_generic", [("tiny_fp32", False), ("gqa_bf16_16x4k-32k", False),
+                                                 ("gqa_bf16_16x4k-32k", True), ("mla_fp8_48x100k", False)])
+def test_decode_out_of_range_table_entries(name, force_generic, monkeypatch):
+    """A block-table entry outside [0, M) is a page of no tokens: the shard's partial leaves out
+    exactly that page's tokens (first, middle and last local pages; negative and too-large
+    entries), and the merge combines what is left."""
+    base = get_workload(name)
+    ps = base.page_size
+    w = scaled(base, seed=base.seed + 210, seq_segments=((1, ps * 9 + 3, ps * 9 + 3), (1, ps * 14, ps * 14),
+                                                        (1, ps * 5 + 1, ps * 5 + 1)), pool_pages=64, q_len=2,
+               num_layers=1, attn_layer=0)
+    n = w.dcp_size
+    case = H.make_decode_case(w, DEV)
+    tables = case.tables.copy()
+    holes = {0: [(1 % n, 0, -1)], 1: [(2 % n, 1, w.pool_pages), (0, 0, -7)], 2: [(0, -(-6 // n) - 1, 1 << 30)]}
+    for b, hs in holes.items():
+        for d, j, v in hs:
+            assert j < -(-(-(-int(case.seq_lens[b]) // ps) - d) // n)  # a page the shard holds
+            tables[d, b, j] = v
+    case.bt_dev.copy_(torch.from_numpy(tables))
+    if force_generic:
+        monkeypatch.setenv("DCPKV_FORCE_GENERIC", "1")
+    outs = H.run_decode(case)
+    _sync()
+    tol_o, tol_l = H.tolerance(w)
+    heads = list(range(min(w.num_q_heads, 8)))
+    for b in range(w.num_requests):
+        T = int(case.seq_lens[b])
+        pb, psc = H.gather_request_pages(case.pools, case.scales, case.pages[b], n, case.layer)
+        k, v = H.oracle_logical_kv(w, pb, psc, T)
+        q = H.q_host(case, b)
+        po, pl = [], []
+        for d in range(n):
+            mask = O.shard_token_mask(case.pages[b], ps, T, n, d)
+            for dd, j, _ in holes.get(b, []):
+                if dd == d:  # local page j of shard d is sequence page j*N + d
+                    mask[(j * n + d) * ps:min(T, (j * n + d + 1) * ps)] = False
+            o_, l_ = O.request_attention(q, k, v, T, w.softmax_scale, mask, heads)
+            po.append(o_)
+            pl.append(l_)
+        po, pl = np.stack(po), np.stack(pl)
+        uo, ul = O.lse_merge(po, pl)
+        for d in range(n):
+            H.check_rows(f"partial d={d} b={b}", outs.partial_out[d, b][:, heads].cpu().numpy(),
+                         outs.partial_lse[d, b][:, heads].cpu().numpy(), po[d][:, heads], pl[d][:, heads],
+                         tol_o, tol_l)
+        H.check_rows(f"merged b={b}", outs.out[b][:, heads].cpu().numpy(), outs.lse[b][:, heads].cpu().numpy(),
+                     uo[:, heads], ul[:, heads], tol_o, tol_l)
+
+
 def test_decode_shard_subset_calls():
     # partials computed one shard range at a time equal the all-shard call
     base = get_workload("gqa_bf16_16x4k-32k")
