@@ -80,10 +80,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
       pp.k = k;
       pp.n_local = nl;
       p.pairs[i] = pp;
+      for (int c = 0; c < k; ++c) {
+        int jb, je;
+        chunk_range(pp, c, jb, je);
+        p.chunks[pp.chunk_begin + c] = ChunkPlan{i, jb, je, kw ? pp.ws_begin + c : -1};
+      }
     }
     carry_k += __shfl(sk, 63, 64);
     carry_w += __shfl(sw, 63, 64);
   }
+  for (int64_t c = carry_k + lane; c < p.max_chunks; c += 64) p.chunks[c] = ChunkPlan{-1, 0, 0, -1};
   if (lane == 0) {
     p.hdr->total_chunks = carry_k;
     p.hdr->ws_chunks = carry_w;
@@ -153,9 +159,9 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
   const int rg_rows = p.group * p.q_len;  // rows sharing one KV head
 
   for (int w = blockIdx.x; w < total; w += gridDim.x) {
-    int pair, chunk, hb;
-    decode_item(p, w, pair, chunk, hb);
-    const PairPlan pp = p.pairs[pair];
+    const int hb = w % p.hb_count;
+    const ChunkPlan cp = load_chunk(p, w / p.hb_count);  // w < total: a planned chunk
+    const int pair = cp.pair;
     const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
     const int hk = hb / p.rb_per_head;
     const int r0 = (hb % p.rb_per_head) * RB;
@@ -179,10 +185,8 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) acc[k] = 0.f;
 
-    int j_begin, j_end;
-    chunk_range(pp, chunk, j_begin, j_end);
     const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
-    for (int jj = j_begin; jj < j_end; ++jj) {
+    for (int jj = cp.j_begin; jj < cp.j_end; ++jj) {
       const int32_t slot = bt[jj];
       if (slot < 0 || slot >= p.pages_per_layer) continue;
       const uint8_t* page =
@@ -276,9 +280,9 @@ __global__ __launch_bounds__(kGenThreads) void partial_generic_kernel(AttnParams
     }
     __syncthreads();
     // write the (chunk) partial
-    const bool direct = pp.k == 1;
+    const bool direct = cp.out < 0;
     const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
-    const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
+    const int64_t ws_row0 = direct ? 0 : (int64_t)cp.out * p.rows;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const int idx = tid + k * kGenThreads;
@@ -398,7 +402,7 @@ struct Geometry {
   int kind;          // KernelKind
   int rb_rows, rb_per_head, hb_count, rows, chunk_pages;
   int64_t ws_cap;
-  size_t hdr_off, pairs_off, o_off, lse_off, bytes;
+  size_t hdr_off, pairs_off, chunks_off, o_off, lse_off, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -424,7 +428,9 @@ static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus,
   const int64_t pairs = (int64_t)D.dcp_size * D.batch;
   g.hdr_off = 0;
   g.pairs_off = align256(sizeof(PlanHeader));
-  g.o_off = align256(g.pairs_off + (size_t)pairs * sizeof(PairPlan));
+  g.chunks_off = align256(g.pairs_off + (size_t)pairs * sizeof(PairPlan));
+  // chunk plans: as many as the grid of any shard range covers (pairs + local pages / C + 1)
+  g.o_off = align256(g.chunks_off + (size_t)(pairs + est_pages / c + 1) * sizeof(ChunkPlan));
   g.lse_off = align256(g.o_off + (size_t)g.ws_cap * g.rows * D.head_dim_v * sizeof(float));
   g.bytes = align256(g.lse_off + (size_t)g.ws_cap * g.rows * sizeof(float));
 }
@@ -481,6 +487,7 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   p.partial_lse = partial_lse;
   p.hdr = reinterpret_cast<PlanHeader*>(ws + g.hdr_off);
   p.pairs = reinterpret_cast<PairPlan*>(ws + g.pairs_off);
+  p.chunks = reinterpret_cast<ChunkPlan*>(ws + g.chunks_off);
   p.ws_o = reinterpret_cast<float*>(ws + g.o_off);
   p.ws_lse = reinterpret_cast<float*>(ws + g.lse_off);
   p.ws_cap = g.ws_cap;

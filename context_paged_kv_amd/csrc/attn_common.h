@@ -31,6 +31,15 @@ struct PairPlan {
   int32_t n_local;      // local pages of this pair
 };
 
+// One chunk of the split, written by the planner so that a work item finds its pair, its
+// pages and its output with a single 16-byte load.  pair < 0 past the planned chunks.
+struct alignas(16) ChunkPlan {
+  int32_t pair;     // pair index (shard - shard_begin) * batch + request
+  int32_t j_begin;  // local pages [j_begin, j_end) of the pair
+  int32_t j_end;
+  int32_t out;      // -1: the partial goes straight to partial_out; else its workspace slot
+};
+
 struct PlanHeader {
   int32_t total_chunks;
   int32_t ws_chunks;
@@ -48,6 +57,7 @@ struct AttnParams {
   float* partial_lse;
   PlanHeader* hdr;
   PairPlan* pairs;
+  ChunkPlan* chunks;        // [max_chunks]
   float* ws_o;
   float* ws_lse;
   int64_t ws_cap;           // chunk partial slots in the workspace
@@ -221,21 +231,10 @@ __device__ __forceinline__ void chunk_range(const PairPlan& pp, int chunk, int& 
   end = begin + base + (chunk < extra ? 1 : 0);
 }
 
-// Decode item w into its pair, chunk and head block.
-__device__ __forceinline__ void decode_item(const AttnParams& p, int w, int& pair, int& chunk,
-                                            int& hb) {
-  const int gc = w / p.hb_count;
-  hb = w - gc * p.hb_count;
-  int lo = 0, hi = p.shard_count * p.batch - 1;
-  while (lo < hi) {  // last pair with chunk_begin <= gc
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.pairs[mid].chunk_begin <= gc)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  pair = lo;
-  chunk = gc - p.pairs[lo].chunk_begin;
+// Plan of chunk gc (pair < 0 when the planner made fewer chunks).
+__device__ __forceinline__ ChunkPlan load_chunk(const AttnParams& p, int64_t gc) {
+  if (gc >= p.max_chunks) return ChunkPlan{-1, 0, 0, -1};
+  return p.chunks[gc];
 }
 
 // Value of an OCP e4m3fn code (bias 7) computed exactly: the code's exponent

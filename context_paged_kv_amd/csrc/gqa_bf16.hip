@@ -79,19 +79,19 @@ __device__ __forceinline__ void load_page(const uint8_t* kb, const uint8_t* vb, 
     vr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + (16 * g + i) * kGqaRow + 16 * c));
 }
 
-__global__ __launch_bounds__(256) void gqa_bf16_kernel(AttnParams p) {
-  __shared__ GqaWaveLds s_lds[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One wavefront per workgroup: four fit a CU (34 KB of LDS each), and each one's LDS is
+// released as soon as it finishes, whatever the length of its neighbours' chunks.
+__global__ __launch_bounds__(64) void gqa_bf16_kernel(AttnParams p) {
+  __shared__ GqaWaveLds s_lds;
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4;  // lane group
   const int c = lane & 15;  // MFMA row/column index within the group
-  const int total = p.hdr->total_chunks * p.hb_count;
-  const int w = blockIdx.x * 4 + wave;
-  if (w >= total) return;
-  GqaWaveLds& L = s_lds[wave];
-
-  int pair, chunk, hb;
-  decode_item(p, w, pair, chunk, hb);
-  const PairPlan pp = p.pairs[pair];
+  const int w = blockIdx.x;
+  const int hb = w % p.hb_count;
+  const ChunkPlan cp = load_chunk(p, w / p.hb_count);
+  if (cp.pair < 0) return;
+  GqaWaveLds& L = s_lds;
+  const int pair = cp.pair;
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int hk = hb;  // one head block per KV head (rows <= 16)
   const int rows = p.group * p.q_len;
@@ -120,8 +120,7 @@ __global__ __launch_bounds__(256) void gqa_bf16_kernel(AttnParams p) {
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int j_begin, j_end;
-  chunk_range(pp, chunk, j_begin, j_end);
+  const int j_begin = cp.j_begin, j_end = cp.j_end;
   const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
   const int64_t head_bytes = (int64_t)kGqaPage * kGqaRow;
   const uint8_t* pool = p.pools[d] + (int64_t)p.layer * p.pages_per_layer * p.page_bytes;
@@ -241,11 +240,11 @@ __global__ __launch_bounds__(256) void gqa_bf16_kernel(AttnParams p) {
 
   // ---- write the (chunk) partial of row c
   if (c < rows) {
-    const bool direct = pp.k == 1;
+    const bool direct = cp.out < 0;
     const int t = c / p.group, h = hk * p.group + (c % p.group);
     const int64_t row = (int64_t)t * p.hq + h;
     const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
-    const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
+    const int64_t ws_row0 = direct ? 0 : (int64_t)cp.out * p.rows;
     float* dst = direct ? p.partial_out + (pair_row0 + row) * kGqaD : p.ws_o + (ws_row0 + row) * kGqaD;
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
@@ -271,9 +270,9 @@ bool gqa_bf16_supported(const dcp_attn_desc& D) {
 
 int launch_gqa_bf16(const AttnParams& p, const dcp_attn_desc& D, int64_t item_bound, hipStream_t st) {
   (void)D;
-  const int64_t blocks = std::max<int64_t>(1, (item_bound + 3) / 4);
-  if (blocks > INT32_MAX / 256) return set_error(DCPKV_EINVAL, "attn: too many work items");
-  hipLaunchKernelGGL(gqa_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, st, p);
+  const int64_t blocks = std::max<int64_t>(1, item_bound);
+  if (blocks > INT32_MAX) return set_error(DCPKV_EINVAL, "attn: too many work items");
+  hipLaunchKernelGGL(gqa_bf16_kernel, dim3((unsigned)blocks), dim3(64), 0, st, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: gqa launch: %s", hipGetErrorString(e));
   return DCPKV_OK;

@@ -203,21 +203,9 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   const int blk = blockIdx.x;
   const int gc = (blk / (8 * hbc)) * 8 + (blk & 7);
   const int hb = (blk >> 3) % hbc;
-  if (gc >= p.hdr->total_chunks) return;
-  int pair = 0;
-  {
-    int lo = 0, hi = p.shard_count * p.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (p.pairs[mid].chunk_begin <= gc)
-        lo = mid;
-      else
-        hi = mid - 1;
-    }
-    pair = lo;
-  }
-  const PairPlan pp = p.pairs[pair];
-  const int chunk = gc - pp.chunk_begin;
+  const ChunkPlan chk = load_chunk(p, gc);
+  if (chk.pair < 0) return;
+  const int pair = chk.pair;
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int T = p.seq_lens[b];
 
@@ -300,8 +288,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
 #pragma unroll
     for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int j_begin, j_end;
-  chunk_range(pp, chunk, j_begin, j_end);
+  const int j_begin = chk.j_begin, j_end = chk.j_end;
   const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
   const uint8_t* pool = p.pools[d] + (int64_t)p.layer * p.pages_per_layer * p.page_bytes;
   const uint16_t* scl = p.scales[d] + (int64_t)p.layer * p.pages_per_layer;
@@ -535,9 +522,9 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   const float lh = mgrp4_sum(l_s);
   if (g == 0) s_l[th][16 * rt + c] = lh;
   __syncthreads();
-  const bool direct = pp.k == 1;
+  const bool direct = chk.out < 0;
   const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
-  const int64_t ws_row0 = direct ? 0 : ((int64_t)pp.ws_begin + chunk) * p.rows;
+  const int64_t ws_row0 = direct ? 0 : (int64_t)chk.out * p.rows;
 #pragma unroll
   for (int nt = 0; nt < kRowTiles; ++nt) {
     const int r = hb * kMlaRowsPerBlock + 16 * nt + c;
