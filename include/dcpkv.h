@@ -316,7 +316,10 @@ typedef struct {
 
 /* Workspace bytes dcp_decode_partial needs for this batch.  total_tokens is
  * the sum of the batch's sequence lengths (a host-side figure that sizes the
- * split of long sequences into chunks).  Returns 0 on a bad descriptor. */
+ * split of long sequences into chunks; pass the same figure to
+ * dcp_decode_partial).  A figure below the true sum only makes the split
+ * coarser, down to one chunk per (shard, request); results do not depend on it.
+ * Returns 0 on a bad descriptor. */
 DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t total_tokens);
 
 /* For shards d in [shard_begin, shard_begin + shard_count), every request b,

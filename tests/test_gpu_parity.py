@@ -195,6 +195,30 @@ def test_decode_out_of_range_table_entries(name, force_generic, monkeypatch):
                      uo[:, heads], ul[:, heads], tol_o, tol_l)
 
 
+@pytest.mark.parametrize("name", ["tiny_fp32", "gqa_bf16_16x4k-32k", "mla_fp8_48x100k"])
+@pytest.mark.parametrize("tokens_hint", ["one", "tenfold"])
+def test_decode_split_does_not_change_results(name, tokens_hint):
+    """total_tokens only sizes the split: far too small a figure forces one chunk per (shard,
+    request) (the workspace cannot hold a split: the planner's fallback), far too large a one
+    longer chunks; both give the oracle's partials and merge."""
+    base = get_workload(name)
+    ps = base.page_size
+    w = scaled(base, seed=base.seed + 220, seq_segments=((2, ps * 40 + 5, ps * 90), (2, 3, ps * 3)),
+               pool_pages=256, num_layers=1, attn_layer=0)
+    case = H.make_decode_case(w, DEV)
+    hint = 1 if tokens_hint == "one" else 10 * case.total_tokens
+    desc = H.attn_desc(case)
+    ws = torch.empty(K.dcp_decode_partial_workspace(desc, hint), dtype=torch.uint8, device=DEV)
+    outs, _ = H.alloc_outputs(case)
+    K.dcp_decode_partial(desc, q=case.q, kv_pools=case.pools, kv_scales=case.scales, block_tables=case.bt_dev,
+                         seq_lens=case.sl_dev, total_tokens=hint, partial_out=outs.partial_out,
+                         partial_lse=outs.partial_lse, workspace=ws)
+    rows = w.num_requests * w.q_len * w.num_q_heads
+    K.dcp_lse_merge(w.dcp_size, rows, w.head_dim_v, outs.partial_out, outs.partial_lse, outs.out, outs.lse)
+    _sync()
+    H.check_decode(case, outs, heads=list(range(min(w.num_q_heads, 16))))
+
+
 def test_decode_shard_subset_calls():
     # partials computed one shard range at a time equal the all-shard call
     base = get_workload("gqa_bf16_16x4k-32k")
