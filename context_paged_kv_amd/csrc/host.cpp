@@ -146,13 +146,30 @@ extern "C" int dcp_pagemap_alloc(dcp_pagemap* pm, int64_t num_tokens, int64_t* o
 extern "C" int dcp_pagemap_release(dcp_pagemap* pm, const int64_t* global_pages, int64_t n) {
   if (!pm || (n > 0 && !global_pages) || n < 0)
     return set_error(DCPKV_EINVAL, "pagemap_release: bad arguments");
-  std::vector<int64_t> vs;
-  for (int64_t i = 0; i < n; ++i) {
-    const int64_t g = global_pages[i];
-    if (g < 0 || g >= pm->m * pm->n)
-      return set_error(DCPKV_EINVAL, "pagemap_release: page %lld out of range", (long long)g);
-    const int64_t v = g / pm->n;
-    if (std::find(vs.begin(), vs.end(), v) == vs.end()) vs.push_back(v);
+  std::vector<int64_t> vs;  // the distinct virtual pages, in first-seen order (that order is appended)
+  try {
+    vs.reserve((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t g = global_pages[i];
+      if (g < 0 || g >= pm->m * pm->n)
+        return set_error(DCPKV_EINVAL, "pagemap_release: page %lld out of range", (long long)g);
+      vs.push_back(g / pm->n);
+    }
+    std::vector<int64_t> sorted = vs;
+    std::sort(sorted.begin(), sorted.end());
+    sorted.erase(std::unique(sorted.begin(), sorted.end()), sorted.end());
+    std::vector<uint8_t> taken(sorted.size(), 0);
+    size_t k = 0;
+    for (size_t i = 0; i < vs.size(); ++i) {  // keep the first occurrence of each, in list order
+      const size_t at = (size_t)(std::lower_bound(sorted.begin(), sorted.end(), vs[i]) - sorted.begin());
+      if (!taken[at]) {
+        taken[at] = 1;
+        vs[k++] = vs[i];
+      }
+    }
+    vs.resize(k);
+  } catch (const std::bad_alloc&) {
+    return set_error(DCPKV_ENOMEM, "pagemap_release: out of host memory");
   }
   for (int64_t v : vs)
     if (!pm->used[(size_t)v])

@@ -76,8 +76,9 @@ def test_pagemap_matches_oracle(n, page, M):
     for step in range(60):
         if live and rng.random() < 0.35:
             g = live.pop(int(rng.integers(len(live))))
-            pm.release(g)
-            om.release(list(g))
+            rel = [int(x) for x in rng.permutation(np.asarray(g))] + [int(x) for x in g[:2]]  # shuffled, repeats
+            pm.release(rel)
+            om.release(rel)
         else:
             T = int(rng.integers(1, page * n * 6))
             try:
