@@ -363,6 +363,22 @@ def plain_copy_gbps(torch, dev, nbytes: int, reps: int = 5) -> float:
     return 2 * n / float(np.median(ts)) / 1e9
 
 
+def mfma_probe_tflops(torch, K, dev, kind: int, iters: int = 4000, reps: int = 3) -> float:
+    """Median TFLOP/s of the library's MFMA rate probe (kind 0: fp16 16x16x32, 1: fp8 16x16x128)."""
+    sink = torch.empty(K.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
+    K.dcpkv_probe_mfma(kind, 100, sink)  # warm-up
+    stream = torch.cuda.current_stream()
+    rates = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        flops = K.dcpkv_probe_mfma(kind, iters, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rates.append(flops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return float(np.median(rates))
+
+
 # kernels of each timed call, as rocprofv3 names them
 CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",), "reshard_tokens_kernel": ("reshard_tokens_kernel",),
                 "dcp_decode_partial": ("plan_kernel", "gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
@@ -530,6 +546,18 @@ def main():
                       "attn_TFLOPs": round(st.flops_attn() / t_pa.mean() / 1e12, 1),
                       "partial_us": round(t_pa.mean() * 1e6, 2), "merge_us": round(t_mg.mean() * 1e6, 2),
                       "decode_tokens_per_s": round(w.num_requests * w.q_len / t_attn, 1)})
+        if w.layout == "mla":
+            # what this device's matrix cores deliver on back-to-back MFMAs of the two kinds the
+            # kernel issues, and the MFMA time of its instructions at those rates (latent scores:
+            # two fp8 products per score, the query's hi and lo terms; rope and PV: fp16)
+            r16, r8 = mfma_probe_tflops(torch, st.K, dev, 0), mfma_probe_tflops(torch, st.K, dev, 1)
+            pairs = st.flops_attn() / (2.0 * w.num_q_heads * (w.head_dim_qk + w.head_dim_v))
+            f8 = 2.0 * pairs * w.num_q_heads * w.head_dim_v * 2
+            f16 = 2.0 * pairs * w.num_q_heads * ((w.head_dim_qk - w.head_dim_v) + w.head_dim_v)
+            t_mfma = f8 / (r8 * 1e12) + f16 / (r16 * 1e12)
+            parts.update({"mfma_probe_f16_TFLOPs": round(r16, 1), "mfma_probe_fp8_TFLOPs": round(r8, 1),
+                          "partial_mfma_us_at_probe_rates": round(t_mfma * 1e6, 2),
+                          "partial_frac_of_probe_rates": round(t_mfma / t_pa.mean(), 4)})
     # roofline of the dominant call of the step
     if st.has_reshard and (not st.has_attention or t_rs.mean() >= t_pa.mean()):
         dom = "reshard_tokens_kernel" if st.own else "reshard_kernel"

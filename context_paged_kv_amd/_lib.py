@@ -55,7 +55,7 @@ EXPORTED = (
     "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
     "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_path_entries", "kv_pack_pages",
     "kv_unpack_pages", "kv_reshard_tokens",
-    "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge",
+    "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge", "dcpkv_probe_mfma",
 )
 
 
@@ -117,10 +117,11 @@ _lib.dcp_decode_partial_workspace.restype = C.c_size_t
 _lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P,
                                     _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P]
 _lib.dcp_lse_merge.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P]
+_lib.dcpkv_probe_mfma.argtypes = [C.c_int32, C.c_int32, _P, C.c_int64, _I64P, _P]
 for _f in ("cp_layersplit_layer_range", "dcp_filter_kv_indices", "dcp_pagemap_create",
            "dcp_pagemap_alloc", "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
            "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
-           "dcp_decode_partial", "dcp_lse_merge"):
+           "dcp_decode_partial", "dcp_lse_merge", "dcpkv_probe_mfma"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -356,3 +357,13 @@ def dcp_lse_merge(dcp_size: int, rows: int, head_dim_v: int, partial_out, partia
     """Enqueue the exact LSE merge of dcp_size partials (see include/dcpkv.h)."""
     _check(_lib.dcp_lse_merge(dcp_size, rows, head_dim_v, _dptr(partial_out), _dptr(partial_lse), _dptr(out),
                               _dptr(out_lse), _stream(stream)))
+
+
+PROBE_SINK_FLOATS = 1024 * 512
+
+
+def dcpkv_probe_mfma(kind: int, iters: int, sink, stream=None) -> int:
+    """Enqueue the MFMA rate probe (see include/dcpkv.h); returns the launch's flops."""
+    flops = C.c_int64(0)
+    _check(_lib.dcpkv_probe_mfma(kind, iters, _dptr(sink), sink.numel(), C.byref(flops), _stream(stream)))
+    return flops.value

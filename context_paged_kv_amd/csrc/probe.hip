@@ -1,0 +1,90 @@
+// Measurement aid, not on the decode path: the matrix-core rate a kernel of
+// back-to-back independent MFMAs reaches on this device, for the two
+// instruction kinds the fp8 MLA kernel issues.  One workgroup of eight
+// wavefronts per CU (two per SIMD, as in the MLA kernel); its shared-memory
+// request keeps a second workgroup off the CU.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+namespace dcpkv {
+
+typedef _Float16 f16x8p __attribute__((ext_vector_type(8)));
+typedef float f32x4p __attribute__((ext_vector_type(4)));
+typedef int i32x8p __attribute__((ext_vector_type(8)));
+
+constexpr int kProbeThreads = 512;
+constexpr int kProbeChains = 8;  // independent accumulators per wavefront
+constexpr int kProbeMaxGrid = 1024;
+constexpr size_t kProbeLds = 96 * 1024;
+
+template <int KIND>
+__global__ __launch_bounds__(kProbeThreads) void mfma_rate_kernel(int iters, float* sink) {
+  extern __shared__ float probe_lds[];
+  const int lane = threadIdx.x & 63;
+  f32x4p acc[kProbeChains];
+#pragma unroll
+  for (int u = 0; u < kProbeChains; ++u) acc[u] = f32x4p{0.f, 0.f, 0.f, 0.f};
+  if (KIND == 0) {
+    f16x8p a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = (_Float16)(0.001f * (lane + i));
+      b[i] = (_Float16)(0.002f * (lane - i));
+    }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int u = 0; u < kProbeChains; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[u], 0, 0, 0);
+  } else {
+    i32x8p a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[i] = 0x30303030 + lane + i;  // small e4m3 codes
+      b[i] = 0x28282828 + lane - i;
+    }
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int u = 0; u < kProbeChains; ++u)
+        acc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[u], 0, 0, 0, 127, 0, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < kProbeChains; ++u) s += acc[u][0] + acc[u][1] + acc[u][2] + acc[u][3];
+  if (iters < 0) probe_lds[threadIdx.x] = s;  // never taken; keeps the request meaningful
+  sink[(size_t)blockIdx.x * kProbeThreads + threadIdx.x] = s;
+}
+
+}  // namespace dcpkv
+
+using namespace dcpkv;
+
+extern "C" int dcpkv_probe_mfma(int32_t kind, int32_t iters, float* sink, int64_t sink_floats, int64_t* out_flops,
+                                void* stream) {
+  if ((kind != 0 && kind != 1) || iters < 1 || !sink || !out_flops)
+    return set_error(DCPKV_EINVAL, "probe_mfma: bad arguments (kind %d, iters %d)", kind, iters);
+  if (sink_floats < (int64_t)kProbeMaxGrid * kProbeThreads)
+    return set_error(DCPKV_EINVAL, "probe_mfma: sink holds %lld floats, needs %d", (long long)sink_floats,
+                     kProbeMaxGrid * kProbeThreads);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return set_error(DCPKV_EDEVICE, "probe_mfma: no device");
+  const int grid = std::min(cus, kProbeMaxGrid);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* fn = kind == 0 ? reinterpret_cast<const void*>(&mfma_rate_kernel<0>)
+                             : reinterpret_cast<const void*>(&mfma_rate_kernel<1>);
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kProbeLds) != hipSuccess)
+    return set_error(DCPKV_EDEVICE, "probe_mfma: cannot request %zu bytes of LDS", kProbeLds);
+  if (kind == 0)
+    hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(grid), dim3(kProbeThreads), kProbeLds, st, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(grid), dim3(kProbeThreads), kProbeLds, st, iters, sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "probe_mfma: launch failed: %s", hipGetErrorString(e));
+  const int64_t per_mfma = kind == 0 ? 2LL * 16 * 16 * 32 : 2LL * 16 * 16 * 128;
+  *out_flops = (int64_t)grid * (kProbeThreads / 64) * (int64_t)iters * kProbeChains * per_mfma;
+  return DCPKV_OK;
+}

@@ -373,6 +373,23 @@ DCPKV_API int dcp_decode_partial(const dcp_attn_desc* desc, const void* q, const
 DCPKV_API int dcp_lse_merge(int32_t dcp_size, int64_t rows, int32_t head_dim_v, const float* partial_out,
                   const float* partial_lse, float* out, float* out_lse, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * (4) Measurement aid (not on the path)                                     *
+ * ------------------------------------------------------------------------ */
+
+/* The matrix-core rate this device reaches on back-to-back independent MFMAs
+ * of one kind, to set the fp8 MLA kernel's time against what the hardware
+ * delivers as well as against its published peak.  kind 0:
+ * v_mfma_f32_16x16x32_f16 (the PV and rope products); kind 1:
+ * v_mfma_scale_f32_16x16x128_f8f6f4 on e4m3 (the latent scores).  One
+ * workgroup of eight wavefronts (two per SIMD) per CU runs `iters` rounds of
+ * eight independent MFMAs each.  sink: device float array of at least
+ * 1024 * 512 entries (caller-owned), written so the work is kept; *out_flops
+ * (host) receives the flops of the launch.  Time it with events on `stream`.
+ * EINVAL on bad arguments or too small a sink; EDEVICE if the launch fails. */
+DCPKV_API int dcpkv_probe_mfma(int32_t kind, int32_t iters, float* sink, int64_t sink_floats, int64_t* out_flops,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

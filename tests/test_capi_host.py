@@ -202,3 +202,14 @@ def test_token_reshard_rejects_bad_arguments_on_host():
     assert call(C.byref(good), p, p, v, v, 4, None, -1, 0, None, None) == E
     mis = (C.c_void_p * 2)(264, 256)
     assert call(C.byref(good), mis, p, v, v, 4, None, 1, 0, None, None) == E
+
+
+def test_probe_rejects_bad_arguments_on_host():
+    v = C.c_void_p(256)
+    flops = C.c_int64(0)
+    E = L.DCPKV_EINVAL
+    assert L._lib.dcpkv_probe_mfma(2, 10, v, L.PROBE_SINK_FLOATS, C.byref(flops), None) == E  # kind
+    assert L._lib.dcpkv_probe_mfma(0, 0, v, L.PROBE_SINK_FLOATS, C.byref(flops), None) == E   # iters
+    assert L._lib.dcpkv_probe_mfma(0, 10, v, L.PROBE_SINK_FLOATS - 1, C.byref(flops), None) == E
+    assert L._lib.dcpkv_probe_mfma(0, 10, None, L.PROBE_SINK_FLOATS, C.byref(flops), None) == E
+    assert L._lib.dcpkv_probe_mfma(1, 10, v, L.PROBE_SINK_FLOATS, None, None) == E

@@ -591,3 +591,27 @@ def test_token_pipeline_reshard_then_decode(q_len):
             H.check_rows(f"partial d={d}", outs.partial_out[d, b].cpu().numpy(), outs.partial_lse[d, b].cpu().numpy(),
                          po[d], pl[d], tol_o, tol_l)
         H.check_rows("merged", outs.out[b].cpu().numpy(), outs.lse[b].cpu().numpy(), uo, ul, tol_o, tol_l)
+
+
+# --------------------------------------------------------------------------- measurement aid
+
+
+@pytest.mark.parametrize("kind,per_mfma", [(0, 2 * 16 * 16 * 32), (1, 2 * 16 * 16 * 128)])
+def test_probe_mfma_counts_its_work(kind, per_mfma):
+    """The MFMA rate probe reports the flops it issues (CUs x 8 wavefronts x iters x 8 MFMAs) and
+    writes finite sums; its rate stays below the published dense peak."""
+    sink = torch.full((K.PROBE_SINK_FLOATS,), float("nan"), dtype=torch.float32, device=DEV)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 500
+    K.dcpkv_probe_mfma(kind, 10, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    flops = K.dcpkv_probe_mfma(kind, iters, sink)
+    e1.record()
+    _sync()
+    grid = min(cus, 1024)
+    assert flops == grid * 8 * iters * 8 * per_mfma
+    assert torch.isfinite(sink[:grid * 512]).all()
+    rate = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    H.log(f"  probe kind {kind}: {rate:.0f} TFLOP/s")
+    assert 0 < rate < (2600 if kind == 0 else 5200)
