@@ -76,14 +76,14 @@ constexpr int kLatSteps = kMlaDv / 128;                // 4 fp8 k-steps of 128 l
 constexpr int kRope0 = kMlaDv;                         // first rope dim
 constexpr int kRopeSteps = (kMlaDim - kMlaDv) / 32;    // 2 f16 k-steps of 32 rope dims
 constexpr int kQWords = kLatSteps * 4 + kRopeSteps;    // 16-byte query loads per lane
-constexpr int kWaveDv = kMlaDv / kWaves;               // 64 value dims per wavefront
-constexpr int kVTiles = kWaveDv / 16;                  // 4 M tiles of 16 dims
+constexpr int kWaveDv = kMlaDv / kRowTiles;            // 128 value dims per accumulating wavefront
+constexpr int kVTiles = kWaveDv / 16;                  // 8 M tiles of 16 dims
 constexpr int kRawStride = 592;                        // LDS bytes per token row of codes
 constexpr int kRawBuf = kMlaPage * kRawStride;         // 37888 bytes per page buffer
 constexpr int kSlotsPerRow = kRawStride / 16;          // 37 16-byte slots (36 data + 1 pad)
 constexpr int kSlots = kMlaPage * kSlotsPerRow;        // 2368
 constexpr int kLoadIters = (kSlots + kThreads - 1) / kThreads;  // copy instructions per wave and page
-constexpr int kEarlyLoads = 3;                         // of them issued between the latent score MFMAs
+constexpr int kPageBufs = 3;                           // page buffers in LDS
 constexpr int kWaitLgkm0 = 0xC07F;                     // s_waitcnt lgkmcnt(0), other counters untouched
 constexpr float kTau = 8.f;                            // lazy-rescale threshold (log2 units)
 constexpr float kLog2eM = 1.4426950408889634f;
@@ -158,6 +158,21 @@ __device__ __forceinline__ int mla_vtok(int g, int k) {
 }
 __device__ __forceinline__ int mla_tok(int tt, int m) { return mla_vtok(m >> 2, 4 * tt + (m & 3)); }
 
+// One LDS DMA piece: 16 bytes per lane from gptr to LDS address m0 + 16 lane (4 bytes per
+// lane for dma4).  Written as asm, so the compiler neither orders LDS reads behind it nor
+// counts it: every wait for these pieces is explicit.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(gptr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // LDS slot q (16 bytes) of a page buffer, row q / 37 and column q % 37, holds
 // page bytes 16 * (q - q / 37) onwards.  Per-lane source offsets of the page copy: load i of wave w moves the 64
 // consecutive 16-byte LDS slots from kThreads * i + 64 * w (none past the page;
@@ -176,6 +191,67 @@ __device__ __forceinline__ CopyPlan copy_plan(int wave, int lane) {
   return cp;
 }
 
+// Largest token x of local page j of shard d at a position <= pos (the 32-bit form of
+// local_limit: positions are below T <= INT32_MAX).
+__device__ __forceinline__ int mla_llim(int pos, int j, int tok_il, int n, int d) {
+  return tok_il ? (pos >= d ? (pos - d) / n : -1) - j * kMlaPage : pos - (j * n + d) * kMlaPage;
+}
+
+// Page copies: global -> LDS by DMA, no registers.  Every wavefront issues kLoadIters
+// requests per page (those with one piece less fetch the page-scale dword instead), so
+// counting requests tells when a page has landed.
+struct MlaCopy {
+  const int32_t* bt;    // the pair's block table, from its first local page of the chunk
+  const uint8_t* pool;  // layer base of the shard's pool
+  const uint16_t* scl;  // layer base of the shard's page scales
+  int64_t page_bytes;
+  uint32_t slots;       // M: entries outside [0, M) are missing pages
+  int np, wave, lane, tid;
+  int wbase;            // block-table entries come in windows of 64 (one per lane), the next
+  int32_t win0, win1;   // window loaded a whole window ahead
+};
+
+__device__ __forceinline__ bool mla_ok(const MlaCopy& m, int32_t sl) { return (uint32_t)sl < m.slots; }
+
+// Page q (local to the chunk, ascending) into buffer q % 3; its entry goes to s_slot.
+__device__ __forceinline__ void mla_fetch(MlaCopy& m, const CopyPlan& cp, int q, uint8_t (*s_raw)[kRawBuf],
+                                          uint32_t (*s_scw)[4], int32_t* s_slot) {
+  if (q - m.wbase == 64) {
+    m.wbase += 64;
+    m.win0 = m.win1;
+    m.win1 = m.wbase + 64 + m.lane < m.np ? m.bt[m.wbase + 64 + m.lane] : -1;
+  }
+  const int32_t sl = __builtin_amdgcn_readlane(m.win0, q - m.wbase);
+  const int bi = q % kPageBufs;
+  const int32_t sl0 = mla_ok(m, sl) ? sl : 0;  // a missing page reads slot 0 (in bounds)
+  const uint8_t* page = m.pool + (int64_t)sl0 * m.page_bytes;
+#pragma unroll
+  for (int i = 0; i < kLoadIters; ++i) {
+    const int base = kThreads * i + 64 * m.wave;
+    if (base < kSlots) {
+      dma16(page + cp.off[i], lds_addr_of(s_raw[bi] + 16 * base));
+    } else if (m.lane == 0) {  // one lane: a dword request writes 4 bytes per active lane
+      const uintptr_t sa = (uintptr_t)(m.scl + sl0);
+      dma4((const void*)(sa & ~(uintptr_t)3), lds_addr_of(&s_scw[bi][m.wave & 3]));
+    }
+  }
+  if (m.tid == 0) s_slot[bi] = sl;
+}
+
+// The bf16 scale of the page in buffer bi (entry sl), out of its dword.
+__device__ __forceinline__ float mla_scale(const MlaCopy& m, int32_t sl, int bi, uint32_t (*s_scw)[4]) {
+  const uint32_t w = s_scw[bi][((kSlots - kThreads * (kLoadIters - 1)) / 64) & 3];
+  const uintptr_t sa = (uintptr_t)(m.scl + (mla_ok(m, sl) ? sl : 0));
+  return fmaxf(bf16_to_float((uint16_t)((sa & 2) ? (w >> 16) : (w & 0xFFFFu))), 1e-30f);
+}
+
+// The reference page scale an accumulator is in units of moves (with a rescale) when a page's
+// ratio to it leaves [1/4, 4].
+__device__ __forceinline__ float mla_next_ref(float ps, float ref) {
+  const float rat = ps * __builtin_amdgcn_rcpf(ref);
+  return (rat > 4.f || rat < 0.25f) ? ps : ref;
+}
+
 // Scale the accumulator tile by f.  The product goes back through an MFMA
 // (adding 0 x 0) so the accumulator keeps one register class across the loop
 // and the common path carries no copies; the empty asm makes the read happen
@@ -187,15 +263,17 @@ __device__ __forceinline__ void scale_acc(f32x4& o, float f) {
 }
 
 __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kRawBuf];  // 75776 B
-  __shared__ f16x8 s_p[kRowTiles][2][64];          // P^T operands by (row tile, token half, lane), 8 KB
-  __shared__ float s_lr[2][kMlaRowsPerBlock];      // the page's exponent offset of each token half
-  __shared__ float s_l[2][kMlaRowsPerBlock];       // denominators of the two token halves
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[kPageBufs][kRawBuf];  // 113664 B
+  __shared__ f16x8 s_p[2][kRowTiles][2][64];  // P^T operands by (step parity, row tile, token half, lane), 16 KB
+  __shared__ float s_off[2][kMlaRowsPerBlock];  // each row's exponent offset for the page, by step parity
+  __shared__ uint32_t s_scw[kPageBufs][4];      // the dword holding each buffer's page scale
+  __shared__ float s_l[kMlaRowsPerBlock];       // final denominators
+  __shared__ int32_t s_slot[kPageBufs];         // block-table entry of the page in each buffer
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   __builtin_assume(wave >= 0 && wave < kWaves);
-  const int rt = wave & (kRowTiles - 1), th = wave / kRowTiles;  // score role
+  const bool scorer = wave < kRowTiles;  // waves 0-3 score row tile `wave`; waves 4-7 accumulate values
   const int g = lane >> 4, c = lane & 15;
 
   // items sharing a chunk run on the same XCD (dispatch is round robin over 8)
@@ -209,343 +287,303 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
   const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
   const int T = p.seq_lens[b];
 
-  // Score role: the lane's query row 16 rt + c of the block.  Latent dims
-  // 128 ks + 32 g + [0, 32) go to the fp8 MFMA as two exact e4m3 terms (hi, lo);
-  // rope dims 512 + 32 ks + 8 g + [0, 8) go to the f16 MFMA.  Both are scaled by
-  // 2^qe (largest |q| of the row in [128, 256)); the factor is taken out of the
-  // scores with the softmax scale.
-  const int r_s = hb * kMlaRowsPerBlock + 16 * rt + c;
-  const bool row_ok = r_s < p.rows;
-  const int lim = row_ok ? T - p.q_len + r_s / p.hq : -1;  // last visible position (below T <= INT32_MAX)
-  i32x8 qhi[kLatSteps], qlo[kLatSteps];
-  f16x8 qrope[kRopeSteps];
-  float sl2;
-  {
-    const int t = row_ok ? r_s / p.hq : 0, h = row_ok ? r_s % p.hq : 0;
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim;
-    u32x4 qraw[kQWords];
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < kQWords; ++i) {
-      const uint16_t* src = i < kLatSteps * 4 ? qr + 128 * (i >> 2) + 32 * g + 8 * (i & 3)
-                                              : qr + kRope0 + 32 * (i - kLatSteps * 4) + 8 * g;
-      const u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
-      qraw[i] = w;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        mx = fmaxf(mx, fmaxf(fabsf(__builtin_bit_cast(float, w[e2] << 16)),
-                             fabsf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u))));
-    }
-    const float am = mgrp4_max(mx);
-    const int qe = am > 0.f ? 7 - ilogbf(am) : 0;
-#pragma unroll
-    for (int ks = 0; ks < kLatSteps; ++ks) {
-      i32x8 hv, lv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {  // 8 dims per u32x4 -> two words of four e4m3 codes
-        const u32x4 w = qraw[4 * ks + j];
-#pragma unroll
-        for (int hw = 0; hw < 2; ++hw) {
-          const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), qe),
-                              ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), qe),
-                              ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), qe),
-                              ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), qe)};
-          uint32_t hw32, lw32;
-          split_e4m3(v, hw32, lw32);
-          hv[2 * j + hw] = (int)hw32;
-          lv[2 * j + hw] = (int)lw32;
-        }
-      }
-      qhi[ks] = hv;
-      qlo[ks] = lv;
-    }
-#pragma unroll
-    for (int ks = 0; ks < kRopeSteps; ++ks) {
-      const u32x4 w = qraw[kLatSteps * 4 + ks];
-      f16x2 h2[4];
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2)
-        h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
-                       (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
-      qrope[ks] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
-                                          __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
-                                          6, 7);
-    }
-    sl2 = p.scale * kLog2eM / ldexpf(1.f, qe);
-  }
-
-  // Exponent offsets (log2 units) of rows 16 nt + c: every wave holds the same
-  // values, updated from the same LDS words.  ref_s is the score row's (= ref[rt]).
-  float ref[kRowTiles];
-#pragma unroll
-  for (int nt = 0; nt < kRowTiles; ++nt) ref[nt] = kNegInf;
-  float ref_s = kNegInf;
-  float l_s = 0.f;     // this lane's share of the score row's denominator over this token half
-  float ps_ref = 1.f;  // the accumulator is in units of ps_ref
-  f32x4 o[kRowTiles][kVTiles];  // O^T tiles: dims 64 w + 16 mt + 4 g + i of row 16 nt + c
-#pragma unroll
-  for (int nt = 0; nt < kRowTiles; ++nt)
-#pragma unroll
-    for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int j_begin = chk.j_begin, j_end = chk.j_end;
+  const int j_begin = chk.j_begin, np = chk.j_end - chk.j_begin;
   const int32_t* bt = p.block_tables + ((int64_t)d * p.batch + b) * p.max_local;
   const uint8_t* pool = p.pools[d] + (int64_t)p.layer * p.pages_per_layer * p.page_bytes;
   const uint16_t* scl = p.scales[d] + (int64_t)p.layer * p.pages_per_layer;
-  // Block-table entries come in windows of 64 (one per lane, the next window loaded a whole
-  // window ahead) and page scales one page ahead, so no dependent load sits between a barrier
-  // and the next page's copies.  Entries outside [0, pages_per_layer) are skipped.
-  const uint32_t slots = (uint32_t)min<int64_t>(p.pages_per_layer, INT32_MAX);
-  auto ok = [&](int32_t sl) { return (uint32_t)sl < slots; };
-  // largest token x of local page j at a position <= pos (local_limit in 32 bits: positions are
-  // below T <= INT32_MAX)
-  auto llim = [&](int pos, int j) {
-    return p.tok_il ? (pos >= d ? (pos - d) / p.n : -1) - j * kMlaPage : pos - (j * p.n + d) * kMlaPage;
-  };
-  int wbase = j_begin;
-  int32_t win0 = j_begin + lane < j_end ? bt[j_begin + lane] : -1;
-  int32_t win1 = j_begin + 64 + lane < j_end ? bt[j_begin + 64 + lane] : -1;
-  int32_t slot_cur = __builtin_amdgcn_readlane(win0, 0);
-  uint16_t sc_cur = 0, sc_nxt = 0;
-  // The page copy goes through registers: the loads of page j + 1 are issued between the
-  // score MFMAs of page j and written to the other LDS buffer between its PV MFMAs.
+  const int tok_il = p.tok_il, nsh = p.n;
+  MlaCopy mc;
+  mc.bt = bt + j_begin;
+  mc.pool = pool;
+  mc.scl = scl;
+  mc.page_bytes = p.page_bytes;
+  mc.slots = (uint32_t)min<int64_t>(p.pages_per_layer, INT32_MAX);
+  mc.np = np;
+  mc.wave = wave;
+  mc.lane = lane;
+  mc.tid = tid;
+  mc.wbase = 0;
+  mc.win0 = lane < np ? mc.bt[lane] : -1;
+  mc.win1 = 64 + lane < np ? mc.bt[64 + lane] : -1;
   const CopyPlan cp = copy_plan(wave, lane);
-  if (j_begin < j_end && ok(slot_cur)) {
-    const uint8_t* page = pool + (int64_t)slot_cur * p.page_bytes;
-    u32x4 stg[kLoadIters];
-#pragma unroll
-    for (int i = 0; i < kLoadIters; ++i)
-      if (kThreads * i + 64 * wave < kSlots)
-        stg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(page + cp.off[i]));
-#pragma unroll
-    for (int i = 0; i < kLoadIters; ++i) {
-      const int base = kThreads * i + 64 * wave;
-      if (base < kSlots) *reinterpret_cast<u32x4*>(s_raw[0] + 16 * (base + lane)) = stg[i];
-    }
-    sc_cur = scl[slot_cur];
+  // Page q + 1 is fetched during step q (three buffers: step q reads pages q - 1 and q).  A
+  // missing page's tokens are all masked; its rows, and those of a page at or past T, are
+  // zeroed before anyone reads them.
+#define MLA_ZERO_TAIL(q)                                                                          \
+  do {                                                                                            \
+    const int32_t zsl = s_slot[(q) % kPageBufs];                                                  \
+    const int valid = mla_ok(mc, zsl) ? min(mla_llim(T - 1, j_begin + (q), tok_il, nsh, d) + 1, kMlaPage) : 0; \
+    if (valid < kMlaPage) {                                                                       \
+      uint8_t* zcur = s_raw[(q) % kPageBufs];                                                     \
+      for (int i = tid; i < (kMlaPage - valid) * 36; i += kThreads) {                             \
+        const int r = valid + i / 36, cc = i - (i / 36) * 36;                                     \
+        *reinterpret_cast<u32x4*>(zcur + r * kRawStride + 16 * cc) = u32x4{0, 0, 0, 0};           \
+      }                                                                                           \
+      __syncthreads();                                                                            \
+    }                                                                                             \
+  } while (0)
+  if (np > 0) {
+    mla_fetch(mc, cp, 0, s_raw, s_scw, s_slot);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    MLA_ZERO_TAIL(0);
   }
-  int buf = 0;
-  for (int jj = j_begin; jj < j_end; ++jj) {
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's copies of page jj (and the prefetched words) have landed
-    __syncthreads();                // ... and everyone's; the other buffer and the exchange area are free
-    if (jj + 1 - wbase == 64) {
-      wbase += 64;
-      win0 = win1;
-      win1 = wbase + 64 + lane < j_end ? bt[wbase + 64 + lane] : -1;
-    }
-    const int32_t slot_nxt = jj + 1 < j_end ? __builtin_amdgcn_readlane(win0, jj + 1 - wbase) : -1;
-    const bool have_nxt = ok(slot_nxt);
-    const uint8_t* npage = pool + (int64_t)(have_nxt ? slot_nxt : 0) * p.page_bytes;
-    uint8_t* nbuf = s_raw[buf ^ 1];
-    u32x4 stg[kLoadIters];  // page j + 1 on its way to the other buffer
-    // No test of have_nxt here: without a next page the loads read slot 0 (in bounds) and the
-    // writes land in the buffer nothing reads before it is filled again; branch-free this way.
-    auto ld = [&](int i) {
-      if (kThreads * i + 64 * wave < kSlots)
-        stg[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(npage + cp.off[i]));
-    };
-    auto st = [&](int i) {
-      const int base = kThreads * i + 64 * wave;
-      if (base < kSlots) *reinterpret_cast<u32x4*>(nbuf + 16 * (base + lane)) = stg[i];
-    };
-    if (have_nxt) sc_nxt = scl[slot_nxt];
-    if (!ok(slot_cur)) {
-#pragma unroll
-      for (int i = 0; i < kLoadIters; ++i) ld(i);
-#pragma unroll
-      for (int i = 0; i < kLoadIters; ++i) st(i);
-    }
-    if (ok(slot_cur)) {
-      // tokens of local page jj before T; no row masks a token of the page when even the
-      // first query position sees all 64
-      const int valid = min(llim(T - 1, jj) + 1, kMlaPage);
-      const bool full = llim(T - p.q_len, jj) >= kMlaPage - 1;
-      const float ps = fmaxf(bf16_to_float(sc_cur), 1e-30f);
-      uint8_t* cur = s_raw[buf];
-      if (valid < kMlaPage) {  // tail of the last page: no code past T reaches a product
-        for (int i = tid; i < (kMlaPage - valid) * 36; i += kThreads) {
-          const int r = valid + i / 36, cc = i - (i / 36) * 36;
-          *reinterpret_cast<u32x4*>(cur + r * kRawStride + 16 * cc) = u32x4{0, 0, 0, 0};
-        }
-        __syncthreads();
-      }
-      // ---- the reference page scale moves (with a rescale) when the ratio leaves [1/4, 4]
-      if (ps * __builtin_amdgcn_rcpf(ps_ref) > 4.f || ps * __builtin_amdgcn_rcpf(ps_ref) < 0.25f) {
-        const float fo = ps_ref * __builtin_amdgcn_rcpf(ps);
-#pragma unroll
-        for (int nt = 0; nt < kRowTiles; ++nt)
-#pragma unroll
-          for (int mt = 0; mt < kVTiles; ++mt) scale_acc(o[nt][mt], fo);
-        ps_ref = ps;
-      }
-      const float lrat = __builtin_amdgcn_logf(ps * __builtin_amdgcn_rcpf(ps_ref));  // log2 of the ratio
-      const float inv_ratio = ps_ref * __builtin_amdgcn_rcpf(ps);
+  // The reference page scale the accumulator is in units of moves (with a rescale) when a
+  // page's ratio to it leaves [1/4, 4]; scorers and accumulators follow the same sequence.
 
-      // ---- S^T = K Q^T for row tile rt, tokens 32 th + [0, 32)
-      f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      // latent: A = 32 fp8 codes of token mla_tok(tt, c) (two 16-byte LDS reads), B = the
-      // row's hi and lo terms; rope: A = 8 codes converted to fp16
-      const uint8_t* khalf = cur + 32 * th * kRawStride;
+  if (scorer) {
+    // ======== scores and numerators of row tile rt = wave, all 64 tokens of page t in step t
+    const int rt = wave;
+    // The lane's query row 16 rt + c of the block.  Latent dims 128 ks + 32 g + [0, 32) go to
+    // the fp8 MFMA as two exact e4m3 terms (hi, lo); rope dims 512 + 32 ks + 8 g + [0, 8) go to
+    // the f16 MFMA.  Both are scaled by 2^qe (largest |q| of the row in [128, 256)); the factor
+    // is taken out of the scores with the softmax scale.
+    const int r_s = hb * kMlaRowsPerBlock + 16 * rt + c;
+    const bool row_ok = r_s < p.rows;
+    const int lim = row_ok ? T - p.q_len + r_s / p.hq : -1;  // last visible position (below T <= INT32_MAX)
+    i32x8 qhi[kLatSteps], qlo[kLatSteps];
+    f16x8 qrope[kRopeSteps];
+    float sl2;
+    {
+      const int t = row_ok ? r_s / p.hq : 0, h = row_ok ? r_s % p.hq : 0;
+      const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim;
+      u32x4 qraw[kQWords];
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < kQWords; ++i) {
+        const uint16_t* src = i < kLatSteps * 4 ? qr + 128 * (i >> 2) + 32 * g + 8 * (i & 3)
+                                                : qr + kRope0 + 32 * (i - kLatSteps * 4) + 8 * g;
+        const u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
+        qraw[i] = w;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2)
+          mx = fmaxf(mx, fmaxf(fabsf(__builtin_bit_cast(float, w[e2] << 16)),
+                               fabsf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u))));
+      }
+      const float am = mgrp4_max(mx);
+      const int qe = am > 0.f ? 7 - ilogbf(am) : 0;
 #pragma unroll
       for (int ks = 0; ks < kLatSteps; ++ks) {
-        i32x8 a[2];
+        i32x8 hv, lv;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const uint8_t* kp = khalf + mla_tok(tt, c) * kRawStride + 128 * ks + 32 * g;
-          const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
-          const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
-          a[tt] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int j = 0; j < 4; ++j) {  // 8 dims per u32x4 -> two words of four e4m3 codes
+          const u32x4 w = qraw[4 * ks + j];
+#pragma unroll
+          for (int hw = 0; hw < 2; ++hw) {
+            const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), qe),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), qe),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), qe),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), qe)};
+            uint32_t hw32, lw32;
+            split_e4m3(v, hw32, lw32);
+            hv[2 * j + hw] = (int)hw32;
+            lv[2 * j + hw] = (int)lw32;
+          }
         }
-        if (ks < kEarlyLoads) ld(ks);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          s[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qhi[ks], s[tt], 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-          s[tt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[tt], qlo[ks], s[tt], 0, 0, 0, 127, 0, 127);
+        qhi[ks] = hv;
+        qlo[ks] = lv;
       }
 #pragma unroll
-      for (int ks = 0; ks < kRopeSteps; ++ks)
+      for (int ks = 0; ks < kRopeSteps; ++ks) {
+        const u32x4 w = qraw[kLatSteps * 4 + ks];
+        f16x2 h2[4];
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const f16x8 a =
-              cvt8(*reinterpret_cast<const u32x2*>(khalf + mla_tok(tt, c) * kRawStride + kRope0 + 32 * ks + 8 * g));
-          s[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[ks], s[tt], 0, 0, 0);
-        }
-
-#pragma unroll
-      for (int i = kEarlyLoads; i < kLoadIters; ++i) ld(i);  // the rest, once the K operands are dead
-
-      // ---- this half's numerators (lane: row 16 rt + c, tokens 32 th + mla_vtok(g, [0, 8)))
-      const float f = sl2 * ps;
-      if (!full) {
-        const int thr = llim(lim, jj);  // this row's last visible token
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (32 * th + mla_tok(tt, 4 * g + i) > thr) s[tt][i] = kNegInf;
+        for (int e2 = 0; e2 < 4; ++e2)
+          h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
+                         (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
+        qrope[ks] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
+                                            __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
+                                            6, 7);
       }
-      float v_max = kNegInf;
+      sl2 = p.scale * kLog2eM / ldexpf(1.f, qe);
+    }
+    float ref_s = kNegInf;  // the row's exponent offset (log2 units), the same in its four lanes
+    float l_s = 0.f;        // this lane's share of the row's denominator, in units of 2^ref_s
+    float ps_ref = 1.f;
+    for (int t = 0; t <= np; ++t) {
+      if (t + 1 < np) mla_fetch(mc, cp, t + 1, s_raw, s_scw, s_slot);
+      if (t < np) {
+        const int bt_ = t % kPageBufs, jj = j_begin + t;
+        const uint8_t* cur = s_raw[bt_];
+        const int32_t sl = s_slot[bt_];
+        const float ps = mla_scale(mc, sl, bt_, s_scw);
+        const bool exists = mla_ok(mc, sl);
+        ps_ref = mla_next_ref(ps, ps_ref);
+        const float lrat = __builtin_amdgcn_logf(ps * __builtin_amdgcn_rcpf(ps_ref));  // log2 of the ratio
+        // ---- S^T = K Q^T: tile 2 th + tt holds tokens 32 th + mla_tok(tt, m)
+        f32x4 sc[4];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+        for (int u = 0; u < 4; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, s[tt][i]);
-      const float lane_max = v_max * f;
-      float lr = ref_s;  // this half's offset for the page: raised only past the threshold
-      if (__any(lane_max > ref_s + kTau)) {
-        const float m_row = mgrp4_max(lane_max);
-        lr = m_row > ref_s + kTau ? m_row : ref_s;
-      }
-      const float off = lr == kNegInf ? 0.f : lr - lrat;  // -inf only while every score is masked
-      float psum = 0.f;
-      float x[8];
+        for (int ks = 0; ks < kLatSteps; ++ks) {
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[4 * tt + i] = __builtin_amdgcn_exp2f(fmaf(s[tt][i], f, -off));
-          psum += x[4 * tt + i];
+          for (int u = 0; u < 4; ++u) {
+            const uint8_t* kp = cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + 128 * ks + 32 * g;
+            const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
+            const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
+            const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[ks], sc[u], 0, 0, 0, 127, 0, 127);
+            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[ks], sc[u], 0, 0, 0, 127, 0, 127);
+          }
         }
-      s_p[rt][th][lane] = f16x8{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
-                                (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
-      if (g == 0) s_lr[th][16 * rt + c] = lr;
-      // LDS writes done, then a bare barrier: a full __syncthreads would also wait for the
-      // next page's copy, which is still in flight
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+        for (int ks = 0; ks < kRopeSteps; ++ks)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const f16x8 a = cvt8(*reinterpret_cast<const u32x2*>(
+                cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + kRope0 + 32 * ks + 8 * g));
+            sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[ks], sc[u], 0, 0, 0);
+          }
+        // ---- numerators (lane: row 16 rt + c, tokens 32 th + mla_vtok(g, [0, 8)) of each half)
+        const float f = sl2 * ps;
+        const bool full = exists && mla_llim(T - p.q_len, jj, tok_il, nsh, d) >= kMlaPage - 1;
+        if (!full) {
+          const int thr = exists ? mla_llim(lim, jj, tok_il, nsh, d) : -1;  // this row's last visible token
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (32 * (u >> 1) + mla_tok(u & 1, 4 * g + i) > thr) sc[u][i] = kNegInf;
+        }
+        float v_max = kNegInf;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v_max = fmaxf(v_max, sc[u][i]);
+        const float lane_max = v_max * f;
+        if (__any(lane_max > ref_s + kTau)) {  // the offset moves only past the threshold
+          const float m_row = mgrp4_max(lane_max);
+          if (m_row > ref_s + kTau) {
+            l_s *= ref_s == kNegInf ? 0.f : exp2f(ref_s - m_row);
+            ref_s = m_row;
+          }
+        }
+        const float off = ref_s == kNegInf ? 0.f : ref_s - lrat;  // -inf only while every score is masked
+        float psum = 0.f;
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+          float x[8];
+#pragma unroll
+          for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[4 * tt + i] = __builtin_amdgcn_exp2f(fmaf(sc[2 * th + tt][i], f, -off));
+              psum += x[4 * tt + i];
+            }
+          s_p[t & 1][rt][th][lane] = f16x8{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3],
+                                           (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
+        }
+        l_s += psum * ps_ref * __builtin_amdgcn_rcpf(ps);  // P carries ps / ps_ref; the denominator not
+        if (g == 0) s_off[t & 1][16 * rt + c] = ref_s;
+      }
+      // this step's LDS writes are done and page t + 1 has landed; then its tail, if any, is cleared
+      __builtin_amdgcn_s_waitcnt(0);
       __builtin_amdgcn_s_barrier();
-
-      // ---- each row's offset for the page: the larger of its two halves'
-      float nref[kRowTiles];
-      bool mv = false;
+      if (t + 1 < np) MLA_ZERO_TAIL(t + 1);
+    }
+    const float lh = mgrp4_sum(l_s);
+    if (g == 0) s_l[16 * rt + c] = lh;
+    __syncthreads();
+  } else {
+    // ======== O^T += V^T P^T for value dims [128 vw, 128 vw + 128) of all 64 rows, page t - 1 in step t
+    const int vw = wave - kRowTiles;
+    float ref[kRowTiles];  // offsets of rows 16 nt + c the accumulator is in units of
 #pragma unroll
-      for (int nt = 0; nt < kRowTiles; ++nt) {
-        nref[nt] = fmaxf(s_lr[0][16 * nt + c], s_lr[1][16 * nt + c]);
-        mv = mv || nref[nt] != ref[nt];
-      }
-      const bool move = __any(mv);  // the same in every wave of the workgroup
-      float own = 1.f;              // factor of this lane's numerators
-      if (move) {
+    for (int nt = 0; nt < kRowTiles; ++nt) ref[nt] = kNegInf;
+    float ps_ref = 1.f;
+    f32x4 o[kRowTiles][kVTiles];  // O^T tiles: dims 128 vw + 16 mt + 4 g + i of row 16 nt + c
 #pragma unroll
-        for (int nt = 0; nt < kRowTiles; ++nt) {
-          const float a = ref[nt] == kNegInf ? 0.f : exp2f(ref[nt] - nref[nt]);
+    for (int nt = 0; nt < kRowTiles; ++nt)
 #pragma unroll
-          for (int mt = 0; mt < kVTiles; ++mt) scale_acc(o[nt][mt], a);
-          if (nt == rt) {
-            l_s *= a;
-            own = lr == nref[nt] ? 1.f : exp2f(lr - nref[nt]);
-            ref_s = nref[nt];
-          }
-          ref[nt] = nref[nt];
-        }
-      }
-      l_s += psum * own * inv_ratio;
-
-      // ---- O^T += V^T P^T over this wave's value dims
-      // source lane (g, c) of the transposing read points at token 32 ks + mla_vtok(g, c >> 1),
-      // dims 16 mt + 8 (c & 1) .. +7; lane (g, j) then holds dim 16 mt + j of those 8 tokens
-      const uint8_t* vrow = cur + mla_vtok(g, c >> 1) * kRawStride + 8 * (c & 1) + kWaveDv * wave;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f16x8 pk[kRowTiles];
-#pragma unroll
-        for (int nt = 0; nt < kRowTiles; ++nt) pk[nt] = s_p[nt][ks][lane];
-        if (move) {  // operands of a half whose offset is below the row's
-#pragma unroll
-          for (int nt = 0; nt < kRowTiles; ++nt) {
-            const float lt = s_lr[ks][16 * nt + c];
-            const float fct = lt == ref[nt] ? 1.f : exp2f(lt - ref[nt]);
-            pk[nt] = pk[nt] * (_Float16)fct;
-          }
-        }
-        i32x2 vx[kVTiles];
-#pragma unroll
-        for (int mt = 0; mt < kVTiles; ++mt)
-          vx[mt] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * mt));
-#pragma unroll
-        for (int mt = 0; mt < kVTiles; ++mt) {
-          const int it = kVTiles * ks + mt;
-          if (it >= 2 * kVTiles - kLoadIters) st(it - (2 * kVTiles - kLoadIters));
-          const f16x8 a = cvt8(__builtin_bit_cast(u32x2, vx[mt]));
+      for (int mt = 0; mt < kVTiles; ++mt) o[nt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t <= np; ++t) {
+      if (t + 1 < np) mla_fetch(mc, cp, t + 1, s_raw, s_scw, s_slot);
+      if (t >= 1) {
+        const int bv = (t - 1) % kPageBufs, pb = (t - 1) & 1;
+        const uint8_t* cur = s_raw[bv];
+        const float ps = mla_scale(mc, s_slot[bv], bv, s_scw);
+        const float nps = mla_next_ref(ps, ps_ref);
+        if (nps != ps_ref) {
+          const float fo = ps_ref * __builtin_amdgcn_rcpf(nps);
 #pragma unroll
           for (int nt = 0; nt < kRowTiles; ++nt)
-            o[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pk[nt], o[nt][mt], 0, 0, 0);
+#pragma unroll
+            for (int mt = 0; mt < kVTiles; ++mt) scale_acc(o[nt][mt], fo);
+          ps_ref = nps;
+        }
+        float nref[kRowTiles];
+        bool mv = false;
+#pragma unroll
+        for (int nt = 0; nt < kRowTiles; ++nt) {
+          nref[nt] = s_off[pb][16 * nt + c];
+          mv = mv || nref[nt] != ref[nt];
+        }
+        if (__any(mv)) {
+#pragma unroll
+          for (int nt = 0; nt < kRowTiles; ++nt) {
+            const float a = nref[nt] == ref[nt] ? 1.f : (ref[nt] == kNegInf ? 0.f : exp2f(ref[nt] - nref[nt]));
+#pragma unroll
+            for (int mt = 0; mt < kVTiles; ++mt) scale_acc(o[nt][mt], a);
+            ref[nt] = nref[nt];
+          }
+        }
+        // source lane (g, c) of the transposing read points at token 32 ks + mla_vtok(g, c >> 1),
+        // dims 16 mt + 8 (c & 1) .. +7; lane (g, j) then holds dim 16 mt + j of those 8 tokens
+        const uint8_t* vrow = cur + mla_vtok(g, c >> 1) * kRawStride + 8 * (c & 1) + kWaveDv * vw;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          f16x8 pk[kRowTiles];
+#pragma unroll
+          for (int nt = 0; nt < kRowTiles; ++nt) pk[nt] = s_p[pb][nt][ks][lane];
+#pragma unroll
+          for (int mh = 0; mh < kVTiles; mh += 4) {
+            i32x2 vx4[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              vx4[u] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                  (lds_i32x2*)(vrow + 32 * ks * kRawStride + 16 * (mh + u)));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const f16x8 a = cvt8(__builtin_bit_cast(u32x2, vx4[u]));
+#pragma unroll
+              for (int nt = 0; nt < kRowTiles; ++nt)
+                o[nt][mh + u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pk[nt], o[nt][mh + u], 0, 0, 0);
+            }
+          }
         }
       }
+      __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_s_barrier();
+      if (t + 1 < np) MLA_ZERO_TAIL(t + 1);
     }
-    slot_cur = slot_nxt;
-    sc_cur = sc_nxt;
-    buf ^= 1;
-  }
-
-  // ---- write the (chunk) partial of rows 16 nt + c, this wave's dims: O = ps_ref * O^T / l
-  const float lh = mgrp4_sum(l_s);
-  if (g == 0) s_l[th][16 * rt + c] = lh;
-  __syncthreads();
-  const bool direct = chk.out < 0;
-  const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
-  const int64_t ws_row0 = direct ? 0 : (int64_t)chk.out * p.rows;
+    __syncthreads();  // the scorers' final denominators
+    // ---- write the (chunk) partial of rows 16 nt + c, this wave's dims: O = ps_ref * O^T / l
+    const bool direct = chk.out < 0;
+    const int64_t pair_row0 = ((int64_t)d * p.batch + b) * p.rows;
+    const int64_t ws_row0 = direct ? 0 : (int64_t)chk.out * p.rows;
 #pragma unroll
-  for (int nt = 0; nt < kRowTiles; ++nt) {
-    const int r = hb * kMlaRowsPerBlock + 16 * nt + c;
-    if (r >= p.rows) continue;
-    const float lrow = s_l[0][16 * nt + c] + s_l[1][16 * nt + c];
-    float* dst = (direct ? p.partial_out + (pair_row0 + r) * kMlaDv : p.ws_o + (ws_row0 + r) * kMlaDv) +
-                 kWaveDv * wave;
-    const float inv = lrow > 0.f ? ps_ref / lrow : 0.f;
+    for (int nt = 0; nt < kRowTiles; ++nt) {
+      const int r = hb * kMlaRowsPerBlock + 16 * nt + c;
+      if (r >= p.rows) continue;
+      const float lrow = s_l[16 * nt + c];
+      float* dst = (direct ? p.partial_out + (pair_row0 + r) * kMlaDv : p.ws_o + (ws_row0 + r) * kMlaDv) +
+                   kWaveDv * vw;
+      const float inv = lrow > 0.f ? ps_ref / lrow : 0.f;
 #pragma unroll
-    for (int mt = 0; mt < kVTiles; ++mt) {
-      const f32x4 v = o[nt][mt] * inv;
-      *reinterpret_cast<float4*>(dst + 16 * mt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
-    }
-    if (g == 0 && wave == 0) {
-      const float lse = lrow > 0.f ? (ref[nt] + log2f(lrow)) * kLn2M : kNegInf;
-      if (direct)
-        p.partial_lse[pair_row0 + r] = lse;
-      else
-        p.ws_lse[ws_row0 + r] = lse;
+      for (int mt = 0; mt < kVTiles; ++mt) {
+        const f32x4 v = o[nt][mt] * inv;
+        *reinterpret_cast<float4*>(dst + 16 * mt + 4 * g) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g == 0 && vw == 0) {
+        const float lse = lrow > 0.f ? (ref[nt] + log2f(lrow)) * kLn2M : kNegInf;
+        if (direct)
+          p.partial_lse[pair_row0 + r] = lse;
+        else
+          p.ws_lse[ws_row0 + r] = lse;
+      }
     }
   }
+#undef MLA_ZERO_TAIL
 }
 
 bool mla_fp8_supported(const dcp_attn_desc& D) {
