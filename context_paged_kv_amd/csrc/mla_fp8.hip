@@ -410,21 +410,28 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
         const bool exists = mla_ok(mc, sl);
         ps_ref = mla_next_ref(ps, ps_ref);
         const float lrat = __builtin_amdgcn_logf(ps * __builtin_amdgcn_rcpf(ps_ref));  // log2 of the ratio
-        // ---- S^T = K Q^T: tile 2 th + tt holds tokens 32 th + mla_tok(tt, m)
+        // ---- S^T = K Q^T: tile 2 th + tt holds tokens 32 th + mla_tok(tt, m).  Per k-step the four
+        // tiles' hi products go first, then their lo products, so no MFMA waits on the one
+        // just before it.
         f32x4 sc[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < kLatSteps; ++ks) {
+          i32x8 a[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const uint8_t* kp = cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + 128 * ks + 32 * g;
             const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
             const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
-            const i32x8 a = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qhi[ks], sc[u], 0, 0, 0, 127, 0, 127);
-            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qlo[ks], sc[u], 0, 0, 0, 127, 0, 127);
+            a[u] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
           }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u], qhi[ks], sc[u], 0, 0, 0, 127, 0, 127);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u], qlo[ks], sc[u], 0, 0, 0, 127, 0, 127);
         }
 #pragma unroll
         for (int ks = 0; ks < kRopeSteps; ++ks)
