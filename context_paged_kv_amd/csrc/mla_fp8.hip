@@ -13,35 +13,31 @@
 //
 // Work item: (shard d, request b, chunk of local pages, block of 64 query
 // rows).  A workgroup of eight wavefronts owns one item, two wavefronts per
-// SIMD, so one wavefront's vector work runs under the other's MFMAs.  Every
-// wavefront has two roles per page:
-//   * scores: wave w computes S^T for row tile rt = w % 4 (16 rows) and token
-//     half th = w / 4 (32 tokens) over all 576 dims, the softmax numerators P
-//     of those 16 x 32 scores, and hands them (fp16, already in the P^T
-//     operand layout) to the others through LDS;
-//   * values: wave w accumulates O^T for value dims [64 w, 64 w + 64) of all
-//     64 rows from every wave's P, so each converted V operand feeds four
+// SIMD of two kinds, one page apart, so one's vector work runs under the
+// other's MFMAs:
+//   * score wavefront w (w < 4): S^T for row tile w (16 rows) and all 64
+//     tokens of page t over all 576 dims, the row offsets and the softmax
+//     numerators P, handed to the value wavefronts through LDS (fp16, already
+//     in the P^T operand layout, double buffered by page parity);
+//   * value wavefront 4 + v: O^T for value dims [128 v, 128 v + 128) of all
+//     64 rows from page t - 1's P, each converted V operand feeding four
 //     MFMAs (one per row tile).
-// Per page:
-//   * the 36 KB of fp8 codes are double buffered in LDS: the loads of page
-//     j+1 go out between the score MFMAs of page j and land in registers,
-//     and are written to the other buffer between its PV MFMAs.  LDS rows
-//     are 592 bytes (576 + 16 pad);
+// Per page (one barrier each):
+//   * the 36 KB of fp8 codes come by LDS DMA into three buffers, page t + 1
+//     during step t.  LDS rows are 592 bytes (576 + 16 pad);
 //   * latent scores on v_mfma_scale_f32_16x16x128_f8f6f4 straight from the
 //     fp8 codes (unit scales): each query row is held as two e4m3 terms,
-//     hi = e4m3(q) and lo = e4m3(q - hi), whose sum is the bf16 query
-//     exactly (8 significant bits = 4 + 4), so no K conversion is needed;
-//     the rope dims use v_mfma_f32_16x16x32_f16 with K converted by
+//     hi = e4m3(q) and lo = e4m3(q - hi), whose sum is the bf16 query exactly
+//     (8 significant bits = 4 + 4), so no K conversion is needed; the rope
+//     dims use v_mfma_f32_16x16x32_f16 with K converted by
 //     v_cvt_scalef32_pk_f16_fp8 (exact).  The query is scaled by 2^qe per row
 //     so its largest entry lies in [128, 256); the factor leaves with the
 //     softmax scale;
-//   * online softmax in base 2 with a lazy reference per row: a token half
-//     raises its row's exponent offset only when its maximum exceeds the
-//     offset by more than 2^8; after the exchange every wave takes the larger
-//     of the two halves' offsets (the same values in every wave, so the same
-//     decision) and rescales accumulator rows and P operands only then.  The
-//     page scale rides in P as the ratio to a reference scale that moves
-//     (with a rescale) only when the ratio leaves [1/4, 4];
+//   * online softmax in base 2 with a lazy offset per row: the score wavefront
+//     raises it only when the page's maximum exceeds it by more than 2^8, and
+//     the value wavefronts rescale accumulator rows only then.  The page scale
+//     rides in P as the ratio to a reference scale that moves (with a rescale)
+//     only when the ratio leaves [1/4, 4];
 //   * O^T += V^T P^T on the f16 MFMA: ds_read_b64_tr_b8 hands each lane eight
 //     tokens of one latent dim straight from the row-major codes, converted
 //     to fp16 as above.
