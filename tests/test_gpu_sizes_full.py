@@ -83,6 +83,19 @@ def test_full_gqa_token_ownership_reshard_then_decode():
     H.log("  sampled rows match")
 
 
+def test_full_mla_fp8_48x100k_token_ownership():
+    """The 48 x 100000 MLA decode under token ownership (token t on shard t mod N), as the bench
+    times it with --own token; sampled rows of every shard and the merge against the oracle."""
+    w = get_workload("mla_fp8_48x100k")
+    H.log("full decode, token ownership: mla fp8 48 x 100000, Hq=128, N=8")
+    case = H.make_decode_case(w, DEV, own=K.OWN_TOKEN)
+    outs = H.run_decode(case)
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs.out).all()
+    worst = H.check_decode(case, outs, requests=[3, 40], heads=[1, 64, 126])
+    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+
+
 @pytest.mark.timeout(400)
 def test_full_longmix_verify_pipeline():
     """Reshard of the long requests from 4 layer-split sources, then q_len 4
