@@ -269,77 +269,114 @@ class Step:
         return qb + 2 * partial + out  # partials written once and read once by the merge
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(st, budget_s: float):
-    """The float64 oracle on the host (one thread), timed on a bounded sample of
-    the same workload and scaled linearly to the step's GB/s."""
-    import oracle as O
+    """The float64 oracle on the host, timed on a bounded sample of the same workload and
+    scaled linearly to the step's GB/s.  Independent units (reshard passes over a page
+    sample; requests of the attention, decoded and merged head by head) run on a pool of
+    worker processes, one per host core up to 16, each with one BLAS thread.  Page bytes
+    are copied from the GPU by this process; the workers never touch it."""
+    import multiprocessing as mp
     import torch
-    from threadpoolctl import threadpool_limits
+    import oracle as O
     from tests import harness as Hn  # oracle-side page gathering shared with the tests
+    from tests import oracle_workers as OW
 
     w = st.w
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
     budget = budget_s / (2 if (st.has_reshard and st.has_attention) else 1)
     notes = []
     rs_time_full = at_time_full = 0.0
-    with threadpool_limits(limits=1):
-        if st.has_reshard:
-            # the real source bytes of the first uncached pages, one layer per source,
-            # re-addressed into compact host pools (same per-page work as the full geometry)
-            n = min(len(st.dst_ids) - st.first_uncached, 16 if w.page_bytes > 65536 else 64)
-            sel = slice(st.first_uncached, st.first_uncached + n)
-            sids = st.src_ids[sel]
-            src_h = []
-            for r in range(w.num_sources):
-                t = np.full((2, n, w.page_bytes), 0x5A, np.uint8)
-                t[0] = st.src[r][0].index_select(0, sids.long()).cpu().numpy()
-                src_h.append(t)
-            g = st.dst_ids[sel].cpu().numpy()
-            g2 = np.arange(n) * w.dcp_size + (g % w.dcp_size)
-            dst_h = [np.zeros((w.num_sources, n, w.page_bytes), np.uint8) for _ in range(w.dcp_size)]
-            if st.own:  # token scatter: sequence pages 0..n-1 of one request, virtual page i div N at slot i div N
-                rows, row_bytes = (1, 576) if w.layout == "mla" else (2 * w.num_kv_heads,
-                                                                       w.head_dim_qk * w.elem_bytes)
-            reps, t0 = 0, time.perf_counter()
-            while time.perf_counter() - t0 < budget:
-                if st.own:
-                    O.reshard_tokens(src_h, dst_h, w.num_sources, w.dcp_size, w.page_size, rows, row_bytes,
-                                     np.arange(n), np.arange(n), 0)
-                else:
-                    O.reshard(src_h, dst_h, w.num_sources, w.dcp_size, np.arange(n), g2, 0)
-                reps += 1
-            t_rs = time.perf_counter() - t0
-            rate = 2.0 * reps * n * w.num_sources * w.page_bytes / t_rs
-            rs_time_full = st.bytes_reshard() / rate
-            kind = "token scatter" if st.own else "page"
-            notes.append(f"scalar {kind} reshard of {n} pages x {w.num_sources} layer(s), {reps} passes in {t_rs:.1f}s")
-        if st.has_attention:
-            done, t0, rows = 0, time.perf_counter(), 0
-            b = 0
-            while time.perf_counter() - t0 < budget and b < w.num_requests:
-                if st.own:
-                    kv = Hn.gather_token_layout_kv(st, b, w.attn_layer)
-                else:
-                    pb, ps = Hn.gather_request_pages(st.pools, st.scales, st.pages[b], w.dcp_size, w.attn_layer)
-                    kv = Hn.oracle_logical_kv(w, pb, ps, int(st.seq_lens[b]))
-                q = st.q[b].float().cpu().numpy().astype(np.float64)
-                for h in range(w.num_q_heads):
-                    po, pl = O.request_partials(q, kv[0], kv[1], int(st.seq_lens[b]), w.softmax_scale,
-                                                st.pages[b], w.page_size, w.dcp_size, heads=[h],
-                                                own="token" if st.own else "page")
-                    O.lse_merge(po[:, :, [h]], pl[:, :, [h]])
-                    rows += 1
-                    done += int(st.seq_lens[b]) * w.q_len
-                    if time.perf_counter() - t0 >= budget:
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    try:
+        with mp.get_context("spawn").Pool(workers) as pool:
+            pool.map(OW.warm, range(workers))  # processes up before anything is timed
+            if st.has_reshard:
+                # the real source bytes of the first uncached pages, one layer per source,
+                # re-addressed into compact host pools (same per-page work as the full geometry)
+                n = min(len(st.dst_ids) - st.first_uncached, 16 if w.page_bytes > 65536 else 64)
+                sel = slice(st.first_uncached, st.first_uncached + n)
+                sids = st.src_ids[sel]
+                src_h = []
+                for r in range(w.num_sources):
+                    t = np.full((2, n, w.page_bytes), 0x5A, np.uint8)
+                    t[0] = st.src[r][0].index_select(0, sids.long()).cpu().numpy()
+                    src_h.append(t)
+                g = st.dst_ids[sel].cpu().numpy()
+                g2 = np.arange(n) * w.dcp_size + (g % w.dcp_size)
+                rows, row_bytes = ((1, 576) if w.layout == "mla" else
+                                   (2 * w.num_kv_heads, w.head_dim_qk * w.elem_bytes))
+                deadline = time.time() + budget
+                t0 = time.perf_counter()
+                task = (src_h, w.dcp_size, (w.num_sources, n, w.page_bytes), w.num_sources, w.dcp_size, st.own,
+                        w.page_size, rows, row_bytes, g2, deadline)
+                reps = sum(pool.map(OW.reshard_passes, [task] * workers))
+                t_rs = time.perf_counter() - t0
+                rate = 2.0 * reps * n * w.num_sources * w.page_bytes / t_rs
+                rs_time_full = st.bytes_reshard() / rate
+                kind = "token scatter" if st.own else "page"
+                notes.append(f"scalar {kind} reshard of {n} pages x {w.num_sources} layer(s), {reps} passes on "
+                             f"{workers} processes in {t_rs:.1f}s")
+            if st.has_attention:
+                geo = {"layout": w.layout, "kv_dtype": w.kv_dtype, "num_kv_heads": w.num_kv_heads,
+                       "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v, "page_size": w.page_size,
+                       "dcp_size": w.dcp_size, "num_q_heads": w.num_q_heads, "q_len": w.q_len,
+                       "softmax_scale": w.softmax_scale, "own": "token" if st.own else "page"}
+                n_sh, lay = w.dcp_size, w.attn_layer
+                deadline = time.time() + budget
+                t0 = time.perf_counter()
+                pending, results = [], []
+                for b in range(w.num_requests):
+                    if time.time() >= deadline:
                         break
-                b += 1
-            t_at = time.perf_counter() - t0
-            at_time_full = t_at * (st.total_tokens * w.q_len * w.num_q_heads) / max(done, 1)
-            notes.append(f"partials + merge for {rows} of {w.num_requests * w.num_q_heads} (request, head) "
-                         f"rows in {t_at:.1f}s (page gather and decode included)")
+                    pages = st.pages[b]
+                    pages_h = scales_h = by_slot = None
+                    if st.own:  # every shard's pages at the request's virtual slots
+                        vslots = [O.dcp_local_slot(int(pages[j]), n_sh) for j in range(0, len(pages), n_sh)]
+                        sl = torch.tensor(vslots, dtype=torch.int64, device=st.pools[0].device)
+                        by_slot = {}
+                        for d in range(n_sh):
+                            pb = st.pools[d][lay].index_select(0, sl).cpu().numpy()
+                            sc = (st.scales[d][lay].index_select(0, sl).cpu().numpy().astype(np.int64) & 0xFFFF
+                                  if st.scales is not None else None)
+                            for i, s_ in enumerate(vslots):
+                                by_slot[(d, s_)] = (pb[i], None if sc is None else int(sc[i]))
+                    else:
+                        pages_h, scales_h = Hn.gather_request_pages(st.pools, st.scales, pages, n_sh, lay)
+                    q = st.q[b].float().cpu().numpy().astype(np.float64)
+                    pending.append(pool.apply_async(OW.request_rows, ((geo, pages_h, scales_h, by_slot, pages,
+                                                                       int(st.seq_lens[b]), q, deadline),)))
+                    while len(pending) > workers + 1:  # bounded host memory: one spare task
+                        results.append(pending.pop(0).get())
+                results += [r.get() for r in pending]
+                t_at = time.perf_counter() - t0
+                rows, done = sum(r for r, _ in results), sum(d for _, d in results)
+                at_time_full = t_at * (st.total_tokens * w.q_len * w.num_q_heads) / max(done, 1)
+                notes.append(f"partials + merge for {rows} of {w.num_requests * w.num_q_heads} (request, head) "
+                             f"rows on {workers} processes in {t_at:.1f}s (page gather and decode included)")
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     step_bytes = st.bytes_reshard() + st.bytes_kv() + st.bytes_attn_other()
     value = step_bytes / (rs_time_full + at_time_full) / 1e9
-    return {"value": round(value, 6), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "float64 numpy oracle, one thread: " + "; ".join(notes) + "; scaled linearly to the full step"}
+    return {"value": round(value, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": f"float64 numpy oracle on {workers} worker processes ({_cpu_model()}), one BLAS thread "
+                      "each: " + "; ".join(notes) + "; scaled linearly to the full step"}
 
 
 def plain_copy_gbps(torch, dev, nbytes: int, reps: int = 5) -> float:
