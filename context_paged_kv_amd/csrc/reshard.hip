@@ -152,7 +152,18 @@ struct TokenReshardArgs {
   int32_t* bad;
   int64_t page_bytes, seg_bytes, src_pages, dst_pages, first, work, items, num_pages;
   int32_t segs, num_layers, num_sources, n, page_size, row_bytes, num_req;
+  int32_t row16, block16;  // 16-byte chunks per token row and per block (page_size rows)
+  float r_row16, r_block16, r_n;  // their reciprocals and 1 / n, for the quotients below
 };
+
+// floor(a / b) for 0 <= a < 2^22 and b >= 1 from a float reciprocal: the product is within
+// 1/2 of a / b, so one correction step makes it exact.
+__device__ __forceinline__ int small_div(int a, int b, float rb) {
+  int q = (int)((float)a * rb);
+  const int r = a - q * b;
+  q += (r >= b ? 1 : 0) - (r < 0 ? 1 : 0);
+  return q;
+}
 
 // First list entry of the request that holds entry i (i < num_pages), or -1 when the offsets
 // name no request that contains i (offsets out of order or out of range).
@@ -176,8 +187,11 @@ __device__ __forceinline__ int64_t token_request_base(const TokenReshardArgs& a,
 // g_{o + (k div N) N} div N on every shard.  A page is token_rows blocks of P rows of row_bytes;
 // token x is row x of each block, and so is its destination row.
 __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenReshardArgs a) {
+  // the destination pools' base addresses, indexed per lane below, from LDS
+  __shared__ uint8_t* s_dst[kMaxShards];
+  if (threadIdx.x < a.n) s_dst[threadIdx.x] = a.dst[threadIdx.x];
+  __syncthreads();
   const int64_t per_layer = a.work * a.segs;
-  const int block_bytes = a.page_size * a.row_bytes;
   for (int64_t it = blockIdx.x; it < a.items; it += gridDim.x) {
     const int layer = (int)(it / per_layer);
     const int64_t rest = it - (int64_t)layer * per_layer;
@@ -199,7 +213,13 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenRe
     const int64_t dst_page = ((int64_t)layer * a.dst_pages + slot) * a.page_bytes;
     const int64_t len = (a.page_bytes - off0) < a.seg_bytes ? (a.page_bytes - off0) : a.seg_bytes;
     const int chunks = (int)(len >> 4);
-    const int64_t t0 = k * a.page_size;  // first token of the page in its request
+    // token t = k * page_size + x of the page goes to shard t mod n, row (t div n) mod page_size;
+    // with t0 = k * page_size = u0 * n + d0 that is shard (d0 + x) mod n, row
+    // (u0 + (d0 + x) div n) mod page_size
+    const int64_t t0 = k * a.page_size;
+    const int d0 = (int)(t0 % a.n);
+    const int y0 = (int)((t0 / a.n) % a.page_size);
+    const int c0 = (int)(off0 >> 4);  // first 16-byte chunk of the segment in the page
     u32x4 v[kReshardUnroll];
 #pragma unroll
     for (int q = 0; q < kReshardUnroll; ++q) {
@@ -210,14 +230,14 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenRe
     for (int q = 0; q < kReshardUnroll; ++q) {
       const int c = q * kReshardThreads + threadIdx.x;
       if (c < chunks) {
-        const int o = (int)(off0 + 16 * (int64_t)c);  // byte offset in the page (< 2^31)
-        const int blk = o / block_bytes, rem = o - blk * block_bytes;
-        const int x = rem / a.row_bytes, off = rem - x * a.row_bytes;
-        const int64_t t = t0 + x;
-        const int d = (int)(t % a.n);
-        const int y = (int)((t / a.n) % a.page_size);
+        const int ci = c0 + c;  // chunk in the page: block, token row, chunk within the row
+        const int blk = small_div(ci, a.block16, a.r_block16), rem = ci - blk * a.block16;
+        const int x = small_div(rem, a.row16, a.r_row16), cr = rem - x * a.row16;
+        const int sx = d0 + x, dq = small_div(sx, a.n, a.r_n);
+        const int d = sx - dq * a.n;
+        const int y = y0 + dq >= a.page_size ? y0 + dq - a.page_size : y0 + dq;
         __builtin_nontemporal_store(
-            v[q], reinterpret_cast<u32x4*>(a.dst[d] + dst_page + ((int64_t)blk * a.page_size + y) * a.row_bytes + off));
+            v[q], reinterpret_cast<u32x4*>(s_dst[d] + dst_page) + ((int64_t)blk * a.page_size + y) * a.row16 + cr);
       }
     }
   }
@@ -317,7 +337,7 @@ extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* 
   const int64_t page_bytes = (int64_t)D.token_rows * D.page_size * D.row_bytes;
   if (D.num_sources < 1 || D.num_sources > kMaxSources || D.num_layers < D.num_sources ||
       D.num_layers > kMaxLayers || D.dcp_size < 1 || D.dcp_size > kMaxShards || D.page_size < 1 ||
-      D.token_rows < 1 || D.row_bytes < 16 || D.row_bytes % 16 != 0 || page_bytes > INT32_MAX ||
+      D.token_rows < 1 || D.row_bytes < 16 || D.row_bytes % 16 != 0 || page_bytes >= (1LL << 26) ||
       D.src_pages < 1 || D.dst_pages < 1)
     return set_error(DCPKV_EINVAL,
                      "token reshard: bad descriptor (N_cp=%d L=%d N=%d page=%d rows=%d row_bytes=%d S=%lld M=%lld)",
@@ -365,6 +385,11 @@ extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* 
   a.n = D.dcp_size;
   a.page_size = D.page_size;
   a.row_bytes = D.row_bytes;
+  a.row16 = D.row_bytes / 16;
+  a.block16 = D.page_size * a.row16;
+  a.r_row16 = 1.0f / (float)a.row16;
+  a.r_block16 = 1.0f / (float)a.block16;
+  a.r_n = 1.0f / (float)D.dcp_size;
   const int64_t grid = std::min<int64_t>(a.items, (int64_t)device_cus_reshard() * kReshardBlocksPerCU);
   hipLaunchKernelGGL(reshard_tokens_kernel, dim3((unsigned)grid), dim3(kReshardThreads), 0,
                      static_cast<hipStream_t>(stream), a);

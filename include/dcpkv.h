@@ -195,7 +195,8 @@ typedef struct {
   int32_t dcp_size;     /* N destination pools, >= 1 */
   int32_t page_size;    /* tokens per page */
   int32_t token_rows;   /* R: a page is R blocks of page_size rows (SPLIT: 2 * Hkv; MLA: 1) */
-  int32_t row_bytes;    /* bytes per row, a multiple of 16 (SPLIT: head_dim * elem; MLA: 576) */
+  int32_t row_bytes;    /* bytes per row, a multiple of 16 (SPLIT: head_dim * elem; MLA: 576);
+                           a page (token_rows * page_size * row_bytes) is below 64 MiB */
   int64_t src_pages;    /* S: page slots per layer slot in each source pool */
   int64_t dst_pages;    /* M: local page slots per layer in each destination */
 } kv_token_reshard_desc;
