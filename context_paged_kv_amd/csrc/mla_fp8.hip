@@ -80,7 +80,6 @@ constexpr int kSlotsPerRow = kRawStride / 16;          // 37 16-byte slots (36 d
 constexpr int kSlots = kMlaPage * kSlotsPerRow;        // 2368
 constexpr int kLoadIters = (kSlots + kThreads - 1) / kThreads;  // copy instructions per wave and page
 constexpr int kPageBufs = 3;                           // page buffers in LDS
-constexpr int kWaitLgkm0 = 0xC07F;                     // s_waitcnt lgkmcnt(0), other counters untouched
 constexpr float kTau = 8.f;                            // lazy-rescale threshold (log2 units)
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;

@@ -189,7 +189,7 @@ __device__ __forceinline__ int64_t token_request_base(const TokenReshardArgs& a,
 __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenReshardArgs a) {
   // the destination pools' base addresses, indexed per lane below, from LDS
   __shared__ uint8_t* s_dst[kMaxShards];
-  if (threadIdx.x < a.n) s_dst[threadIdx.x] = a.dst[threadIdx.x];
+  if ((int)threadIdx.x < a.n) s_dst[threadIdx.x] = a.dst[threadIdx.x];
   __syncthreads();
   const int64_t per_layer = a.work * a.segs;
   for (int64_t it = blockIdx.x; it < a.items; it += gridDim.x) {
