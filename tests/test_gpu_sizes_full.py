@@ -29,6 +29,21 @@ def test_full_reshard_mla_128k():
     H.log(f"  {n_copies} page copies verified")
 
 
+def test_full_gqa_reshard_16_requests():
+    """The transfer the default bench times: every page of the 16 requests (4K-32K tokens, bf16
+    GQA pages of 256 KiB) from the source into the N = 4 pools, bit for bit against the
+    oracle's copy plan."""
+    w = get_workload("gqa_bf16_16x4k-32k")
+    H.log("full reshard: gqa bf16 16 x U[4K,32K], 256 KiB pages, N=4")
+    sl = np.asarray(H.gen.draw_seq_lens(w))
+    rc = H.make_reshard_case(w, DEV, seq_lens=sl, first_uncached=0)
+    H.run_reshard(rc)
+    torch.cuda.synchronize()
+    n_copies = H.check_reshard_by_plan(rc)
+    assert n_copies == len(rc.dst_ids)
+    H.log(f"  {n_copies} page copies verified")
+
+
 def test_full_gqa_bf16_16x4k_32k():
     w = get_workload("gqa_bf16_16x4k-32k")
     H.log("full decode: gqa bf16 16 x U[4K,32K], N=4")
