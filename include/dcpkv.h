@@ -310,9 +310,9 @@ typedef struct {
   float softmax_scale;     /* scores are softmax_scale * q . k */
   int32_t token_interleave; /* DCPKV_OWN_PAGE (0): page p of a sequence lives on shard
                                p mod N ([2DR] section 5.1).  DCPKV_OWN_TOKEN (1): token t
-                               lives on shard t mod N, local token t div N ([SGL]: rank i
-                               holds tokens i, i+N, i+2N, ...).  The block tables are the
-                               same for both: entry j of (d, b) is the slot of local page j. */
+                               lives on shard t mod N, local token t div N ([SGL], the
+                               DCP paragraph).  The block tables are the same for both:
+                               entry j of (d, b) is the slot of local page j. */
 } dcp_attn_desc;
 
 /* Workspace bytes dcp_decode_partial needs for this batch.  total_tokens is
@@ -333,8 +333,8 @@ DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t
  *     LSE_d = log sum_{j in J} exp(s_j)
  *     O_d   = sum_{j in J} exp(s_j - LSE_d) v_j
  * i.e. the shard's output normalised by its own denominator plus the
- * log-sum-exp of its scores; exp(LSE_d) * O_d is the unnormalised weighted
- * sum of [SGL].  An empty J gives O_d = 0, LSE_d = -inf.  MLA: k_j is the
+ * log-sum-exp of its scores; exp(LSE_d) * O_d is the weighted sum [SGL]
+ * describes before normalisation.  An empty J gives O_d = 0, LSE_d = -inf.  MLA: k_j is the
  * whole dequantised 576-d latent (code x page scale), v_j its first 512.
  *
  * q: [B][q_len][Hq][head_dim_qk] (f32 or bf16).  kv_pools: host array [N] of

@@ -16,20 +16,20 @@ Sources (cited by short name below):
 Readings where the pages are silent or garbled (each one is listed in the
 design notes as well):
   R1  A shard's partial output is normalised by the shard's own softmax
-      denominator: O_d = sum_{j in d} exp(s_j - LSE_d) v_j.  The raw
-      "unnormalised weighted sum" of [SGL] is exp(LSE_d) * O_d; both carry the
-      same information, the raw one overflows float32.
+      denominator: O_d = sum_{j in d} exp(s_j - LSE_d) v_j.  The raw weighted
+      sum [SGL] describes is exp(LSE_d) * O_d; both carry the same
+      information, the raw one overflows float32.
   R2  Partials are combined as O = sum_d exp(LSE_d - LSE) O_d with LSE the
-      [2DR] section 5.2 merge; the page's "concat along seq dim" line for O is
-      not a combination rule.
+      [2DR] section 5.2 merge; the page's annotation of the all-gather of O as a
+      concatenation along the sequence is not a combination rule.
   R3  Logs are natural; the softmax scale is applied inside the scores.
   R4  Absorbed MLA: q is 576-d per head, K is the whole 576-d latent, V is its
       first 512 entries, one latent shared by all query heads.
   R5  fp8 is OCP e4m3fn (bias 7, max 448, codes 0x7F/0xFF are NaN, no inf),
       one bf16 scale per (layer, page); value = code * scale.
   R6  Ownership is decided by the destination global page VALUE (g mod N), as
-      [2DR] section 6.3 states and [PR28] warns ("do not take the modulo of
-      the position in the source page list").
+      [2DR] section 6.3 states; the [PR28] review warns against using the
+      residue of a position in the source page list.
   R7  Prefix-cached pages are the leading whole pages [0, c): never read,
       never written.
   R8  The reshard copies whole pages, tail bytes of a partial last page
@@ -45,7 +45,7 @@ design notes as well):
       a row) into a staging buffer of a fixed number of pages, window after
       window; the pages give the idea (a fixed pre-registered buffer reused in
       chunks, the same bytes moved), not a layout, so the order is ours.
-  R18 Token ownership ([SGL]: rank i holds tokens i, i+N, ...): token t is the
+  R18 Token ownership ([SGL]: token t lives on rank t mod N): token t is the
       (t div N)-th token of shard t mod N; shard d's local page j holds its
       tokens j*page_size .. j*page_size + page_size - 1 and sits at the slot of
       the request's j-th virtual page (the allocator's unit of N pages), the
@@ -199,7 +199,7 @@ def block_tables(global_pages: Sequence[Sequence[int]], n: int, own: str = "page
 
 
 def token_owner(t: int, n: int) -> int:
-    """[SGL]: rank i holds tokens i, i+N, i+2N, ... of the sequence."""
+    """[SGL]: token t of the sequence lives on rank t mod N."""
     return t % n
 
 

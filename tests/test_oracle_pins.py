@@ -231,7 +231,7 @@ def test_reshard_moves_scales():
 
 
 def test_token_ownership_fixture():
-    """[SGL]: rank i holds tokens i, i+N, i+2N, ... (tests/golden/token_ownership_10_over_4.txt)."""
+    """[SGL]: token t lives on rank t mod N (tests/golden/token_ownership_10_over_4.txt)."""
     for row in _rows("token_ownership_10_over_4.txt"):
         d, toks = int(row[0]), [int(x) for x in row[1:]]
         mask = O.shard_token_mask([0, 1, 2, 3], 16, 10, 4, d, own="token")

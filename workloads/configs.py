@@ -4,8 +4,8 @@ Each workload is named by what it is.  The shapes follow the deployment the
 pages describe: 64-token pages and a 576-byte fp8 latent per token per layer
 (512 latent + 64 rope) from "Serving Macaron-V1 at Scale: Page-Level 2D KV
 Resharding", section 5.3 (Table 3 caption); 4K-32K and 500K-1M token
-requests from sections 1 and 5.3 of the same page; "48 sessions at 100K
-context" from "SGLang's path" (the DCP paragraph).
+requests from sections 1 and 5.3 of the same page; 48 sessions with a
+100K-token context each from "SGLang's path" (the DCP paragraph).
 
 Size readings (the pages are silent): 2K/4K/32K/128K are binary
 (4K = 4096 tokens), 100K/500K/1M are decimal (100K = 100000 tokens); uniform
