@@ -155,14 +155,14 @@ __device__ __forceinline__ int mla_tok(int tt, int m) { return mla_vtok(m >> 2, 
 
 // One LDS DMA piece: 16 bytes per lane from gptr to LDS address m0 + 16 lane (4 bytes per
 // lane for dma4).  Written as asm, so the compiler neither orders LDS reads behind it nor
-// counts it: every wait for these pieces is explicit.
+// counts it: every wait for these pieces is explicit.  The LDS address is an operand bound
+// to m0, so the compiler sets m0 itself and knows it is in use; the s_nop is the one wait
+// state an SALU write of m0 needs before an LDS DMA reads it.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"{m0}"(lds_addr), "v"(gptr) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds_addr), "v"(gptr)
-               : "memory", "m0");
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %1, off" ::"{m0}"(lds_addr), "v"(gptr) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
