@@ -387,8 +387,11 @@ static int validate(const dcp_attn_desc& D) {
     return set_error(DCPKV_EINVAL, "attn: bad geometry");
   if (D.token_interleave != DCPKV_OWN_PAGE && D.token_interleave != DCPKV_OWN_TOKEN)
     return set_error(DCPKV_EINVAL, "attn: token_interleave must be %d or %d", DCPKV_OWN_PAGE, DCPKV_OWN_TOKEN);
-  if ((int64_t)D.q_len * D.num_q_heads > (1 << 20) || (int64_t)D.batch * D.dcp_size > (1 << 24))
-    return set_error(DCPKV_EINVAL, "attn: batch too large");
+  // the chunk reduction's grid is (pairs, row blocks): at most 65535 row blocks
+  if ((int64_t)D.q_len * D.num_q_heads > 65535LL * kRowsPerMergeBlock || (int64_t)D.batch * D.dcp_size > (1 << 24))
+    return set_error(DCPKV_EINVAL, "attn: q_len * Hq = %lld rows (limit %d) or B * N = %lld (limit %d) too large",
+                     (long long)D.q_len * D.num_q_heads, 65535 * kRowsPerMergeBlock,
+                     (long long)D.batch * D.dcp_size, 1 << 24);
   return DCPKV_OK;
 }
 

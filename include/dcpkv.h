@@ -349,8 +349,9 @@ DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t
  * slices are written.  workspace: device, >= dcp_decode_partial_workspace()
  * bytes, 256-byte aligned; its contents need not be initialised.
  * A table entry outside [0, M) is treated as a page of no tokens.
- * EINVAL on a bad descriptor/pointer or too small a workspace; ENOTSUP for
- * shapes no kernel here handles. */
+ * Limits: q_len * Hq <= 262,140 query rows per request, B * N <= 2^24.
+ * EINVAL on a bad descriptor/pointer, a limit exceeded or too small a
+ * workspace (every descriptor that passes these checks has a kernel). */
 DCPKV_API int dcp_decode_partial(const dcp_attn_desc* desc, const void* q, const void* const* kv_pools,
                        const void* const* kv_scales, const int32_t* block_tables,
                        const int32_t* seq_lens, int64_t total_tokens, int32_t shard_begin,

@@ -154,6 +154,16 @@ def test_device_entry_points_reject_bad_arguments_on_host():
                            num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64, dcp_size=4, batch=2,
                            q_len=1, max_local_pages=4, layer=0, num_layers=1, pages_per_layer=16, softmax_scale=0.1)
     assert L._lib.dcp_decode_partial_workspace(C.byref(bad), 1000) == 0
+    # the chunk reduction launches one block per 4 query rows, at most 65535 of them
+    edge = dict(kv_dtype=K.KV_F32, kv_layout=K.LAYOUT_SPLIT, q_dtype=K.Q_F32, num_q_heads=4, num_kv_heads=4,
+                head_dim_qk=64, head_dim_v=64, page_size=16, dcp_size=2, batch=1, max_local_pages=4, layer=0,
+                num_layers=1, pages_per_layer=16, softmax_scale=0.1)
+    assert K.dcp_decode_partial_workspace(K.make_attn_desc(q_len=65535, **edge), 1000) > 0
+    big = K.make_attn_desc(q_len=65536, **edge)
+    assert L._lib.dcp_decode_partial_workspace(C.byref(big), 1000) == 0
+    rc = L._lib.dcp_decode_partial(C.byref(big), C.c_void_p(256), p, None, C.c_void_p(256), C.c_void_p(256), 0,
+                                   0, 2, C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1 << 30, None)
+    assert rc == L.DCPKV_EINVAL and "limit" in K.dcpkv_last_error()
     rc = L._lib.dcp_decode_partial(C.byref(good), None, None, None, None, None, 0, 0, 4, None, None, None, 0, None)
     assert rc == L.DCPKV_EINVAL
     rc = L._lib.dcp_decode_partial(C.byref(good), C.c_void_p(256), p, None, C.c_void_p(256), C.c_void_p(256), 0,
