@@ -42,11 +42,34 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
   const int lane = threadIdx.x;
   const int num_pairs = p.shard_count * p.batch;
-  const int C = p.chunk_pages;
   auto pair_pages = [&](int i) {
     const int d = p.shard_begin + i / p.batch, b = i % p.batch;
     return local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local, p.tok_il);
   };
+  // Pairs of (nearly) equal length whose work items fill the device's workgroup slots in
+  // whole rounds are already balanced: splitting them would only add the chunk round trip
+  // and its reduction, so they keep one chunk each.  Equal: longest <= 17/16 of the
+  // shortest non-empty pair; whole rounds: at most 1/32 of the slots of the last round idle.
+  int ne = 0, lo = INT32_MAX, hi = 0;
+  for (int i = lane; i < num_pairs; i += 64) {
+    const int nl = pair_pages(i);
+    if (nl > 0) {
+      ++ne;
+      lo = min(lo, nl);
+      hi = max(hi, nl);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    ne += __shfl_xor(ne, off, 64);
+    lo = min(lo, __shfl_xor(lo, off, 64));
+    hi = max(hi, __shfl_xor(hi, off, 64));
+  }
+  const long long items1 = (long long)ne * p.hb_count, slots = p.slots;
+  const long long rounds1 = slots > 0 ? (items1 + slots - 1) / slots : 0;
+  const bool whole = ne > 0 && (long long)hi * 16 <= (long long)lo * 17 && items1 >= slots && slots > 0 &&
+                     (rounds1 * slots - items1) * 32 <= rounds1 * slots;
+  const int C = whole ? INT32_MAX : p.chunk_pages;
   // chunk totals first: one chunk per pair when the split would not fit the workspace or
   // the launched grid
   long long need = 0, need_all = 0;
@@ -512,6 +535,7 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   p.shard_begin = shard_begin;
   p.shard_count = shard_count;
   p.chunk_pages = g.chunk_pages;
+  p.slots = (int32_t)std::min<int64_t>((int64_t)device_cus() * kernel_resident_per_cu(g.kind), INT32_MAX);
   p.group = D.num_q_heads / D.num_kv_heads;
   p.rows = g.rows;
   p.hb_count = g.hb_count;

@@ -68,6 +68,7 @@ struct AttnParams {
   int32_t hq, hkv, dqk, dv, page_size, n, batch, q_len, max_local, layer;
   int32_t shard_begin, shard_count;
   int32_t chunk_pages;  // C
+  int32_t slots;        // workgroups of the partial kernel the device runs at once
   int32_t group;        // Hq / Hkv
   int32_t rows;         // q_len * Hq: query rows per pair
   int32_t hb_count;     // head blocks per chunk

@@ -1,6 +1,7 @@
 // Kernel selection for dcp_decode_partial.  Each kernel kind states how many
 // query rows one work item covers, how many items per compute unit the
-// planner should aim for, the smallest chunk it wants, and how it launches.
+// planner should aim for, how many of its workgroups one compute unit holds at
+// once, the smallest chunk it wants, and how it launches.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,6 +19,7 @@ enum KernelKind : int {
 int choose_kernel(const dcp_attn_desc& D);
 int kernel_rows_per_block(int kind, const dcp_attn_desc& D);
 int kernel_items_per_cu(int kind);
+int kernel_resident_per_cu(int kind);
 int kernel_min_chunk_pages(int kind, const dcp_attn_desc& D);
 int launch_partial(int kind, const AttnParams& p, const dcp_attn_desc& D, int cus,
                    int64_t item_bound, hipStream_t st);

@@ -39,6 +39,20 @@ int kernel_items_per_cu(int kind) {
   }
 }
 
+// Workgroups of the kind one compute unit runs at once: the GQA kernel's one-wave
+// workgroups are bounded by their 34 KB of LDS, the MLA kernel's by its 128 KB, and the
+// generic kernel launches a grid of two per compute unit.
+int kernel_resident_per_cu(int kind) {
+  switch (kind) {
+    case KK_GQA_BF16:
+      return 4;
+    case KK_MLA_FP8:
+      return 1;
+    default:
+      return 2;
+  }
+}
+
 int kernel_min_chunk_pages(int kind, const dcp_attn_desc& D) {
   (void)D;
   switch (kind) {
