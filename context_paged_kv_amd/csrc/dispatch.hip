@@ -34,6 +34,8 @@ int kernel_items_per_cu(int kind) {
   switch (kind) {
     case KK_GQA_BF16:
       return 16;  // one wavefront per item
+    case KK_MLA_FP8:
+      return 8;  // one workgroup per compute unit at a time: eight rounds of chunks balance mixed lengths
     default:
       return 4;
   }
