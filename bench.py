@@ -114,6 +114,7 @@ class Step:
             if sc is not None:
                 sc[-1].fill_(gen.SCALE_SENTINEL)
                 self.src_scales.append(sc)
+            print(f"[bench] source {r} of {w.num_sources} filled", file=sys.stderr, flush=True)
         # pools: random pages where requests are not transferred in the step, else a sentinel
         fill_random = self.has_attention and len(self.reshard_reqs) < w.num_requests
         self.pools, self.scales = [], ([] if w.has_scales else None)
@@ -129,6 +130,7 @@ class Step:
             self.pools.append(t)
             if sc is not None:
                 self.scales.append(sc)
+            print(f"[bench] pool {d} of {N} filled", file=sys.stderr, flush=True)
         self.src_ids = torch.from_numpy(gen.draw_src_order(w, S)[: self.num_pages].astype(np.int32)).to(dev)
         self.dst_ids = torch.from_numpy(np.concatenate([self.pages[b] for b in self.reshard_reqs] or [np.zeros(0)])
                                         .astype(np.int64)).to(dev)

@@ -29,6 +29,12 @@ namespace dcpkv {
 constexpr int kPlanThreads = 64;  // one wavefront: shuffles instead of barriers
 
 // Inclusive prefix sum over the wavefront.
+// Size class of a chunk of `size` pages, 0 for the longest (size >= range), 63 for empty ones.
+__device__ __forceinline__ int size_key(int size, int range) {
+  const long long k = ((long long)(range - min(size, range)) * 64) / ((long long)range + 1);
+  return (int)k;
+}
+
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -85,6 +91,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
     need_all += __shfl_xor(need_all, off, 64);
   }
   const int fallback = (need > (long long)p.ws_cap || need_all > (long long)p.max_chunks) ? 1 : 0;
+  // size classes of the longest-first order: chunk sizes run up to C pages (a pair's whole
+  // length when it is not split)
+  __shared__ int s_cnt[64];
+  s_cnt[lane] = 0;
+  __syncthreads();
+  const int range = (C == INT32_MAX || fallback) ? max(hi, 1) : C;
   // then exclusive prefix sums of the chunks and of the workspace slots, 64 pairs at a time
   int carry_k = 0, carry_w = 0;
   for (int base = 0; base < num_pairs; base += 64) {
@@ -103,14 +115,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
       pp.k = k;
       pp.n_local = nl;
       p.pairs[i] = pp;
-      for (int c = 0; c < k; ++c) {
-        int jb, je;
-        chunk_range(pp, c, jb, je);
-        p.chunks[pp.chunk_begin + c] = ChunkPlan{i, jb, je, kw ? pp.ws_begin + c : -1};
-      }
+      // a pair's chunks have at most two sizes: `extra` of base + 1 pages, then k - extra of base
+      const int base_sz = nl / k, extra = nl - base_sz * k;
+      if (extra) atomicAdd(&s_cnt[size_key(base_sz + 1, range)], extra);
+      if (k > extra) atomicAdd(&s_cnt[size_key(base_sz, range)], k - extra);
     }
     carry_k += __shfl(sk, 63, 64);
     carry_w += __shfl(sw, 63, 64);
+  }
+  // Chunks go out longest first (a counting sort over 64 size classes), so the work items
+  // the hardware dispatches last are the short ones and the tail of the grid stays short.
+  // The order changes no result: a chunk's output slot is fixed by its pair and index.
+  __syncthreads();
+  {
+    const int n_in = s_cnt[lane];
+    s_cnt[lane] = wave_incl_scan(n_in) - n_in;
+  }
+  __syncthreads();
+  for (int i = lane; i < num_pairs; i += 64) {
+    const PairPlan pp = p.pairs[i];
+    const int base_sz = pp.n_local / pp.k, extra = pp.n_local - base_sz * pp.k;
+    const int at_hi = extra ? atomicAdd(&s_cnt[size_key(base_sz + 1, range)], extra) : 0;
+    const int at_lo = pp.k > extra ? atomicAdd(&s_cnt[size_key(base_sz, range)], pp.k - extra) : 0;
+    for (int c = 0; c < pp.k; ++c) {
+      int jb, je;
+      chunk_range(pp, c, jb, je);
+      p.chunks[c < extra ? at_hi + c : at_lo + (c - extra)] =
+          ChunkPlan{i, jb, je, pp.ws_begin >= 0 ? pp.ws_begin + c : -1};
+    }
   }
   for (int64_t c = carry_k + lane; c < p.max_chunks; c += 64) p.chunks[c] = ChunkPlan{-1, 0, 0, -1};
   if (lane == 0) {
