@@ -219,6 +219,98 @@ def test_decode_split_does_not_change_results(name, tokens_hint):
     H.check_decode(case, outs, heads=list(range(min(w.num_q_heads, 16))))
 
 
+def _read_plan(ws: torch.Tensor, pairs: int):
+    """The planner's output in the workspace: the header's chunk count, the per-pair plans
+    (chunk prefix, workspace slot, k, local pages) and the chunk entries (pair, first page,
+    end page, output slot).  Layout: 64-byte header at 0, pair plans from byte 256, chunk
+    entries from the next 256-byte boundary, 16 bytes each."""
+    raw = ws.cpu().numpy().view(np.int32)
+    total = int(raw[0])
+    pp = raw[64: 64 + 4 * pairs].reshape(pairs, 4)
+    c0 = ((256 + 16 * pairs + 255) // 256) * 256 // 4
+    ch = raw[c0: c0 + 4 * (total + 1)].reshape(total + 1, 4)
+    return total, pp, ch
+
+
+def _check_plan(total, pp, ch, nl_expected):
+    """Every pair's local pages are covered once, by its k chunks of sizes that differ by at
+    most one, each written to its own output slot; the entries run longest first (to within
+    one of the 64 size classes) and the entry after the last is empty."""
+    assert ch[total, 0] == -1
+    assert total == int(pp[:, 2].sum())
+    seen = {}
+    for pair, jb, je, out in ch[:total]:
+        seen.setdefault(int(pair), []).append((int(jb), int(je), int(out)))
+    for i, n_local in enumerate(nl_expected):
+        k = int(pp[i, 2])
+        assert int(pp[i, 3]) == n_local and k >= 1
+        got = sorted(seen.get(i, []))
+        assert len(got) == k
+        assert [g[0] for g in got] == [0] + [g[1] for g in got[:-1]] and got[-1][1] == n_local
+        sizes = [je - jb for jb, je, _ in got]
+        assert max(sizes) - min(sizes) <= 1
+        outs = [o for _, _, o in got]
+        assert outs == ([-1] if k == 1 else list(range(int(pp[i, 1]), int(pp[i, 1]) + k)))
+    sizes = (ch[:total, 2] - ch[:total, 1]).astype(np.int64)
+    span = max(int(sizes.max()), 1)
+    assert (np.diff(sizes) <= span // 64 + 1).all(), "chunks are not longest first"
+
+
+def _local_pages(seq_lens, page_size, n):
+    out = []
+    for d in range(n):
+        for t in seq_lens:
+            p = -(-int(t) // page_size)
+            out.append((p - 1 - d) // n + 1 if p > d else 0)
+    return out
+
+
+def test_decode_plan_splits_mixed_lengths_longest_first():
+    """Unequal pairs are split into chunks of at most C pages, emitted longest first."""
+    base = get_workload("gqa_bf16_16x4k-32k")
+    ps, n = base.page_size, base.dcp_size
+    w = scaled(base, seed=base.seed + 240, seq_segments=((12, ps * n * 4, ps * n * 40), (2, 5, ps)),
+               pool_pages=512, num_layers=1, attn_layer=0)
+    H.log("plan: GQA bf16 B=14 mixed 5..10240 tokens, N=4")
+    case = H.make_decode_case(w, DEV)
+    outs, ws = H.alloc_outputs(case)
+    H.run_decode(case, outs, ws)
+    _sync()
+    pairs = n * w.num_requests
+    total, pp, ch = _read_plan(ws, pairs)
+    nl = _local_pages(case.seq_lens, ps, n)
+    _check_plan(total, pp, ch, nl)
+    assert (pp[:, 2] >= 2).any(), "the long pairs were not split"
+    H.check_decode(case, outs, heads=list(range(8)))
+
+
+def test_decode_plan_keeps_equal_pairs_whole_when_they_fill_the_device():
+    """Equal-length pairs whose work items fill every workgroup slot in whole rounds keep one
+    chunk each (GQA kernel: four resident workgroups per compute unit, one per KV head and
+    chunk); one pair shorter than the rest breaks the rule and the long pairs split again."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    base = get_workload("gqa_bf16_16x4k-32k")
+    ps, n = base.page_size, base.dcp_size
+    b = cus * 4 // (n * base.num_kv_heads)  # pairs x KV heads = one round of slots
+    t = ps * n * 20                        # 20 local pages per pair: above the chunk size
+    for shorter in (False, True):
+        segs = ((b, t, t),) if not shorter else ((b - 1, t, t), (1, t // 2, t // 2))
+        w = scaled(base, seed=base.seed + 250, seq_segments=segs, pool_pages=24 * b, num_layers=1, attn_layer=0)
+        H.log(f"plan: GQA bf16 B={b} x {t} tokens (one shorter: {shorter}), N={n}, {cus} CUs")
+        case = H.make_decode_case(w, DEV)
+        outs, ws = H.alloc_outputs(case)
+        H.run_decode(case, outs, ws)
+        _sync()
+        pairs = n * b
+        total, pp, ch = _read_plan(ws, pairs)
+        _check_plan(total, pp, ch, _local_pages(case.seq_lens, ps, n))
+        if shorter:
+            assert (pp[:, 2] >= 2).any()
+        else:
+            assert total == pairs and (pp[:, 2] == 1).all()
+        H.check_decode(case, outs, requests=[0, b - 1], heads=list(range(4)))
+
+
 def test_decode_shard_subset_calls():
     # partials computed one shard range at a time equal the all-shard call
     base = get_workload("gqa_bf16_16x4k-32k")
