@@ -62,10 +62,12 @@ def kernel_source_hash(files):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_key: str, src_hash: str, launches_bytes: float):
+TRAFFIC_DB = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+
+
+def load_traffic(kernel_key: str, src_hash: str, launches_bytes: float, path: str = TRAFFIC_DB):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
@@ -424,7 +426,7 @@ CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",), "reshard_tokens_kernel": 
                                        "chunk_reduce_kernel")}
 
 
-def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: int) -> None:
+def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: int, path: str = TRAFFIC_DB) -> dict:
     """Scale the FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) of the dominant call's kernels by
     what the same counters read for the calibration copy, and store HBM bytes per launch."""
     import csv
@@ -452,23 +454,22 @@ def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: in
         return [rows[k] for k in sorted(rows)]
 
     out = {}
-    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        ds = per_dispatch(path, counter)
+    for counter, csv_path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        ds = per_dispatch(csv_path, counter)
         calib = [v for k, v in ds if "bitwise_not" in k]
         if len(calib) != 1:
-            sys.exit(f"{path}: expected one calibration copy dispatch, found {len(calib)}")
+            sys.exit(f"{csv_path}: expected one calibration copy dispatch, found {len(calib)}")
         scale = calib_mib * (1 << 20) / (calib[0] * 1024.0)  # true bytes per counted byte
         # the timed call's kernels, grouped per launch of the call: one group per launch of its main kernel
         mine = [(k, v) for k, v in ds if any(re.search(r"\b" + n + r"\b", k) for n in names)]
         main_name = [n for n in names if n not in ("plan_kernel", "chunk_reduce_kernel")]
         launches = sum(1 for k, _ in mine if any(n in k for n in main_name))
         if launches == 0:
-            sys.exit(f"{path}: no dispatch of {names}")
+            sys.exit(f"{csv_path}: no dispatch of {names}")
         out[counter] = {"kib_per_launch": sum(v for _, v in mine) / launches, "scale": scale,
                         "calib_kib": calib[0], "launches": launches}
     hbm = sum(out[c]["kib_per_launch"] * 1024.0 * out[c]["scale"] for c in out)
     key = f"{wl}:{call}" + (":token" if line["config"].get("ownership") == "token" else "")
-    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
             db = json.load(f)
@@ -484,6 +485,7 @@ def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: in
         json.dump(db, f, indent=1, sort_keys=True)
         f.write("\n")
     print(json.dumps({key: db[key]}))
+    return db[key]
 
 
 def main():
