@@ -437,18 +437,24 @@ def softmax_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, visible: np.ndarra
     visible: bool [R][T].  Returns (O [R][Dv], LSE [R]) with
     s_j = scale * q . k_j,  LSE = log sum_j exp(s_j),  O = sum_j exp(s_j - LSE) v_j
     over visible j; a row with nothing visible gives (0, -inf) (reading R11).
+    Consecutive rows that see the same tokens share one gather of those keys and
+    values and one matmul for their scores (column c of S holds row r0 + c's).
     """
     r_rows = q.shape[0]
     out = np.zeros((r_rows, v.shape[1]), dtype=np.float64)
     lse = np.full((r_rows,), NEG_INF, dtype=np.float64)
-    for r in range(r_rows):
-        idx = np.nonzero(visible[r])[0]
-        if idx.size == 0:
-            continue
-        s = scale * (k[idx] @ q[r])
-        m = s.max()
-        lse[r] = m + math.log(np.exp(s - m).sum())
-        out[r] = np.exp(s - lse[r]) @ v[idx]
+    r0 = 0
+    while r0 < r_rows:
+        r1 = r0 + 1
+        while r1 < r_rows and np.array_equal(visible[r1], visible[r0]):
+            r1 += 1
+        idx = np.nonzero(visible[r0])[0]
+        if idx.size:
+            s = scale * (k[idx] @ q[r0:r1].T)       # [visible tokens][rows]
+            m = s.max(axis=0)
+            lse[r0:r1] = m + np.log(np.exp(s - m).sum(axis=0))
+            out[r0:r1] = np.exp(s - lse[r0:r1]).T @ v[idx]
+        r0 = r1
     return out, lse
 
 
@@ -472,14 +478,18 @@ def request_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seq_len: int,
     t_all = np.arange(seq_len)
     out = np.zeros((q_len, hq, v.shape[2]), dtype=np.float64)
     lse = np.full((q_len, hq), NEG_INF, dtype=np.float64)
+    hs = list(range(hq) if heads is None else heads)
     for t, pos in enumerate(query_positions(seq_len, q_len)):
         vis = t_all <= pos
         if token_mask is not None:
             vis = vis & token_mask[:seq_len]
-        for h in (range(hq) if heads is None else heads):
-            kh = h // group  # reading R10
-            o, l = softmax_rows(q[t, h][None, :], k[kh, :seq_len], v[kh, :seq_len], vis[None, :], scale)
-            out[t, h], lse[t, h] = o[0], l[0]
+        for kh in range(hkv):
+            rows = [h for h in hs if h // group == kh]  # reading R10: query head h reads KV head h // group
+            if not rows:
+                continue
+            o, l = softmax_rows(q[t, rows], k[kh, :seq_len], v[kh, :seq_len],
+                                np.broadcast_to(vis, (len(rows), seq_len)), scale)
+            out[t, rows], lse[t, rows] = o, l
     return out, lse
 
 

@@ -831,3 +831,53 @@ def test_logical_kv_mla_vs_torch():
     ref = torch.cat(ref)[:T].numpy()
     assert k.shape == (1, T, 576) and v.shape == (1, T, 512)
     assert np.array_equal(k[0], ref) and np.array_equal(v[0], ref[:, :512])
+
+
+def test_softmax_rows_mixed_visibility_bruteforce_fsum():
+    """Rows with different visible sets (runs of equal sets, an empty row, a set that differs
+    from its neighbours) each match a math.fsum brute force of the definition; rows that share
+    a visible set are computed together, so a mix-up between them would show here."""
+    rng = np.random.default_rng(13)
+    T, dqk, dv, R = 9, 4, 3, 7
+    q = rng.standard_normal((R, dqk))
+    k = rng.standard_normal((T, dqk))
+    v = rng.standard_normal((T, dv))
+    vis = np.zeros((R, T), dtype=bool)
+    vis[0:3, :6] = True      # three rows, one set
+    vis[3, [1, 4, 8]] = True  # its own set
+    vis[5:7, 2:] = True      # row 4 sees nothing; rows 5-6 share a set
+    out, lse = O.softmax_rows(q, k, v, vis, 0.9)
+    for r in range(R):
+        js = [j for j in range(T) if vis[r, j]]
+        if not js:
+            assert lse[r] == float("-inf") and (out[r] == 0).all()
+            continue
+        s = {j: 0.9 * math.fsum(q[r, i] * k[j, i] for i in range(dqk)) for j in js}
+        z = math.fsum(math.exp(x) for x in s.values())
+        assert math.isclose(lse[r], math.log(z), rel_tol=1e-13)
+        for c in range(dv):
+            want = math.fsum(math.exp(s[j]) / z * v[j, c] for j in js)
+            assert math.isclose(out[r, c], want, rel_tol=1e-12, abs_tol=1e-14)
+
+
+def test_attention_gqa_head_subset_bruteforce_fsum():
+    """A subset of query heads spread over several KV heads (groups of 3): each listed head
+    matches the brute force with its own KV head; unlisted heads stay (0, -inf)."""
+    rng = np.random.default_rng(14)
+    T, dqk, dv, hq, hkv = 6, 3, 2, 6, 2
+    q, k, v = _rand_req(rng, T, 2, hq, hkv, dqk, dv)
+    heads = [0, 2, 4, 5]
+    out, lse = O.request_attention(q, k, v, T, 0.5, None, heads)
+    for t in range(2):
+        pos = T - 2 + t
+        for h in range(hq):
+            if h not in heads:
+                assert lse[t, h] == float("-inf") and (out[t, h] == 0).all()
+                continue
+            kh = h // 3
+            s = [0.5 * math.fsum(q[t, h, i] * k[kh, j, i] for i in range(dqk)) for j in range(pos + 1)]
+            z = math.fsum(math.exp(x) for x in s)
+            assert math.isclose(lse[t, h], math.log(z), rel_tol=1e-13)
+            for c in range(dv):
+                want = math.fsum(math.exp(s[j]) / z * v[kh, j, c] for j in range(pos + 1))
+                assert math.isclose(out[t, h, c], want, rel_tol=1e-12, abs_tol=1e-14)
