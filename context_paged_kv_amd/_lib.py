@@ -24,16 +24,22 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m context_paged_kv_amd.build` "
         "(this package has no fallback path)")
 
+# DCPKV_HOST_ONLY=1 binds a build of the host part alone (the page map, block
+# tables, filters and checks; used to run the host tests under the address and
+# undefined-behaviour sanitizers): no HIP runtime, and no device entry point.
+HOST_ONLY = os.environ.get("DCPKV_HOST_ONLY") == "1"
+
 # One HIP runtime per process: torch ships its own libamdhip64 (same SONAME as
 # ROCm's).  Importing torch first makes the loader bind this library to the
 # runtime torch already uses; loading ours first would bring up a second HIP/HSA
 # runtime that sees no device.
-import torch  # noqa: E402,F401
+if not HOST_ONLY:
+    import torch  # noqa: E402,F401
 
 _lib = C.CDLL(LIB_PATH)
 
 # the include/dcpkv.h revision these signatures follow; a library of another revision is refused
-ABI_VERSION = 5
+ABI_VERSION = 6
 _lib.dcpkv_abi_version.restype = C.c_int
 if _lib.dcpkv_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {_lib.dcpkv_abi_version()}, this binding needs {ABI_VERSION}: "
@@ -53,8 +59,8 @@ OWN_PAGE, OWN_TOKEN = 0, 1
 EXPORTED = (
     "dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
     "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
-    "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_path_entries", "kv_pack_pages",
-    "kv_unpack_pages", "kv_reshard_tokens",
+    "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_check_unique_pages",
+    "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
     "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge", "dcpkv_probe_mfma",
 )
 
@@ -90,39 +96,43 @@ _P = C.c_void_p
 _I32P = C.POINTER(C.c_int32)
 _I64P = C.POINTER(C.c_int64)
 
-_lib.dcpkv_last_error.restype = C.c_char_p
-_lib.dcpkv_last_error.argtypes = []
-_lib.dcpkv_abi_version.restype = C.c_int
-_lib.cp_layersplit_layer_range.argtypes = [C.c_int32, C.c_int32, C.c_int32, _I32P, _I32P]
-_lib.dcp_filter_kv_indices.argtypes = [_I64P, C.c_int64, C.c_int32, C.c_int32, _I64P, _I64P]
-_lib.dcp_pagemap_create.argtypes = [C.c_int32, C.c_int32, C.c_int64, _I64P, C.POINTER(_P)]
-_lib.dcp_pagemap_destroy.argtypes = [_P]
-_lib.dcp_pagemap_destroy.restype = None
-_lib.dcp_pagemap_num_free.argtypes = [_P]
-_lib.dcp_pagemap_num_free.restype = C.c_int64
-_lib.dcp_pagemap_alloc.argtypes = [_P, C.c_int64, _I64P, C.c_int64]
-_lib.dcp_pagemap_release.argtypes = [_P, _I64P, C.c_int64]
-_lib.dcp_build_block_tables.argtypes = [C.c_int32, C.c_int32, _I64P, _I64P, C.c_int32, C.c_int32, _I32P, _I32P]
-_lib.kv_reshard_pages.argtypes = [C.POINTER(kv_reshard_desc), C.POINTER(_P), C.POINTER(_P),
-                                  C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, C.c_int64, _P, _P]
-_lib.kv_path_entries.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, C.c_int64, C.c_int64, _P, _P, _P]
-_lib.kv_pack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, _P, _P, _P, C.c_int64, C.c_int64,
-                               _P, _P, _P, _P]
-_lib.kv_unpack_pages.argtypes = [C.POINTER(kv_reshard_desc), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, C.c_int64,
-                                 C.c_int64, _P, _P, _P]
-_lib.kv_reshard_tokens.argtypes = [C.POINTER(kv_token_reshard_desc), C.POINTER(_P), C.POINTER(_P), _P, _P,
-                                   C.c_int64, _P, C.c_int32, C.c_int64, _P, _P]
-_lib.dcp_decode_partial_workspace.argtypes = [C.POINTER(dcp_attn_desc), C.c_int64]
-_lib.dcp_decode_partial_workspace.restype = C.c_size_t
-_lib.dcp_decode_partial.argtypes = [C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P,
-                                    _P, C.c_int64, C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P]
-_lib.dcp_lse_merge.argtypes = [C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P]
-_lib.dcpkv_probe_mfma.argtypes = [C.c_int32, C.c_int32, _P, C.c_int64, _I64P, _P]
-for _f in ("cp_layersplit_layer_range", "dcp_filter_kv_indices", "dcp_pagemap_create",
-           "dcp_pagemap_alloc", "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages",
-           "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
-           "dcp_decode_partial", "dcp_lse_merge", "dcpkv_probe_mfma"):
-    getattr(_lib, _f).restype = C.c_int
+# (argtypes, restype) of every entry point; the host part comes first
+_SIGS = {
+    "dcpkv_last_error": ([], C.c_char_p),
+    "dcpkv_abi_version": ([], C.c_int),
+    "cp_layersplit_layer_range": ([C.c_int32, C.c_int32, C.c_int32, _I32P, _I32P], C.c_int),
+    "dcp_filter_kv_indices": ([_I64P, C.c_int64, C.c_int32, C.c_int32, _I64P, _I64P], C.c_int),
+    "dcp_pagemap_create": ([C.c_int32, C.c_int32, C.c_int64, _I64P, C.POINTER(_P)], C.c_int),
+    "dcp_pagemap_destroy": ([_P], None),
+    "dcp_pagemap_num_free": ([_P], C.c_int64),
+    "dcp_pagemap_alloc": ([_P, C.c_int64, _I64P, C.c_int64], C.c_int),
+    "dcp_pagemap_release": ([_P, _I64P, C.c_int64], C.c_int),
+    "dcp_build_block_tables": ([C.c_int32, C.c_int32, _I64P, _I64P, C.c_int32, C.c_int32, _I32P, _I32P], C.c_int),
+    "kv_check_unique_pages": ([_I64P, C.c_int64, C.c_int64, _I64P], C.c_int),
+    "kv_reshard_pages": ([C.POINTER(kv_reshard_desc), C.POINTER(_P), C.POINTER(_P), C.POINTER(_P), C.POINTER(_P),
+                          _P, _P, C.c_int64, C.c_int64, _P, _P, _P], C.c_int),
+    "kv_path_entries": ([C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, C.c_int64, C.c_int64, _P, _P, _P], C.c_int),
+    "kv_pack_pages": ([C.POINTER(kv_reshard_desc), C.c_int32, _P, _P, _P, _P, _P, C.c_int64, C.c_int64, _P, _P, _P,
+                       _P], C.c_int),
+    "kv_unpack_pages": ([C.POINTER(kv_reshard_desc), C.c_int32, C.c_int32, _P, _P, _P, _P, _P, C.c_int64, C.c_int64,
+                         _P, _P, _P], C.c_int),
+    "kv_reshard_tokens": ([C.POINTER(kv_token_reshard_desc), C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, _P,
+                           C.c_int32, C.c_int64, _P, _P], C.c_int),
+    "dcp_decode_partial_workspace": ([C.POINTER(dcp_attn_desc), C.c_int64], C.c_size_t),
+    "dcp_decode_partial": ([C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, C.c_int32,
+                            C.c_int32, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "dcp_lse_merge": ([C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P], C.c_int),
+    "dcpkv_probe_mfma": ([C.c_int32, C.c_int32, _P, C.c_int64, _I64P, _P], C.c_int),
+}
+HOST_SYMBOLS = ("dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
+                "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
+                "dcp_pagemap_release", "dcp_build_block_tables", "kv_check_unique_pages")
+for _name, (_args, _res) in _SIGS.items():
+    if HOST_ONLY and _name not in HOST_SYMBOLS:
+        continue
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
 
 
 def _check(rc: int) -> None:
@@ -262,14 +272,27 @@ def dcp_build_block_tables(dcp_size: int, pages_per_request: Sequence[Sequence[i
 def kv_reshard_pages(*, num_layers: int, dcp_size: int, page_bytes: int, src_pages: int, dst_pages: int,
                      src_pools, dst_pools, src_page_ids, dst_global_pages, first_uncached: int = 0,
                      dst_filter: int = -1, src_scales=None, dst_scales=None, bad_entries=None,
-                     num_pages: Optional[int] = None, stream=None) -> None:
+                     pages_per_dst=None, num_pages: Optional[int] = None, stream=None) -> None:
     """Enqueue the page-level 2D reshard (see include/dcpkv.h)."""
     desc = kv_reshard_desc(len(src_pools), num_layers, dcp_size, dst_filter, page_bytes, src_pages, dst_pages)
     n = src_page_ids.numel() if num_pages is None else num_pages
     _check(_lib.kv_reshard_pages(C.byref(desc), _ptr_array(src_pools), _ptr_array(dst_pools),
                                  _ptr_array(src_scales), _ptr_array(dst_scales), _dptr(src_page_ids),
                                  _dptr(dst_global_pages), n, first_uncached, _dptr(bad_entries),
-                                 _stream(stream)))
+                                 _dptr(pages_per_dst), _stream(stream)))
+
+
+def kv_check_unique_pages(dst_global_pages: Sequence[int], first_uncached: int = 0) -> int:
+    """-1 when the destination pages past first_uncached are distinct (host list), else raises
+    DcpkvError; the error's `first_duplicate` is the first list position that repeats a page."""
+    g = _i64(dst_global_pages)
+    dup = C.c_int64(-2)
+    rc = _lib.kv_check_unique_pages(_ptr64(g) if g.size else None, g.size, first_uncached, C.byref(dup))
+    if rc != DCPKV_OK:
+        err = DcpkvError(rc, _lib.dcpkv_last_error().decode(errors="replace"))
+        err.first_duplicate = dup.value
+        raise err
+    return dup.value
 
 
 def kv_reshard_tokens(*, num_layers: int, dcp_size: int, page_size: int, token_rows: int, row_bytes: int,
@@ -367,3 +390,4 @@ def dcpkv_probe_mfma(kind: int, iters: int, sink, stream=None) -> int:
     flops = C.c_int64(0)
     _check(_lib.dcpkv_probe_mfma(kind, iters, _dptr(sink), sink.numel(), C.byref(flops), _stream(stream)))
     return flops.value
+

@@ -86,6 +86,27 @@ def build(jobs: int = 0, verbose: bool = True) -> str:
     return LIB
 
 
+HOST_ASAN_LIB = os.path.join(BUILD, "libdcpkv_host_asan.so")
+# the host part (page map, block tables, filters, checks) alone, with the address and
+# undefined-behaviour sanitizers, for the host tests; plain g++, no device code
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build_host_asan() -> str:
+    """Compile csrc/host.cpp with g++ and the sanitizers into a host-only shared library."""
+    os.makedirs(BUILD, exist_ok=True)
+    gxx = shutil.which("g++") or "/usr/bin/g++"
+    tmp = HOST_ASAN_LIB + ".tmp"
+    cmd = [gxx, "-std=c++17", "-fPIC", "-shared", "-Wall", *SANITIZE_FLAGS, "-I", INCLUDE, "-I", CSRC,
+           os.path.join(CSRC, "host.cpp"), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host sanitizer build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, HOST_ASAN_LIB)
+    return HOST_ASAN_LIB
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=0)

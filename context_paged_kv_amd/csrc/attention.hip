@@ -15,6 +15,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "attn_common.h"
@@ -420,6 +423,14 @@ static int device_cus() {
   return cache[dev];
 }
 
+// DCPKV_MLA_SCORES selects the fp8 MLA kernel's score path: "auto" (default: exact fp16 scores
+// for the rows whose query has outliers, fp8 for the rest), "fp8" or "exact" for every row.
+static int mla_score_mode() {
+  const char* e = std::getenv("DCPKV_MLA_SCORES");
+  if (!e || !e[0] || !std::strcmp(e, "auto")) return 0;
+  return !std::strcmp(e, "fp8") ? 1 : (!std::strcmp(e, "exact") ? 2 : 0);
+}
+
 static int validate(const dcp_attn_desc& D) {
   const bool split = D.kv_layout == DCPKV_LAYOUT_SPLIT, mla = D.kv_layout == DCPKV_LAYOUT_MLA;
   if (!split && !mla) return set_error(DCPKV_EINVAL, "attn: unknown kv_layout %d", D.kv_layout);
@@ -438,8 +449,10 @@ static int validate(const dcp_attn_desc& D) {
     return set_error(DCPKV_EINVAL, "attn: MLA layout needs Dqk=576, Dv=512, one KV head");
   if (D.page_size < 1 || D.dcp_size < 1 || D.dcp_size > kMaxShards || D.batch < 1 ||
       D.q_len < 1 || D.max_local_pages < 1 || D.layer < 0 || D.layer >= D.num_layers ||
-      D.pages_per_layer < 1 || !(D.softmax_scale == D.softmax_scale))
+      D.pages_per_layer < 1)
     return set_error(DCPKV_EINVAL, "attn: bad geometry");
+  if (!(D.softmax_scale > 0.f) || !std::isfinite(D.softmax_scale))
+    return set_error(DCPKV_EINVAL, "attn: softmax_scale %g must be positive and finite", (double)D.softmax_scale);
   if (D.token_interleave != DCPKV_OWN_PAGE && D.token_interleave != DCPKV_OWN_TOKEN)
     return set_error(DCPKV_EINVAL, "attn: token_interleave must be %d or %d", DCPKV_OWN_PAGE, DCPKV_OWN_TOKEN);
   // the chunk reduction's grid is (pairs, row blocks): at most 65535 row blocks
@@ -521,6 +534,8 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
     return set_error(DCPKV_EINVAL, "attn: NULL pointer argument");
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return set_error(DCPKV_EINVAL, "attn: workspace must be 256-byte aligned");
+  if (!aligned16(q) || !aligned16(partial_out) || (reinterpret_cast<uintptr_t>(partial_lse) & 3u))
+    return set_error(DCPKV_EINVAL, "attn: q and partial_out must be 16-byte aligned, partial_lse 4-byte aligned");
   if (D.kv_layout == DCPKV_LAYOUT_MLA && !kv_scales)
     return set_error(DCPKV_EINVAL, "attn: MLA fp8 needs per-page scales");
   Geometry g;
@@ -531,10 +546,12 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   AttnParams p = {};
   p.q = q;
   for (int d = shard_begin; d < shard_begin + shard_count; ++d) {
-    if (!kv_pools[d]) return set_error(DCPKV_EINVAL, "attn: pool %d is NULL", d);
+    if (!kv_pools[d] || !aligned16(kv_pools[d]))
+      return set_error(DCPKV_EINVAL, "attn: pool %d is NULL or not 16-byte aligned", d);
     p.pools[d] = static_cast<const uint8_t*>(kv_pools[d]);
     if (D.kv_layout == DCPKV_LAYOUT_MLA) {
-      if (!kv_scales[d]) return set_error(DCPKV_EINVAL, "attn: scale array %d is NULL", d);
+      if (!kv_scales[d] || (reinterpret_cast<uintptr_t>(kv_scales[d]) & 3u))
+        return set_error(DCPKV_EINVAL, "attn: scale array %d is NULL or not 4-byte aligned", d);
       p.scales[d] = static_cast<const uint16_t*>(kv_scales[d]);
     }
   }
@@ -575,6 +592,7 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   p.rb_per_head = g.rb_per_head;
   p.scale = D.softmax_scale;
   p.tok_il = D.token_interleave;
+  p.mla_scores = mla_score_mode();
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int cus = device_cus();
 
@@ -632,6 +650,9 @@ extern "C" int dcp_lse_merge(int32_t dcp_size, int64_t rows, int32_t head_dim_v,
     return set_error(DCPKV_EINVAL, "merge: bad arguments (N=%d rows=%lld Dv=%d)", dcp_size,
                      (long long)rows, head_dim_v);
   if (rows == 0) return DCPKV_OK;
+  if (!aligned16(partial_out) || !aligned16(out) || (reinterpret_cast<uintptr_t>(partial_lse) & 3u) ||
+      (reinterpret_cast<uintptr_t>(out_lse) & 3u))
+    return set_error(DCPKV_EINVAL, "merge: partial_out and out must be 16-byte aligned, the LSE arrays 4-byte aligned");
   const int64_t blocks = (rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock;
   if (blocks > INT32_MAX / 256) return set_error(DCPKV_EINVAL, "merge: too many rows");
   hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)blocks), dim3(256), 0,

@@ -76,6 +76,7 @@ struct AttnParams {
   int32_t rb_per_head;  // head blocks per KV head
   float scale;
   int32_t tok_il;       // 1: token t on shard t mod N; 0: page ownership
+  int32_t mla_scores;   // fp8 MLA kernel: 0 exact scores for rows with outliers, 1 fp8 always, 2 exact always
 };
 
 // Tokens of (request with seq_len tokens) held by shard d, and its local pages.

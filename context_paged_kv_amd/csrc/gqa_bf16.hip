@@ -234,7 +234,11 @@ __global__ __launch_bounds__(64) void gqa_bf16_kernel(AttnParams p) {
       }
       o[mt] = acc;
     }
-    __builtin_amdgcn_wave_barrier();  // this page's LDS reads precede the next page's writes
+    // this page's LDS reads precede the next page's writes (the fences keep the compiler from
+    // moving one lane's accesses across the point where another lane's begin)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     jj = jn;
   }
 

@@ -7,6 +7,7 @@
 #include <cstring>
 #include <deque>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -31,7 +32,7 @@ using namespace dcpkv;
 
 extern "C" const char* dcpkv_last_error(void) { return g_err; }
 
-extern "C" int dcpkv_abi_version(void) { return 5; }
+extern "C" int dcpkv_abi_version(void) { return 6; }
 
 // [2DR] section 4.1: start_r = r*floor(L/N) + min(r, L mod N), end_r = start_{r+1}.
 extern "C" int cp_layersplit_layer_range(int32_t num_layers, int32_t num_sources, int32_t r,
@@ -217,6 +218,16 @@ extern "C" int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int
       if (nv > max_local_pages)
         return set_error(DCPKV_EINVAL, "block_tables: request %d needs more than %d local pages", b,
                          max_local_pages);
+      // the N pages of virtual page j must share one slot: every shard reads its tokens of that
+      // virtual page from the same slot
+      for (int64_t i = a; i < e; ++i) {
+        const int64_t head = a + ((i - a) / dcp_size) * dcp_size;
+        if (global_pages[i] / dcp_size != global_pages[head] / dcp_size)
+          return set_error(DCPKV_EINVAL,
+                           "block_tables: request %d page %lld (id %lld) is not in the slot of virtual page %lld "
+                           "(id %lld)", b, (long long)(i - a), (long long)global_pages[i],
+                           (long long)((i - a) / dcp_size), (long long)global_pages[head]);
+      }
       for (int32_t d = 0; d < dcp_size; ++d) {
         for (int64_t j = 0; j < nv; ++j)
           out_tables[((size_t)d * batch + b) * max_local_pages + j] = (int32_t)(global_pages[a + j * dcp_size] / dcp_size);
@@ -225,6 +236,33 @@ extern "C" int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int
     }
     if (out_counts)
       for (int32_t d = 0; d < dcp_size; ++d) out_counts[(size_t)d * batch + b] = cnt[d];
+  }
+  return DCPKV_OK;
+}
+
+// The reshard's precondition that no destination page is written twice in one call: the
+// destination global pages of the uncached entries are pairwise distinct.
+extern "C" int kv_check_unique_pages(const int64_t* dst_global_pages, int64_t num_pages, int64_t first_uncached,
+                                     int64_t* out_first_duplicate) {
+  if (num_pages < 0 || first_uncached < 0 || first_uncached > num_pages ||
+      (num_pages > first_uncached && !dst_global_pages))
+    return set_error(DCPKV_EINVAL, "check_unique: bad arguments");
+  if (out_first_duplicate) *out_first_duplicate = -1;
+  std::vector<std::pair<int64_t, int64_t>> v;  // (page, list position)
+  try {
+    v.reserve((size_t)(num_pages - first_uncached));
+    for (int64_t i = first_uncached; i < num_pages; ++i) v.emplace_back(dst_global_pages[i], i);
+  } catch (const std::bad_alloc&) {
+    return set_error(DCPKV_ENOMEM, "check_unique: out of host memory");
+  }
+  std::sort(v.begin(), v.end());
+  int64_t first = -1;  // the smallest list position whose page appeared earlier in the list
+  for (size_t k = 1; k < v.size(); ++k)
+    if (v[k].first == v[k - 1].first && (first < 0 || v[k].second < first)) first = v[k].second;
+  if (first >= 0) {
+    if (out_first_duplicate) *out_first_duplicate = first;
+    return set_error(DCPKV_EINVAL, "check_unique: destination page %lld appears twice (again at entry %lld)",
+                     (long long)dst_global_pages[first], (long long)first);
   }
   return DCPKV_OK;
 }

@@ -26,13 +26,17 @@
 //   * the 36 KB of fp8 codes come by LDS DMA into three buffers, page t + 1
 //     during step t.  LDS rows are 592 bytes (576 + 16 pad);
 //   * latent scores on v_mfma_scale_f32_16x16x128_f8f6f4 straight from the
-//     fp8 codes (unit scales): each query row is held as two e4m3 terms,
-//     hi = e4m3(q) and lo = e4m3(q - hi), whose sum is the bf16 query exactly
-//     (8 significant bits = 4 + 4), so no K conversion is needed; the rope
-//     dims use v_mfma_f32_16x16x32_f16 with K converted by
-//     v_cvt_scalef32_pk_f16_fp8 (exact).  The query is scaled by 2^qe per row
-//     so its largest entry lies in [128, 256); the factor leaves with the
-//     softmax scale;
+//     fp8 codes: each query row is held as two e4m3 terms per 32-dim block
+//     of the instruction's block scaling, hi = e4m3(2^k q) and
+//     lo = e4m3(16 (2^k q - hi)), with k chosen per block so that its largest
+//     entry lies in [128, 256) and the block's scale operands 2^-k and 2^-k-4
+//     taking the factors out inside the instruction.  A bf16 value has 8
+//     significant bits, each term 4, so hi + lo is the query itself for every
+//     entry within 2^13 of its block's largest; no K conversion is needed.  The
+//     rope dims use v_mfma_f32_16x16x32_f16 with K converted by
+//     v_cvt_scalef32_pk_f16_fp8 (exact).  The whole row is scaled by 2^qe
+//     (largest entry in [128, 256)) for the fp16 rope operand and the latent
+//     blocks' scales are relative to it; 2^qe leaves with the softmax scale;
 //   * online softmax in base 2 with a lazy offset per row: the score wavefront
 //     raises it only when the page's maximum exceeds it by more than 2^8, and
 //     the value wavefronts rescale accumulator rows only then.  The page scale
@@ -59,6 +63,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 constexpr int kMlaPage = 64;
@@ -81,6 +86,11 @@ constexpr int kSlots = kMlaPage * kSlotsPerRow;        // 2368
 constexpr int kLoadIters = (kSlots + kThreads - 1) / kThreads;  // copy instructions per wave and page
 constexpr int kPageBufs = 3;                           // page buffers in LDS
 constexpr float kTau = 8.f;                            // lazy-rescale threshold (log2 units)
+constexpr int kF16Steps = kMlaDim / 32;                // 18 f16 k-steps over all 576 dims (exact scores)
+// A row whose largest |q| exceeds kOutlier times its root mean square takes the exact score path
+// (fp16 operands): the fp8 instruction keeps about 2^-12 of the largest product of a block, so
+// a row with outliers would lose more than the scores may.
+constexpr float kOutlier = 16.f;
 constexpr float kLog2eM = 1.4426950408889634f;
 constexpr float kLn2M = 0.6931471805599453f;
 
@@ -124,17 +134,19 @@ __device__ __forceinline__ f16x8 cvt8(u32x2 x) {
 }
 
 // Four values (already scaled so |v| < 256) as two e4m3fn words: hi = e4m3(v),
-// lo = e4m3(v - hi).  A bf16 value has 8 significant bits, each e4m3 term 4, so
-// hi + lo is v itself for every value whose terms stay in the normal e4m3
-// range (the rest lose less than 2^-9 of the row's largest entry).
+// lo = e4m3(16 (v - hi)).  A bf16 value has 8 significant bits, each e4m3 term
+// 4 (the residual's 4 bits are scaled by 16 to keep them out of e4m3's
+// subnormal range), so hi + lo / 16 is v itself for every |v| >= 2^-6; smaller
+// values lose the bits below 2^-13, less than 2^-20 of a block whose largest
+// entry lies in [128, 256).
 __device__ __forceinline__ void split_e4m3(const float v[4], uint32_t& hi, uint32_t& lo) {
   int h = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
   h = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], h, true);
   float r[4];
-  r[0] = v[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0);
-  r[1] = v[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1);
-  r[2] = v[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2);
-  r[3] = v[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3);
+  r[0] = 16.f * (v[0] - __builtin_amdgcn_cvt_f32_fp8(h, 0));
+  r[1] = 16.f * (v[1] - __builtin_amdgcn_cvt_f32_fp8(h, 1));
+  r[2] = 16.f * (v[2] - __builtin_amdgcn_cvt_f32_fp8(h, 2));
+  r[3] = 16.f * (v[3] - __builtin_amdgcn_cvt_f32_fp8(h, 3));
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(r[0], r[1], 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(r[2], r[3], w, true);
   hi = (uint32_t)h;
@@ -152,6 +164,38 @@ __device__ __forceinline__ int mla_vtok(int g, int k) {
   return 4 * g + k + (k < 4 ? (g < 2 ? 0 : 16) : 4);
 }
 __device__ __forceinline__ int mla_tok(int tt, int m) { return mla_vtok(m >> 2, 4 * tt + (m & 3)); }
+
+// Eight bf16 values (one 16-byte load) times 2^e as eight fp16 values (exact for the range a
+// query row scaled to a largest entry in [128, 256) occupies).
+__device__ __forceinline__ f16x8 bf16x8_to_f16(u32x4 w, int e) {
+  f16x2 h2[4];
+#pragma unroll
+  for (int e2 = 0; e2 < 4; ++e2)
+    h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), e),
+                   (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), e)};
+  return __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
+                                 __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// The two halves of an eight-dword register group as fp16 operands, and back.
+__device__ __forceinline__ f16x8 f16_half(i32x8 v, int h) {
+  const i32x4 q = h ? __builtin_shufflevector(v, v, 4, 5, 6, 7) : __builtin_shufflevector(v, v, 0, 1, 2, 3);
+  return __builtin_bit_cast(f16x8, q);
+}
+__device__ __forceinline__ i32x8 f16_pair(f16x8 a, f16x8 b) {
+  return __builtin_shufflevector(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), 0, 1, 2, 3, 4, 5, 6,
+                                 7);
+}
+
+// Block scaling of v_mfma_scale_f32_16x16x128_f8f6f4 (lane layout checked with an in-bounds
+// probe): lane (g, c) holds 32 bytes of row (or column) c; its bytes [0, 16) belong to the
+// instruction's 32-element block g / 2 and bytes [16, 32) to block 2 + g / 2, so each block is
+// shared by lanes g and g ^ 1, and the scale of block b of row c is the operand of lane
+// (b, c).  Exponent k of a block with largest magnitude m (2^k m in [128, 256)), relative to
+// the row's 2^qe and kept within 2^120 of it (a block that far below its row adds nothing).
+__device__ __forceinline__ int mla_block_exp(float m, int qe) {
+  return m > 0.f ? min(7 - ilogbf(m), qe + 120) : qe;
+}
 
 // One LDS DMA piece: 16 bytes per lane from gptr to LDS address m0 + 16 lane (4 bytes per
 // lane for dma4).  Written as asm, so the compiler neither orders LDS reads behind it nor
@@ -330,45 +374,88 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
     // ======== scores and numerators of row tile rt = wave, all 64 tokens of page t in step t
     const int rt = wave;
     // The lane's query row 16 rt + c of the block.  Latent dims 128 ks + 32 g + [0, 32) go to
-    // the fp8 MFMA as two exact e4m3 terms (hi, lo); rope dims 512 + 32 ks + 8 g + [0, 8) go to
-    // the f16 MFMA.  Both are scaled by 2^qe (largest |q| of the row in [128, 256)); the factor
-    // is taken out of the scores with the softmax scale.
+    // the fp8 MFMA as two e4m3 terms (hi, lo) scaled per block of the instruction; rope dims
+    // 512 + 32 ks + 8 g + [0, 8) go to the f16 MFMA scaled by 2^qe (largest |q| of the row in
+    // [128, 256)).  The latent blocks' scale operands are relative to 2^qe, which is taken out
+    // of the scores with the softmax scale.
     const int r_s = hb * kMlaRowsPerBlock + 16 * rt + c;
     const bool row_ok = r_s < p.rows;
     const int lim = row_ok ? T - p.q_len + r_s / p.hq : -1;  // last visible position (below T <= INT32_MAX)
+    // fp8 path: latent terms and scales in qhi, qlo, qsc, rope in qrope.  Exact path: the fp16
+    // query of step kk in half kk & 1 of qhi[kk / 2] (kk < 8) or qlo[(kk - 8) / 2] (kk < 16), or
+    // in qrope[kk - 16].
     i32x8 qhi[kLatSteps], qlo[kLatSteps];
+    int qsc[kLatSteps];  // scale operand (E8M0) of the hi term's block this lane supplies; lo: qsc - 4
     f16x8 qrope[kRopeSteps];
     float sl2;
+    bool exact;  // this wavefront's rows take the exact (fp16) score path
     {
       const int t = row_ok ? r_s / p.hq : 0, h = row_ok ? r_s % p.hq : 0;
       const uint16_t* qr = static_cast<const uint16_t*>(p.q) + (((int64_t)b * p.q_len + t) * p.hq + h) * kMlaDim;
       u32x4 qraw[kQWords];
-      float mx = 0.f;
+      float mx = 0.f, ss = 0.f;
+      float mh[kLatSteps][2];  // largest |q| of the lane's first and second 16 latent dims per k-step
 #pragma unroll
       for (int i = 0; i < kQWords; ++i) {
         const uint16_t* src = i < kLatSteps * 4 ? qr + 128 * (i >> 2) + 32 * g + 8 * (i & 3)
                                                 : qr + kRope0 + 32 * (i - kLatSteps * 4) + 8 * g;
         const u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(src) : u32x4{0, 0, 0, 0};
         qraw[i] = w;
+        float m8 = 0.f;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          mx = fmaxf(mx, fmaxf(fabsf(__builtin_bit_cast(float, w[e2] << 16)),
-                               fabsf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u))));
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float lo = __builtin_bit_cast(float, w[e2] << 16), hi = __builtin_bit_cast(float, w[e2] & 0xFFFF0000u);
+          m8 = fmaxf(m8, fmaxf(fabsf(lo), fabsf(hi)));
+          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+        }
+        mx = fmaxf(mx, m8);
+        if (i < kLatSteps * 4) {
+          float& slot = mh[i >> 2][(i & 3) >> 1];
+          slot = (i & 1) ? fmaxf(slot, m8) : m8;
+        }
       }
       const float am = mgrp4_max(mx);
       const int qe = am > 0.f ? 7 - ilogbf(am) : 0;
+      const bool outlier_row = am * am * (float)kMlaDim > kOutlier * kOutlier * mgrp4_sum(ss);
+      exact = p.mla_scores == 2 || (p.mla_scores == 0 && __any(outlier_row));
+      if (exact) {  // fp16 query over all 576 dims, lane (g, c): dims 32 kk + 8 g + [0, 8) of step kk
 #pragma unroll
-      for (int ks = 0; ks < kLatSteps; ++ks) {
+        for (int kk = 0; kk < kF16Steps; ++kk) {
+          const u32x4 w = row_ok ? *reinterpret_cast<const u32x4*>(qr + 32 * kk + 8 * g) : u32x4{0, 0, 0, 0};
+          const f16x8 h = bf16x8_to_f16(w, qe);
+          if (kk < 2 * kLatSteps) {
+            qhi[kk >> 1] = (kk & 1) ? f16_pair(f16_half(qhi[kk >> 1], 0), h) : f16_pair(h, h);
+          } else if (kk < 4 * kLatSteps) {
+            const int j = (kk - 2 * kLatSteps) >> 1;
+            qlo[j] = (kk & 1) ? f16_pair(f16_half(qlo[j], 0), h) : f16_pair(h, h);
+          } else {
+            qrope[kk - 4 * kLatSteps] = h;
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < (exact ? 0 : kLatSteps); ++ks) {
+        // mf, ms: largest |q| of the blocks this lane's first and second halves belong to (each
+        // shared with lane g ^ 1); mine: that of block g, whose scale operand this lane supplies
+        // (lane 1 takes block 1, the first halves of lanes 2 and 3, from lane 2; lane 2 takes
+        // block 2, the second halves of lanes 0 and 1, from lane 1)
+        const float mf = fmaxf(mh[ks][0], __shfl_xor(mh[ks][0], 16, 64));
+        const float ms = fmaxf(mh[ks][1], __shfl_xor(mh[ks][1], 16, 64));
+        const float other = __shfl_xor(g == 2 ? mf : ms, 48, 64);  // lane 1 gets block 1, lane 2 block 2
+        const float mine = g == 0 ? mf : (g == 3 ? ms : other);
+        const int kf = mla_block_exp(mf, qe), ksec = mla_block_exp(ms, qe);
+        qsc[ks] = 127 + qe - mla_block_exp(mine, qe);
         i32x8 hv, lv;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {  // 8 dims per u32x4 -> two words of four e4m3 codes
           const u32x4 w = qraw[4 * ks + j];
+          const int kx = j < 2 ? kf : ksec;
 #pragma unroll
           for (int hw = 0; hw < 2; ++hw) {
-            const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), qe),
-                                ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), qe),
-                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), qe),
-                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), qe)};
+            const float v[4] = {ldexpf(__builtin_bit_cast(float, w[2 * hw] << 16), kx),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw] & 0xFFFF0000u), kx),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] << 16), kx),
+                                ldexpf(__builtin_bit_cast(float, w[2 * hw + 1] & 0xFFFF0000u), kx)};
             uint32_t hw32, lw32;
             split_e4m3(v, hw32, lw32);
             hv[2 * j + hw] = (int)hw32;
@@ -379,17 +466,7 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
         qlo[ks] = lv;
       }
 #pragma unroll
-      for (int ks = 0; ks < kRopeSteps; ++ks) {
-        const u32x4 w = qraw[kLatSteps * 4 + ks];
-        f16x2 h2[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2)
-          h2[e2] = f16x2{(_Float16)ldexpf(__builtin_bit_cast(float, w[e2] << 16), qe),
-                         (_Float16)ldexpf(__builtin_bit_cast(float, w[e2] & 0xFFFF0000u), qe)};
-        qrope[ks] = __builtin_shufflevector(__builtin_shufflevector(h2[0], h2[1], 0, 1, 2, 3),
-                                            __builtin_shufflevector(h2[2], h2[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
-                                            6, 7);
-      }
+      for (int ks = 0; ks < (exact ? 0 : kRopeSteps); ++ks) qrope[ks] = bf16x8_to_f16(qraw[kLatSteps * 4 + ks], qe);
       sl2 = p.scale * kLog2eM / ldexpf(1.f, qe);
     }
     float ref_s = kNegInf;  // the row's exponent offset (log2 units), the same in its four lanes
@@ -411,31 +488,47 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
         f32x4 sc[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (exact) {
 #pragma unroll
-        for (int ks = 0; ks < kLatSteps; ++ks) {
-          i32x8 a[4];
+          for (int kk = 0; kk < kF16Steps; ++kk) {
+            const f16x8 bq = kk < 2 * kLatSteps ? f16_half(qhi[kk >> 1], kk & 1)
+                             : kk < 4 * kLatSteps ? f16_half(qlo[(kk - 2 * kLatSteps) >> 1], kk & 1)
+                                                  : qrope[kk - 4 * kLatSteps];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint8_t* kp = cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + 128 * ks + 32 * g;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
-            a[u] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            for (int u = 0; u < 4; ++u) {
+              const f16x8 a = cvt8(*reinterpret_cast<const u32x2*>(
+                  cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + 32 * kk + 8 * g));
+              sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bq, sc[u], 0, 0, 0);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < kLatSteps; ++ks) {
+            i32x8 a[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint8_t* kp = cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + 128 * ks + 32 * g;
+              const u32x4 a0 = *reinterpret_cast<const u32x4*>(kp);
+              const u32x4 a1 = *reinterpret_cast<const u32x4*>(kp + 16);
+              a[u] = __builtin_bit_cast(i32x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u], qhi[ks], sc[u], 0, 0, 0, 127, 0, qsc[ks]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u], qlo[ks], sc[u], 0, 0, 0, 127, 0,
+                                                                       qsc[ks] - 4);
           }
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u], qhi[ks], sc[u], 0, 0, 0, 127, 0, 127);
+          for (int ks = 0; ks < kRopeSteps; ++ks)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            sc[u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[u], qlo[ks], sc[u], 0, 0, 0, 127, 0, 127);
+            for (int u = 0; u < 4; ++u) {
+              const f16x8 a = cvt8(*reinterpret_cast<const u32x2*>(
+                  cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + kRope0 + 32 * ks + 8 * g));
+              sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[ks], sc[u], 0, 0, 0);
+            }
         }
-#pragma unroll
-        for (int ks = 0; ks < kRopeSteps; ++ks)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const f16x8 a = cvt8(*reinterpret_cast<const u32x2*>(
-                cur + (32 * (u >> 1) + mla_tok(u & 1, c)) * kRawStride + kRope0 + 32 * ks + 8 * g));
-            sc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, qrope[ks], sc[u], 0, 0, 0);
-          }
         // ---- numerators (lane: row 16 rt + c, tokens 32 th + mla_vtok(g, [0, 8)) of each half)
         const float f = sl2 * ps;
         const bool full = exists && mla_llim(T - p.q_len, jj, tok_il, nsh, d) >= kMlaPage - 1;
@@ -478,9 +571,13 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
         l_s += psum * ps_ref * __builtin_amdgcn_rcpf(ps);  // P carries ps / ps_ref; the denominator not
         if (g == 0) s_off[t & 1][16 * rt + c] = ref_s;
       }
-      // this step's LDS writes are done and page t + 1 has landed; then its tail, if any, is cleared
+      // this step's LDS writes are done and page t + 1 has landed; then its tail, if any, is cleared.
+      // The workgroup fences keep the compiler from moving LDS accesses across the barrier (the
+      // explicit wait already covers what they would make the hardware wait for).
       __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if (t + 1 < np) MLA_ZERO_TAIL(t + 1);
     }
     const float lh = mgrp4_sum(l_s);
@@ -555,7 +652,9 @@ __global__ __launch_bounds__(kThreads) void mla_fp8_kernel(AttnParams p) {
         }
       }
       __builtin_amdgcn_s_waitcnt(0);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       if (t + 1 < np) MLA_ZERO_TAIL(t + 1);
     }
     __syncthreads();  // the scorers' final denominators

@@ -88,3 +88,4 @@ extern "C" int dcpkv_probe_mfma(int32_t kind, int32_t iters, float* sink, int64_
   *out_flops = (int64_t)grid * (kProbeThreads / 64) * (int64_t)iters * kProbeChains * per_mfma;
   return DCPKV_OK;
 }
+

@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
+#include <vector>
 
 #include "common.h"
 
@@ -33,6 +35,7 @@ struct ReshardArgs {
   const int32_t* src_ids;
   const int64_t* dst_ids;
   int32_t* bad;
+  int64_t* per_dst;    // entries written per destination (nullable)
   int64_t page_bytes;
   int64_t seg_bytes;   // bytes per segment (a multiple of 16)
   int64_t src_pages;   // S
@@ -112,6 +115,7 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a)
       continue;
     }
     if (a.dst_filter >= 0 && d != a.dst_filter) continue;
+    if (a.per_dst && layer == 0 && sg == 0 && threadIdx.x == 0) atomicAdd((unsigned long long*)&a.per_dst[d], 1ull);
     int r, begin;
     layer_owner(layer, a.num_layers, a.num_sources, r, begin);
     const int64_t off = (int64_t)sg * a.seg_bytes;
@@ -243,6 +247,28 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenRe
   }
 }
 
+// DCPKV_CHECK_PRECONDITIONS=1: the reshard calls copy the destination page list to the host
+// (synchronising the caller's stream) and refuse a list that names a page twice.
+static bool check_preconditions() {
+  const char* e = std::getenv("DCPKV_CHECK_PRECONDITIONS");
+  return e && e[0] == '1';
+}
+
+static int check_unique_on_device(const int64_t* dst_ids, int64_t num_pages, int64_t first, void* stream,
+                                  const char* who) {
+  std::vector<int64_t> h((size_t)num_pages);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(h.data(), dst_ids, (size_t)num_pages * sizeof(int64_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return set_error(DCPKV_EDEVICE, "%s: copying the page list for the precondition check failed", who);
+  int64_t dup = -1;
+  if (kv_check_unique_pages(h.data(), num_pages, first, &dup) != DCPKV_OK)
+    return set_error(DCPKV_EINVAL, "%s: destination page %lld appears twice (again at entry %lld)", who,
+                     (long long)h[(size_t)dup], (long long)dup);
+  return DCPKV_OK;
+}
+
 static int device_cus_reshard() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -259,7 +285,8 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
                                 void* const* dst_pools, const void* const* src_scales,
                                 void* const* dst_scales, const int32_t* src_page_ids,
                                 const int64_t* dst_global_pages, int64_t num_pages,
-                                int64_t first_uncached, int32_t* bad_entries, void* stream) {
+                                int64_t first_uncached, int32_t* bad_entries, int64_t* pages_per_dst,
+                                void* stream) {
   if (!desc || !src_pools || !dst_pools) return set_error(DCPKV_EINVAL, "reshard: NULL argument");
   const kv_reshard_desc& D = *desc;
   if (D.num_sources < 1 || D.num_sources > kMaxSources || D.num_layers < D.num_sources ||
@@ -280,6 +307,12 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   if (work == 0) return DCPKV_OK;
   if (!src_page_ids || !dst_global_pages)
     return set_error(DCPKV_EINVAL, "reshard: NULL page id arrays");
+  if (pages_per_dst && (reinterpret_cast<uintptr_t>(pages_per_dst) & 7u))
+    return set_error(DCPKV_EINVAL, "reshard: pages_per_dst must be 8-byte aligned");
+  if (check_preconditions()) {
+    const int rc = check_unique_on_device(dst_global_pages, num_pages, first_uncached, stream, "reshard");
+    if (rc) return rc;
+  }
   ReshardArgs a = {};
   for (int r = 0; r < D.num_sources; ++r) {
     if (!src_pools[r] || !aligned16(src_pools[r]))
@@ -303,6 +336,7 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   a.src_ids = src_page_ids;
   a.dst_ids = dst_global_pages;
   a.bad = bad_entries;
+  a.per_dst = pages_per_dst;
   a.page_bytes = D.page_bytes;
   {  // near-equal segments of at most 36 KB, 16-byte multiples, covering the page exactly
     const int64_t nseg = (D.page_bytes + kReshardSegMax - 1) / kReshardSegMax;
@@ -352,6 +386,10 @@ extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* 
   const int64_t work = num_pages - first_uncached;
   if (work == 0) return DCPKV_OK;
   if (!src_page_ids || !dst_global_pages) return set_error(DCPKV_EINVAL, "token reshard: NULL page id arrays");
+  if (check_preconditions()) {
+    const int rc = check_unique_on_device(dst_global_pages, num_pages, first_uncached, stream, "token reshard");
+    if (rc) return rc;
+  }
   TokenReshardArgs a = {};
   a.req_off = request_offsets;
   a.num_req = request_offsets ? num_requests : 1;

@@ -132,7 +132,8 @@ DCPKV_API int dcp_pagemap_release(dcp_pagemap* pm, const int64_t* global_pages, 
  *     j*N + d (the pages d owns, in sequence order);
  *   token_interleave = DCPKV_OWN_TOKEN ([SGL]: token t on rank t mod N): local
  *     page j of every shard holds that shard's tokens of virtual page j, so every
- *     shard lists v_0 .. v_{ceil(P/N)-1}.
+ *     shard lists v_0 .. v_{ceil(P/N)-1}; the N pages of virtual page j must
+ *     share its slot (g_{jN+d} div N == g_{jN} div N), EINVAL otherwise.
  * EINVAL if a count exceeds max_local_pages or token_interleave is neither. */
 DCPKV_API int dcp_build_block_tables(int32_t dcp_size, int32_t batch, const int64_t* global_pages,
                            const int64_t* page_offsets, int32_t max_local_pages, int32_t token_interleave,
@@ -175,14 +176,33 @@ typedef struct {
  * call (each (layer, page) then has one writer).
  * bad_entries (device int32 [1], nullable): incremented by one for each
  * (layer, entry) whose ids fall outside [0, S) or [0, M*N); such entries are
- * skipped, never written.  Pointers must be 16-byte aligned.
+ * skipped, never written.
+ * pages_per_dst (device int64 [N], nullable, 8-byte aligned): pages_per_dst[d]
+ * is incremented by the number of entries written to destination d (each on
+ * every layer), the per-destination page count of the transfer worker's
+ * "pages: 256 -> 64" log line (section 6.3); the caller zeroes it first.
+ * Pointers must be 16-byte aligned.
+ * With the environment variable DCPKV_CHECK_PRECONDITIONS=1 the call first
+ * copies dst_global_pages to the host (synchronising `stream`) and returns
+ * EINVAL, writing nothing, if a page repeats among the uncached entries.
  * EINVAL on a bad descriptor, NULL pool pointers, page_bytes % 16 != 0,
  * first_uncached outside [0, num_pages] or misaligned pointers. */
 DCPKV_API int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* src_pools,
                      void* const* dst_pools, const void* const* src_scales,
                      void* const* dst_scales, const int32_t* src_page_ids,
                      const int64_t* dst_global_pages, int64_t num_pages,
-                     int64_t first_uncached, int32_t* bad_entries, void* stream);
+                     int64_t first_uncached, int32_t* bad_entries, int64_t* pages_per_dst,
+                     void* stream);
+
+/* The reshard's one-writer precondition, on the host: the destination global
+ * pages dst_global_pages[first_uncached .. num_pages) (host) are pairwise
+ * distinct, so every (layer, destination page) of a call has one writer
+ * ([2DR] section 6.2, the guarantee that each rank's pages are written once).
+ * Returns OK, or EINVAL with *out_first_duplicate (host, nullable) set to the
+ * first list position whose page appeared earlier (-1 when none).  EINVAL also
+ * on bad sizes or a NULL list. */
+DCPKV_API int kv_check_unique_pages(const int64_t* dst_global_pages, int64_t num_pages,
+                                    int64_t first_uncached, int64_t* out_first_duplicate);
 
 /* ------------------------------------------------------------------------ *
  * (1c) Token scatter reshard for pools under token ownership                *
@@ -225,7 +245,8 @@ typedef struct {
  * whose source id is outside [0, S), whose virtual page slot is outside
  * [0, M), or that no request of request_offsets contains consistently; such
  * entries are skipped.  Every access stays in bounds whatever the id arrays
- * and offsets hold.  EINVAL on a bad descriptor, NULL or misaligned pools,
+ * and offsets hold.  DCPKV_CHECK_PRECONDITIONS=1 checks the destination pages
+ * for repeats first, as in kv_reshard_pages.  EINVAL on a bad descriptor, NULL or misaligned pools,
  * first_uncached outside [0, num_pages], num_requests < 0, num_requests > 1
  * without offsets, or offsets with num_requests < 1. */
 DCPKV_API int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* const* src_pools,
@@ -307,7 +328,7 @@ typedef struct {
   int32_t layer;           /* layer to read from the pools, < num_layers */
   int32_t num_layers;      /* L: layers in each pool */
   int64_t pages_per_layer; /* M: local slots per layer in each pool */
-  float softmax_scale;     /* scores are softmax_scale * q . k */
+  float softmax_scale;     /* scores are softmax_scale * q . k; positive and finite */
   int32_t token_interleave; /* DCPKV_OWN_PAGE (0): page p of a sequence lives on shard
                                p mod N ([2DR] section 5.1).  DCPKV_OWN_TOKEN (1): token t
                                lives on shard t mod N, local token t div N ([SGL], the
@@ -339,7 +360,8 @@ DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t
  *
  * q: [B][q_len][Hq][head_dim_qk] (f32 or bf16).  kv_pools: host array [N] of
  * device pointers to DCP pools; kv_scales: host array [N] of device pointers
- * to bf16 [L][M] page scales (MLA), else NULL.  block_tables: device int32
+ * to bf16 [L][M] page scales (MLA), else NULL; page scales must be positive
+ * and finite (a zero or negative scale gives undefined results).  block_tables: device int32
  * [N][B][max_local_pages] as built by dcp_build_block_tables: entry j of
  * (d, b) is the slot of shard d's local page j, which holds sequence page
  * j*N + d (DCPKV_OWN_PAGE) or the tokens (j*page_size + x)*N + d, x < page_size
@@ -347,10 +369,13 @@ DCPKV_API size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_t
  * [B], each T_b >= q_len.  Out: partial_out fp32 [N][B][q_len][Hq][head_dim_v],
  * partial_lse fp32 [N][B][q_len][Hq] (natural log); only the requested shards'
  * slices are written.  workspace: device, >= dcp_decode_partial_workspace()
- * bytes, 256-byte aligned; its contents need not be initialised.
+ * bytes, 256-byte aligned; its contents need not be initialised.  q, the pools
+ * and partial_out must be 16-byte aligned, partial_lse and the scale arrays
+ * 4-byte aligned.
  * A table entry outside [0, M) is treated as a page of no tokens.
  * Limits: q_len * Hq <= 262,140 query rows per request, B * N <= 2^24.
- * EINVAL on a bad descriptor/pointer, a limit exceeded or too small a
+ * EINVAL on a bad descriptor/pointer (a softmax_scale that is not positive and
+ * finite included), a misaligned pointer, a limit exceeded or too small a
  * workspace (every descriptor that passes these checks has a kernel). */
 DCPKV_API int dcp_decode_partial(const dcp_attn_desc* desc, const void* q, const void* const* kv_pools,
                        const void* const* kv_scales, const int32_t* block_tables,
@@ -371,7 +396,8 @@ DCPKV_API int dcp_decode_partial(const dcp_attn_desc* desc, const void* q, const
  * out fp32 [rows][head_dim_v]; out_lse fp32 [rows], nullable.  Rows whose
  * every LSE_d is -inf give out = 0, LSE = -inf.  The result does not depend on
  * the order of the shards beyond rounding.  out may not alias the inputs.
- * EINVAL on bad sizes or NULL pointers. */
+ * partial_out and out must be 16-byte aligned, the LSE arrays 4-byte aligned.
+ * EINVAL on bad sizes, NULL or misaligned pointers. */
 DCPKV_API int dcp_lse_merge(int32_t dcp_size, int64_t rows, int32_t head_dim_v, const float* partial_out,
                   const float* partial_lse, float* out, float* out_lse, void* stream);
 

@@ -238,13 +238,29 @@ def lse_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
         return np.where(both_inf, 0.0, np.abs(got - ref))
 
 
+def elem_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-element error |got_i - ref_i| / max_j |ref_j| over each row (the last axis); rows
+    whose reference is all zero give the plain absolute error."""
+    den = np.abs(ref).max(axis=-1, keepdims=True)
+    return np.abs(got - ref) / np.where(den > 0, den, 1.0)
+
+
 def check_rows(name, got_o, got_l, ref_o, ref_l, tol_o, tol_l):
-    eo = rel_row_err(np.asarray(got_o, np.float64), ref_o)
+    """Rows of outputs (last axis) and their LSEs against the oracle: every element within
+    tol_o of its row's largest reference magnitude, every row's relative L2 error within
+    tol_o, every |LSE error| within tol_l.  Returns the worst (row L2, LSE, element) errors."""
+    got_o = np.asarray(got_o, np.float64)
+    eo = rel_row_err(got_o, ref_o)
     el = lse_err(np.asarray(got_l, np.float64), ref_l)
-    assert np.isfinite(eo).all(), f"{name}: non-finite output error"
-    assert eo.max() <= tol_o, f"{name}: max relative row error {eo.max():.3e} > {tol_o}"
-    assert el.max() <= tol_l, f"{name}: max |LSE error| {el.max():.3e} > {tol_l}"
-    return float(eo.max()), float(el.max())
+    ee = elem_err(got_o, ref_o)
+    assert np.isfinite(eo).all() and np.isfinite(ee).all(), f"{name}: non-finite output error"
+    if ee.size and ee.max() > tol_o:
+        at = np.unravel_index(int(np.argmax(ee)), ee.shape)
+        raise AssertionError(f"{name}: element {at} off by {ee.max():.3e} of its row's largest value > {tol_o}")
+    assert eo.size == 0 or eo.max() <= tol_o, f"{name}: max relative row error {eo.max():.3e} > {tol_o}"
+    assert el.size == 0 or el.max() <= tol_l, f"{name}: max |LSE error| {el.max():.3e} > {tol_l}"
+    return (float(eo.max()) if eo.size else 0.0, float(el.max()) if el.size else 0.0,
+            float(ee.max()) if ee.size else 0.0)
 
 
 def tolerance(w: Workload):
@@ -259,17 +275,111 @@ def check_decode(case: DecodeCase, outs: DecodeOut, requests=None, heads=None, s
     n = w.dcp_size
     shards = range(n) if shards is None else shards
     hs = list(range(w.num_q_heads)) if heads is None else list(heads)
-    worst = [0.0, 0.0]
+    worst = [0.0, 0.0, 0.0]
     for b in (range(w.num_requests) if requests is None else requests):
         (po, pl), (uo, ul) = oracle_request(case, b, heads=hs)
         for d in shards:
             e = check_rows(f"partial d={d} b={b}", outs.partial_out[d, b][:, hs].cpu().numpy(),
                            outs.partial_lse[d, b][:, hs].cpu().numpy(), po[d][:, hs], pl[d][:, hs], tol_o, tol_l)
-            worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+            worst = [max(x, y) for x, y in zip(worst, e)]
         if shards == range(n):
             e = check_rows(f"merged b={b}", outs.out[b][:, hs].cpu().numpy(), outs.lse[b][:, hs].cpu().numpy(),
                            uo[:, hs], ul[:, hs], tol_o, tol_l)
-            worst = [max(worst[0], e[0]), max(worst[1], e[1])]
+            worst = [max(x, y) for x, y in zip(worst, e)]
+    return worst
+
+
+def fmt_worst(worst) -> str:
+    return f"worst rel row {worst[0]:.2e}, lse {worst[1]:.2e}, element {worst[2]:.2e}"
+
+
+def request_geo(case: DecodeCase) -> dict:
+    w = case.w
+    return {"layout": w.layout, "kv_dtype": w.kv_dtype, "num_kv_heads": w.num_kv_heads,
+            "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v, "page_size": w.page_size,
+            "dcp_size": w.dcp_size, "num_q_heads": w.num_q_heads, "q_len": w.q_len,
+            "softmax_scale": w.softmax_scale, "own": "token" if case.own else "page"}
+
+
+def check_decode_parallel(case: DecodeCase, outs: DecodeOut, heads_of, requests=None, layer=None, workers=None,
+                          pages_of=None, label=""):
+    """check_decode at full size: the oracle runs per request in spawned worker processes (numpy
+    and the oracle only, one BLAS thread each), fed with host copies of the request's pages that
+    this process gathers; heads_of(b) lists the query heads checked for request b.  pages_of(b),
+    if given, returns (page bytes, page scales) of request b in sequence order instead of the
+    pools' (e.g. the source pages of a reshard).  Every shard's partial and the merged output
+    of those rows are compared element by element.  Returns the worst errors."""
+    import multiprocessing as mp
+    import os
+    from tests import oracle_workers as OW
+
+    w = case.w
+    lay = case.layer if layer is None else layer
+    tol_o, tol_l = tolerance(w)
+    reqs = list(range(w.num_requests) if requests is None else requests)
+    workers = workers or max(1, min(16, len(os.sched_getaffinity(0))))
+    got_po = outs.partial_out.cpu().numpy()
+    got_pl = outs.partial_lse.cpu().numpy()
+    got_o = outs.out.cpu().numpy()
+    got_l = outs.lse.cpu().numpy()
+    geo = request_geo(case)
+    worst = [0.0, 0.0, 0.0]
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+
+    def task(b):
+        hs = list(heads_of(b))
+        pages = case.pages[b]
+        pages_h = scales_h = by_slot = None
+        if pages_of is not None:
+            pages_h, scales_h = pages_of(b)
+        elif case.own:
+            n = w.dcp_size
+            vslots = [O.dcp_local_slot(int(pages[j]), n) for j in range(0, len(pages), n)]
+            sl = torch.tensor(vslots, dtype=torch.int64, device=case.pools[0].device)
+            by_slot = {}
+            for d in range(n):
+                pb = case.pools[d][lay].index_select(0, sl).cpu().numpy()
+                sc = (case.scales[d][lay].index_select(0, sl).cpu().numpy().astype(np.int64) & 0xFFFF
+                      if case.scales is not None else None)
+                for i, s_ in enumerate(vslots):
+                    by_slot[(d, s_)] = (pb[i], None if sc is None else int(sc[i]))
+        else:
+            pages_h, scales_h = gather_request_pages(case.pools, case.scales, pages, w.dcp_size, lay)
+        return (geo, pages_h, scales_h, by_slot, pages, int(case.seq_lens[b]), q_host(case, b), hs), hs
+
+    def compare(b, hs, res):
+        nonlocal worst
+        po, pl, uo, ul = res
+        for d in range(w.dcp_size):
+            e = check_rows(f"{label}partial d={d} b={b}", got_po[d, b][:, hs], got_pl[d, b][:, hs], po[d], pl[d],
+                           tol_o, tol_l)
+            worst = [max(x, y) for x, y in zip(worst, e)]
+        e = check_rows(f"{label}merged b={b}", got_o[b][:, hs], got_l[b][:, hs], uo, ul, tol_o, tol_l)
+        worst = [max(x, y) for x, y in zip(worst, e)]
+
+    try:
+        with mp.get_context("spawn").Pool(workers) as pool:
+            pending = []
+            done = 0
+            for b in reqs:
+                args, hs = task(b)
+                pending.append((b, hs, pool.apply_async(OW.oracle_request_rows, (args,))))
+                while len(pending) > workers:  # bounded host memory: one task queued per worker
+                    b0, hs0, r0 = pending.pop(0)
+                    compare(b0, hs0, r0.get())
+                    done += 1
+                    if done % 8 == 0:
+                        log(f"  {label}{done} of {len(reqs)} requests match the oracle ({fmt_worst(worst)})")
+            for b0, hs0, r0 in pending:
+                compare(b0, hs0, r0.get())
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
     return worst
 
 
@@ -331,7 +441,8 @@ def make_reshard_case(w: Workload, device="cuda", seq_lens=None, requests=None, 
                        dst_ids=dst_ids, first_uncached=c, src_pages=S)
 
 
-def run_reshard(rc: ReshardCase, dst_filter=-1, bad=None, src_ids=None, dst_ids=None, stream=None):
+def run_reshard(rc: ReshardCase, dst_filter=-1, bad=None, src_ids=None, dst_ids=None, stream=None,
+                pages_per_dst=None):
     w = rc.w
     dev = rc.src_pools[0].device
     si = torch.from_numpy((rc.src_ids if src_ids is None else src_ids).astype(np.int32)).to(dev)
@@ -340,7 +451,7 @@ def run_reshard(rc: ReshardCase, dst_filter=-1, bad=None, src_ids=None, dst_ids=
                        src_pages=rc.src_pages, dst_pages=w.pool_pages, src_pools=rc.src_pools,
                        dst_pools=rc.dst_pools, src_page_ids=si, dst_global_pages=di,
                        first_uncached=rc.first_uncached, dst_filter=dst_filter, src_scales=rc.src_scales,
-                       dst_scales=rc.dst_scales, bad_entries=bad, stream=stream)
+                       dst_scales=rc.dst_scales, bad_entries=bad, pages_per_dst=pages_per_dst, stream=stream)
     return si, di
 
 

@@ -65,6 +65,18 @@ def request_rows(args):
     return rows, done
 
 
+def oracle_request_rows(args):
+    """The oracle's per-shard partials and unsharded attention of one request, for the listed
+    heads only: (partial O [N][q_len][H'][Dv], partial LSE [N][q_len][H'], O [q_len][H'][Dv],
+    LSE [q_len][H'])."""
+    geo, pages_h, scales_h, host_by_slot, global_pages, seq_len, q, heads = args
+    k, v = _logical_kv(geo, pages_h, scales_h, host_by_slot, global_pages, seq_len)
+    po, pl = O.request_partials(q, k, v, seq_len, geo["softmax_scale"], global_pages, geo["page_size"],
+                                geo["dcp_size"], heads=heads, own=geo["own"])
+    uo, ul = O.request_attention(q, k, v, seq_len, geo["softmax_scale"], None, heads)
+    return po[:, :, heads], pl[:, :, heads], uo[:, heads], ul[:, heads]
+
+
 def warm(_):
     """No work: lets the pool start its processes before the timed region."""
     return 0

@@ -13,6 +13,9 @@ import oracle as O
 from context_paged_kv_amd import _lib as L
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "dcpkv.h")
+# under DCPKV_HOST_ONLY=1 the binding loads the host part alone (the sanitizer build): the tests
+# of device entry points' argument checks need the whole library
+device_symbols = pytest.mark.skipif(L.HOST_ONLY, reason="host-only build of the library")
 
 
 def declared_symbols():
@@ -24,12 +27,14 @@ def test_library_exports_every_declared_symbol():
     names = declared_symbols()
     assert len(names) >= 14
     lib = C.CDLL(L.LIB_PATH)
-    for n in names:
+    for n in (L.HOST_SYMBOLS if L.HOST_ONLY else names):
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTED)
-    assert K.dcpkv_abi_version() == 5 == L.ABI_VERSION
+    assert set(L.HOST_SYMBOLS) <= set(names)
+    assert K.dcpkv_abi_version() == 6 == L.ABI_VERSION
 
 
+@device_symbols
 def test_graft_build_entry_accepts_the_built_library(monkeypatch):
     """build() compiles and then checks the library's ABI; with the compile step stubbed the
     check runs against the library already built."""
@@ -133,17 +138,61 @@ def test_block_tables_match_oracle(own):
         K.dcp_build_block_tables(n, pages, mx, token_interleave=2)
 
 
+def test_token_block_tables_need_one_slot_per_virtual_page():
+    """Under token ownership every shard reads virtual page j at one slot: pages with the right
+    residues but in different slots are rejected (page ownership does not care)."""
+    n = 4
+    ok = [0 * n + 0, 0 * n + 1, 0 * n + 2, 0 * n + 3, 7 * n + 0, 7 * n + 1]
+    mixed = [0 * n + 0, 0 * n + 1, 5 * n + 2, 0 * n + 3, 7 * n + 0, 7 * n + 1]  # page 2 in slot 5
+    tail = [0 * n + 0, 0 * n + 1, 0 * n + 2, 0 * n + 3, 7 * n + 0, 8 * n + 1]   # page 5 in slot 8
+    tables, _ = K.dcp_build_block_tables(n, [ok], 2, token_interleave=1)
+    assert [list(tables[d, 0]) for d in range(n)] == [[0, 7]] * n
+    for bad in (mixed, tail):
+        with pytest.raises(L.DcpkvError) as e:
+            K.dcp_build_block_tables(n, [bad], 2, token_interleave=1)
+        assert e.value.code == L.DCPKV_EINVAL and "slot of virtual page" in str(e.value)
+        K.dcp_build_block_tables(n, [bad], 2, token_interleave=0)  # page ownership: valid
+
+
+def test_check_unique_pages():
+    """The reshard's one-writer precondition: repeats among the uncached entries are found and
+    the first list position that repeats is reported; cached entries do not count."""
+    rng = np.random.default_rng(11)
+    g = rng.permutation(10_000)[:3000]
+    assert K.kv_check_unique_pages(g) == -1
+    for first, at in ((0, 2999), (0, 1), (0, 1500), (100, 101)):
+        h = g.copy()
+        h[at] = h[first if first < at - 1 else at - 1]
+        with pytest.raises(L.DcpkvError) as e:
+            K.kv_check_unique_pages(h)
+        assert e.value.code == L.DCPKV_EINVAL and e.value.first_duplicate == at
+    h = g.copy()
+    h[5] = h[2]            # a repeat whose first copy is cached is no repeat of the call
+    assert K.kv_check_unique_pages(h, first_uncached=3) == -1
+    with pytest.raises(L.DcpkvError) as e:
+        K.kv_check_unique_pages(h, first_uncached=2)
+    assert e.value.first_duplicate == 5
+    h = np.array([4, 9, 4, 9, 4])
+    with pytest.raises(L.DcpkvError) as e:
+        K.kv_check_unique_pages(h)
+    assert e.value.first_duplicate == 2
+    assert K.kv_check_unique_pages([]) == -1
+    assert L._lib.kv_check_unique_pages(None, 4, 0, None) == L.DCPKV_EINVAL
+    assert L._lib.kv_check_unique_pages(None, 4, 5, None) == L.DCPKV_EINVAL
+
+
+@device_symbols
 def test_device_entry_points_reject_bad_arguments_on_host():
     d = L.kv_reshard_desc(1, 1, 2, -1, 100, 4, 4)  # page_bytes not a multiple of 16
     p = (C.c_void_p * 2)(16, 16)
-    rc = L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, C.c_void_p(16), C.c_void_p(16), 4, 0, None, None)
+    rc = L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, C.c_void_p(16), C.c_void_p(16), 4, 0, None, None, None)
     assert rc == L.DCPKV_EINVAL and "page_bytes" in K.dcpkv_last_error()
     d = L.kv_reshard_desc(2, 1, 2, -1, 64, 4, 4)  # fewer layers than sources
-    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 0, None, None) == L.DCPKV_EINVAL
+    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 0, None, None, None) == L.DCPKV_EINVAL
     d = L.kv_reshard_desc(1, 1, 2, -1, 64, 4, 4)
-    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 5, None, None) == L.DCPKV_EINVAL
+    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 5, None, None, None) == L.DCPKV_EINVAL
     # nothing to copy is a no-op success even without a GPU
-    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 4, None, None) == 0
+    assert L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, None, None, 4, 4, None, None, None) == 0
     assert L._lib.dcp_lse_merge(0, 4, 4, None, None, None, None, None) == L.DCPKV_EINVAL
     assert L._lib.dcp_lse_merge(2, 0, 4, None, None, None, None, None) == 0
     good = K.make_attn_desc(kv_dtype=K.KV_BF16, kv_layout=K.LAYOUT_SPLIT, q_dtype=K.Q_BF16, num_q_heads=32,
@@ -169,8 +218,36 @@ def test_device_entry_points_reject_bad_arguments_on_host():
     rc = L._lib.dcp_decode_partial(C.byref(good), C.c_void_p(256), p, None, C.c_void_p(256), C.c_void_p(256), 0,
                                    2, 3, C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1 << 30, None)
     assert rc == L.DCPKV_EINVAL and "shard range" in K.dcpkv_last_error()
+    # a misaligned per-destination count array, query or output is refused before any launch
+    d = L.kv_reshard_desc(1, 1, 2, -1, 64, 4, 4)
+    rc = L._lib.kv_reshard_pages(C.byref(d), p, p, None, None, C.c_void_p(256), C.c_void_p(256), 4, 0, None,
+                                 C.c_void_p(260), None)
+    assert rc == L.DCPKV_EINVAL and "pages_per_dst" in K.dcpkv_last_error()
+    q4 = (C.c_void_p * 4)(256, 256, 256, 256)
+    for q, po in ((264, 256), (256, 260)):
+        rc = L._lib.dcp_decode_partial(C.byref(good), C.c_void_p(q), q4, None, C.c_void_p(256), C.c_void_p(256),
+                                       0, 0, 4, C.c_void_p(po), C.c_void_p(256), C.c_void_p(256), 1 << 30, None)
+        assert rc == L.DCPKV_EINVAL and "aligned" in K.dcpkv_last_error()
+    q4m = (C.c_void_p * 4)(256, 264, 256, 256)
+    rc = L._lib.dcp_decode_partial(C.byref(good), C.c_void_p(256), q4m, None, C.c_void_p(256), C.c_void_p(256),
+                                   0, 0, 4, C.c_void_p(256), C.c_void_p(256), C.c_void_p(256), 1 << 30, None)
+    assert rc == L.DCPKV_EINVAL and "pool 1" in K.dcpkv_last_error()
+    assert L._lib.dcp_lse_merge(2, 4, 4, C.c_void_p(264), C.c_void_p(256), C.c_void_p(256), None,
+                                None) == L.DCPKV_EINVAL
+    # the softmax scale must be positive and finite
+    for sc in (0.0, -0.1, float("inf"), float("nan")):
+        bad_sc = K.make_attn_desc(kv_dtype=K.KV_BF16, kv_layout=K.LAYOUT_SPLIT, q_dtype=K.Q_BF16, num_q_heads=32,
+                                  num_kv_heads=8, head_dim_qk=128, head_dim_v=128, page_size=64, dcp_size=4,
+                                  batch=2, q_len=1, max_local_pages=4, layer=0, num_layers=1, pages_per_layer=16,
+                                  softmax_scale=sc)
+        assert L._lib.dcp_decode_partial_workspace(C.byref(bad_sc), 1000) == 0
+        rc = L._lib.dcp_decode_partial(C.byref(bad_sc), C.c_void_p(256), q4, None, C.c_void_p(256),
+                                       C.c_void_p(256), 0, 0, 4, C.c_void_p(256), C.c_void_p(256), C.c_void_p(256),
+                                       1 << 30, None)
+        assert rc == L.DCPKV_EINVAL and "softmax_scale" in K.dcpkv_last_error()
 
 
+@device_symbols
 def test_path_entry_points_reject_bad_arguments_on_host():
     """The bounded-pack calls check their arguments before anything is enqueued."""
     v = C.c_void_p(256)
@@ -194,6 +271,7 @@ def test_path_entry_points_reject_bad_arguments_on_host():
     assert L._lib.kv_unpack_pages(C.byref(good), 0, 0, None, None, v, v, v, 0, 4, v, None, None) == E
 
 
+@device_symbols
 def test_token_reshard_rejects_bad_arguments_on_host():
     p = (C.c_void_p * 4)(256, 256, 256, 256)
     v = C.c_void_p(256)
@@ -214,6 +292,7 @@ def test_token_reshard_rejects_bad_arguments_on_host():
     assert call(C.byref(good), mis, p, v, v, 4, None, 1, 0, None, None) == E
 
 
+@device_symbols
 def test_probe_rejects_bad_arguments_on_host():
     v = C.c_void_p(256)
     flops = C.c_int64(0)

@@ -34,7 +34,7 @@ def test_decode_tiny_fp32_full():
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
-    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+    H.log("  " + H.fmt_worst(worst))
 
 
 @pytest.mark.parametrize("seed_shift,q_len", [(0, 1), (1, 1), (2, 2), (3, 4)])
@@ -47,7 +47,7 @@ def test_decode_gqa_bf16_small(seed_shift, q_len):
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
-    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+    H.log("  " + H.fmt_worst(worst))
 
 
 def test_decode_gqa_bf16_generic_kernel(monkeypatch):
@@ -70,7 +70,7 @@ def test_decode_mla_fp8_small():
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
-    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+    H.log("  " + H.fmt_worst(worst))
 
 
 def test_decode_mla_fp8_verify_small():
@@ -82,7 +82,84 @@ def test_decode_mla_fp8_verify_small():
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
-    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+    H.log("  " + H.fmt_worst(worst))
+
+
+# Every instantiation of the generic VALU kernel (KV kind x query dtype) against the oracle: the
+# fast kernels take bf16 queries only, so an f32 query, an MLA page other than 64 tokens or the
+# library's switch routes a call here.
+_GENERIC_CASES = {
+    "split f32 KV, bf16 q": ("tiny_fp32", dict(q_dtype="bf16"), False),
+    "split bf16 KV, f32 q": ("gqa_bf16_16x4k-32k", dict(q_dtype="f32", seq_segments=((3, 70, 2000),),
+                                                        pool_pages=128), False),
+    "mla fp8, f32 q": ("mla_fp8_48x100k", dict(q_dtype="f32", seq_segments=((2, 100, 3000),), pool_pages=256),
+                       False),
+    "mla fp8, page 32": ("mla_fp8_48x100k", dict(page_size=32, seq_segments=((2, 100, 3000),), pool_pages=512),
+                         False),
+    "mla fp8, forced, q_len 1": ("mla_fp8_48x100k", dict(seq_segments=((2, 64 * 9 + 5, 3000), (1, 3, 3)),
+                                                         pool_pages=256), True),
+    "mla fp8, forced, q_len 4": ("mla_fp8_longmix_verify", dict(seq_segments=((2, 64 * 9 + 5, 3000), (1, 4, 4)),
+                                                                pool_pages=256, num_layers=2, attn_layer=1), True),
+}
+
+
+@pytest.mark.parametrize("label", list(_GENERIC_CASES))
+def test_decode_generic_kernel_instantiations(label, monkeypatch):
+    name, over, force = _GENERIC_CASES[label]
+    base = get_workload(name)
+    w = scaled(base, seed=base.seed + 160 + list(_GENERIC_CASES).index(label), **over)
+    H.log(f"decode generic kernel: {label}")
+    case = H.make_decode_case(w, DEV)
+    if force:
+        monkeypatch.setenv("DCPKV_FORCE_GENERIC", "1")
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs, heads=list(range(min(w.num_q_heads, 16))))
+    H.log("  " + H.fmt_worst(worst))
+
+
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_decode_mla_fp8_outlier_queries(q_len):
+    """Queries with outliers: three entries x 64 and about half of the entries at 2^-12 .. 2^-14
+    of the row's largest.  The fp8 score instruction keeps about 2^-12 of the largest product of
+    a block (measured), which is too coarse for such rows, so the kernel sends the wavefronts
+    whose rows have an entry above 16x their root mean square down its exact (fp16) score path;
+    the outputs must meet the bar against the oracle on the same bf16 queries."""
+    base = get_workload("mla_fp8_longmix_verify" if q_len == 4 else "mla_fp8_48x100k")
+    w = scaled(base, seed=base.seed + 500 + q_len, seq_segments=((3, 700, 4000),), pool_pages=256, num_layers=1,
+               attn_layer=0, q_len=q_len)
+    case = H.make_decode_case(w, DEV)
+    g = torch.Generator().manual_seed(31 + q_len)
+    q = case.q.float().cpu()
+    big = torch.rand(q.shape, generator=g).argsort(dim=-1)[..., :3]
+    q.scatter_(-1, big, q.gather(-1, big) * 64.0)
+    rmax = q.abs().amax(dim=-1, keepdim=True)
+    tiny = torch.rand(q.shape, generator=g) < 0.5
+    tiny.scatter_(-1, big, False)
+    mag = rmax * torch.exp2(-12.0 - 2.0 * torch.rand(q.shape, generator=g))
+    sign = torch.where(torch.rand(q.shape, generator=g) < 0.5, -1.0, 1.0)
+    q = torch.where(tiny, sign * mag, q)
+    case.q.copy_(q.to(torch.bfloat16).to(DEV))
+    H.log(f"decode mla fp8 outlier queries, q_len {q_len}")
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs, heads=list(range(0, w.num_q_heads, 4)))
+    H.log("  " + H.fmt_worst(worst))
+
+
+@pytest.mark.parametrize("mode,q_len", [("exact", 1), ("exact", 4), ("fp8", 1)])
+def test_decode_mla_fp8_score_paths(mode, q_len, monkeypatch):
+    """Each score path of the fp8 MLA kernel for every row (DCPKV_MLA_SCORES), on N(0,1) queries
+    with ragged tails, against the oracle."""
+    base = get_workload("mla_fp8_longmix_verify" if q_len == 4 else "mla_fp8_48x100k")
+    w = scaled(base, seed=base.seed + 520 + q_len, seq_segments=((3, 64 * 7 + 9, 4000),), pool_pages=256,
+               num_layers=1, attn_layer=0, q_len=q_len)
+    case = H.make_decode_case(w, DEV)
+    monkeypatch.setenv("DCPKV_MLA_SCORES", mode)
+    outs = H.run_decode(case)
+    _sync()
+    worst = H.check_decode(case, outs, heads=list(range(0, w.num_q_heads, 4)))
+    H.log(f"  {mode} scores, q_len {q_len}: " + H.fmt_worst(worst))
 
 
 def _rescale_pages(case, f_repr, f_value):
@@ -120,7 +197,7 @@ def test_decode_mla_fp8_rescale_paths(q_len):
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
-    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+    H.log("  " + H.fmt_worst(worst))
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "gqa_bf16_16x4k-32k", "mla_fp8_longmix_verify"])
@@ -381,16 +458,68 @@ def test_reshard_multi_source_scales(cached, dst_filter):
     src_before = [t.clone() for t in rc.src_pools]
     dst_host = _host_pools(rc.dst_pools)
     dsc_host = _host_pools(rc.dst_scales)
-    O.reshard(_host_pools(rc.src_pools), dst_host, rc.num_layers, w.dcp_size, rc.src_ids, rc.dst_ids,
-              rc.first_uncached, dst_filter, _host_pools(rc.src_scales), dsc_host)
-    H.run_reshard(rc, dst_filter=dst_filter)
+    sent = O.reshard(_host_pools(rc.src_pools), dst_host, rc.num_layers, w.dcp_size, rc.src_ids, rc.dst_ids,
+                     rc.first_uncached, dst_filter, _host_pools(rc.src_scales), dsc_host)
+    counts = torch.zeros(w.dcp_size, dtype=torch.int64, device=DEV)
+    H.run_reshard(rc, dst_filter=dst_filter, pages_per_dst=counts)
     _sync()
+    assert counts.cpu().tolist() == sent  # the per-destination page counts of the transfer
     for d in range(w.dcp_size):
         assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
         assert np.array_equal(rc.dst_scales[d].cpu().numpy(), dsc_host[d])
     for a, b in zip(src_before, rc.src_pools):
         assert torch.equal(a, b)
     H.check_reshard_by_plan(rc, dst_filter)
+
+
+def test_reshard_pages_per_dst_full_transfer_log_line():
+    """[2DR] section 6.3's transfer log at N = 4: 256 pages of a 16K-token request, 64 to each
+    destination; the counts accumulate over calls and skip bad entries."""
+    base = get_workload("gqa_bf16_16x4k-32k")
+    w = scaled(base, seed=base.seed + 130, seq_segments=((1, 16384, 16384),), pool_pages=128)
+    rc = H.make_reshard_case(w, DEV, first_uncached=0)
+    assert len(rc.dst_ids) == 256
+    counts = torch.zeros(4, dtype=torch.int64, device=DEV)
+    H.run_reshard(rc, pages_per_dst=counts)
+    _sync()
+    assert counts.cpu().tolist() == [64, 64, 64, 64]
+    dst = rc.dst_ids.copy()
+    dst[[0, 5]] = -1  # two bad entries (owners 0 and 1) are not counted
+    H.run_reshard(rc, pages_per_dst=counts, dst_ids=dst)
+    _sync()
+    assert counts.cpu().tolist() == [127, 127, 128, 128]
+    H.check_reshard_by_plan(rc)
+
+
+def test_reshard_precondition_check_refuses_repeated_pages(monkeypatch):
+    """With DCPKV_CHECK_PRECONDITIONS=1 a destination page listed twice is refused before anything
+    is written (page and token reshards); a list without repeats still moves as the oracle says."""
+    base = get_workload("reshard_mla_128k")
+    w = scaled(base, seed=base.seed + 103, seq_segments=((1, 64 * 12, 64 * 12),), num_layers=2, num_sources=1,
+               pool_pages=8, dcp_size=2)
+    rc = H.make_reshard_case(w, DEV, first_uncached=2)
+    monkeypatch.setenv("DCPKV_CHECK_PRECONDITIONS", "1")
+    dup = rc.dst_ids.copy()
+    dup[9] = dup[4]
+    before = [t.clone() for t in rc.dst_pools]
+    with pytest.raises(K.DcpkvError) as e:
+        H.run_reshard(rc, dst_ids=dup)
+    assert e.value.code == K.DCPKV_EINVAL and "appears twice" in str(e.value)
+    rc_tok = H.ReshardCase(**{**rc.__dict__, "dst_scales": None, "src_scales": None})
+    with pytest.raises(K.DcpkvError):
+        H.run_reshard_tokens(rc_tok, dst_ids=dup)
+    _sync()
+    for a, b in zip(before, rc.dst_pools):
+        assert torch.equal(a, b)
+    dup[0] = dup[4]  # a repeat of a cached entry's page is no repeat of the call
+    dup[9] = rc.dst_ids[9]
+    dst_host = _host_pools(rc.dst_pools)
+    O.reshard(_host_pools(rc.src_pools), dst_host, 2, 2, rc.src_ids, dup, rc.first_uncached,
+              -1, _host_pools(rc.src_scales), _host_pools(rc.dst_scales))
+    H.run_reshard(rc, dst_ids=dup)
+    _sync()
+    for d in range(2):
+        assert np.array_equal(rc.dst_pools[d].cpu().numpy(), dst_host[d])
 
 
 def test_reshard_follows_destination_value_not_position():
@@ -452,7 +581,7 @@ def test_decode_token_ownership(name):
     outs = H.run_decode(case)
     _sync()
     worst = H.check_decode(case, outs)
-    H.log(f"  worst rel {worst[0]:.2e} lse {worst[1]:.2e}")
+    H.log("  " + H.fmt_worst(worst))
 
 
 def test_decode_token_ownership_generic_kernel(monkeypatch):
