@@ -61,8 +61,10 @@ EXPORTED = (
     "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
     "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_check_unique_pages",
     "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
-    "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_lse_merge", "dcpkv_probe_mfma",
+    "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_decode_partial_noalloc", "dcp_lse_merge",
+    "dcpkv_probe_mfma",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DCPKV_NOALLOC_SCRATCH_BYTES
 
 
 class DcpkvError(RuntimeError):
@@ -121,6 +123,8 @@ _SIGS = {
     "dcp_decode_partial_workspace": ([C.POINTER(dcp_attn_desc), C.c_int64], C.c_size_t),
     "dcp_decode_partial": ([C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64, C.c_int32,
                             C.c_int32, _P, _P, _P, C.c_size_t, _P], C.c_int),
+    "dcp_decode_partial_noalloc": ([C.POINTER(dcp_attn_desc), _P, C.POINTER(_P), C.POINTER(_P), _P, _P, C.c_int64,
+                                    C.c_int32, C.c_int32, _P, _P, _P], C.c_int),
     "dcp_lse_merge": ([C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P], C.c_int),
     "dcpkv_probe_mfma": ([C.c_int32, C.c_int32, _P, C.c_int64, _I64P, _P], C.c_int),
 }
@@ -373,6 +377,17 @@ def dcp_decode_partial(desc: dcp_attn_desc, *, q, kv_pools, kv_scales, block_tab
                                    _dptr(block_tables), _dptr(seq_lens), total_tokens, shard_begin, sc,
                                    _dptr(partial_out), _dptr(partial_lse), _dptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def dcp_decode_partial_noalloc(desc: dcp_attn_desc, *, q, kv_pools, kv_scales, block_tables, seq_lens,
+                               total_tokens: int, partial_out, partial_lse, shard_begin: int = 0,
+                               shard_count: Optional[int] = None, stream=None) -> None:
+    """Enqueue per-shard partial attention without a workspace (the library's scratch; see
+    include/dcpkv.h)."""
+    sc = desc.dcp_size - shard_begin if shard_count is None else shard_count
+    _check(_lib.dcp_decode_partial_noalloc(C.byref(desc), _dptr(q), _ptr_array(kv_pools), _ptr_array(kv_scales),
+                                           _dptr(block_tables), _dptr(seq_lens), total_tokens, shard_begin, sc,
+                                           _dptr(partial_out), _dptr(partial_lse), _stream(stream)))
 
 
 def dcp_lse_merge(dcp_size: int, rows: int, head_dim_v: int, partial_out, partial_lse, out, out_lse=None,

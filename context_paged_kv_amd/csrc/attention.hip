@@ -506,6 +506,42 @@ static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus,
   g.bytes = align256(g.lse_off + (size_t)g.ws_cap * g.rows * sizeof(float));
 }
 
+// Fit the geometry into `cap` bytes by holding fewer chunk partials (a coarser split: the
+// planner keeps one chunk per pair when the split it wants does not fit).  False when even the
+// plan without chunk partials does not fit.
+static bool cap_geometry(const dcp_attn_desc& D, size_t cap, Geometry& g) {
+  if (g.bytes <= cap) return true;
+  if (g.o_off + 512 > cap) return false;
+  const size_t per_slot = (size_t)g.rows * (D.head_dim_v + 1) * sizeof(float);
+  const int64_t fit = (int64_t)((cap - g.o_off - 512) / per_slot);
+  g.ws_cap = std::min<int64_t>(g.ws_cap, fit);
+  g.lse_off = align256(g.o_off + (size_t)g.ws_cap * g.rows * D.head_dim_v * sizeof(float));
+  g.bytes = align256(g.lse_off + (size_t)g.ws_cap * g.rows * sizeof(float));
+  return g.bytes <= cap;
+}
+
+// Scratch of dcp_decode_partial_noalloc: one array per device, held until the process ends.
+// Host code uses only the device address hipGetSymbolAddress returns for it.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[DCPKV_NOALLOC_SCRATCH_BYTES];
+
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: no current device");
+  if (dev < 0 || dev >= 64) return set_error(DCPKV_EDEVICE, "attn: device %d beyond the 64 this build tracks", dev);
+  std::lock_guard<std::mutex> lk(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return set_error(DCPKV_EDEVICE, "attn: scratch address on device %d: %s", dev, hipGetErrorString(e));
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return DCPKV_OK;
+}
+
 }  // namespace dcpkv
 
 using namespace dcpkv;
@@ -517,12 +553,13 @@ extern "C" size_t dcp_decode_partial_workspace(const dcp_attn_desc* desc, int64_
   return g.bytes;
 }
 
-extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
-                                  const void* const* kv_pools, const void* const* kv_scales,
-                                  const int32_t* block_tables, const int32_t* seq_lens,
-                                  int64_t total_tokens, int32_t shard_begin, int32_t shard_count,
-                                  float* partial_out, float* partial_lse, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+// Both entry points: with fit_scratch the workspace is the no-alloc scratch and the split is
+// made as coarse as it must be to fit.
+static int decode_partial(const dcp_attn_desc* desc, const void* q, const void* const* kv_pools,
+                          const void* const* kv_scales, const int32_t* block_tables, const int32_t* seq_lens,
+                          int64_t total_tokens, int32_t shard_begin, int32_t shard_count, float* partial_out,
+                          float* partial_lse, void* workspace, size_t workspace_bytes, bool fit_scratch,
+                          void* stream) {
   if (!desc) return set_error(DCPKV_EINVAL, "attn: NULL descriptor");
   const dcp_attn_desc& D = *desc;
   int rc = validate(D);
@@ -540,6 +577,10 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
     return set_error(DCPKV_EINVAL, "attn: MLA fp8 needs per-page scales");
   Geometry g;
   plan_geometry(D, total_tokens, device_cus(), g);
+  if (fit_scratch && !cap_geometry(D, workspace_bytes, g))
+    return set_error(DCPKV_EINVAL,
+                     "attn (no-alloc): the plan of %lld (shard, request) pairs needs %zu bytes, more than the "
+                     "%zu-byte scratch", (long long)D.dcp_size * D.batch, g.o_off + 512, workspace_bytes);
   if (workspace_bytes < g.bytes)
     return set_error(DCPKV_EINVAL, "attn: workspace %zu bytes < %zu needed", workspace_bytes,
                      g.bytes);
@@ -616,6 +657,29 @@ extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: reduce launch: %s", hipGetErrorString(e));
   return DCPKV_OK;
+}
+
+extern "C" int dcp_decode_partial(const dcp_attn_desc* desc, const void* q,
+                                  const void* const* kv_pools, const void* const* kv_scales,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  int64_t total_tokens, int32_t shard_begin, int32_t shard_count,
+                                  float* partial_out, float* partial_lse, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return decode_partial(desc, q, kv_pools, kv_scales, block_tables, seq_lens, total_tokens, shard_begin,
+                        shard_count, partial_out, partial_lse, workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int dcp_decode_partial_noalloc(const dcp_attn_desc* desc, const void* q,
+                                          const void* const* kv_pools, const void* const* kv_scales,
+                                          const int32_t* block_tables, const int32_t* seq_lens,
+                                          int64_t total_tokens, int32_t shard_begin, int32_t shard_count,
+                                          float* partial_out, float* partial_lse, void* stream) {
+  if (!desc) return set_error(DCPKV_EINVAL, "attn: NULL descriptor");
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return decode_partial(desc, q, kv_pools, kv_scales, block_tables, seq_lens, total_tokens, shard_begin,
+                        shard_count, partial_out, partial_lse, ws, DCPKV_NOALLOC_SCRATCH_BYTES, true, stream);
 }
 
 // Launch the generic kernel for this call (also the path for shapes the fast

@@ -383,6 +383,25 @@ DCPKV_API int dcp_decode_partial(const dcp_attn_desc* desc, const void* q, const
                        int32_t shard_count, float* partial_out, float* partial_lse,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * operation, arguments, layouts and errors as dcp_decode_partial, without a
+ * workspace.  The library's own scratch array of DCPKV_NOALLOC_SCRATCH_BYTES
+ * per device (held from the library's load until the process ends) takes its
+ * place; the call allocates nothing.  When the split the planner wants needs
+ * more chunk partials than the scratch holds, the split is coarser (down to
+ * one chunk per (shard, request)), which changes results only by rounding.
+ * EINVAL, before anything is enqueued, when even the plan without chunk
+ * partials does not fit (about 32 bytes per (shard, request) pair plus 16 per
+ * chunk).  Every call on a device shares that device's scratch: calls that can
+ * overlap on one device (other streams, other threads) race and must be
+ * serialised by the caller.  The scratch needs no clearing between calls. */
+#define DCPKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+DCPKV_API int dcp_decode_partial_noalloc(const dcp_attn_desc* desc, const void* q, const void* const* kv_pools,
+                       const void* const* kv_scales, const int32_t* block_tables,
+                       const int32_t* seq_lens, int64_t total_tokens, int32_t shard_begin,
+                       int32_t shard_count, float* partial_out, float* partial_lse, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * (3) Exact LSE merge over N partials ([2DR] section 5.2; [SGL])           *
  * ------------------------------------------------------------------------ */
