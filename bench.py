@@ -1,16 +1,19 @@
 """Benchmark of the DCP hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-  1. page-level 2D reshard of every request's pages from the layer-split
-     source into the N DCP pools (kv_reshard_pages),
+  1. page-level 2D reshard of the transferred requests' pages from the
+     layer-split sources into the N DCP pools (kv_reshard_pages),
   2. per-shard partial decode attention over the N pools (dcp_decode_partial),
   3. exact LSE merge of the N partials (dcp_lse_merge).
 
-Default workload: 16 requests of U[4096, 32768] tokens, 32 query / 8 KV heads,
-head_dim 128, bf16, 64-token pages, N = 4 pools.  Inputs are resident in HBM
-before the timed region.  Prints one JSON line.
+With no arguments the bench runs the four full-size workloads one after the
+other in one process (each with its own inputs resident in HBM before its timed
+region) and prints ONE JSON line.  The headline (`config.workload`, `value`,
+`roofline`, `cpu_baseline`) is the largest single-GPU workload, the long-context
+mix with speculative verify; every workload's own figures, roofline and CPU
+oracle baseline are under `parts.workloads`.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload all|NAME] [--gpus 1]
 """
 
 from __future__ import annotations
@@ -18,7 +21,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -28,16 +30,28 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0
 MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16/bf16 matrix peak
 ROOT = os.path.dirname(os.path.abspath(__file__))
+WORKLOADS = ("gqa_bf16_16x4k-32k", "reshard_mla_128k", "mla_fp8_48x100k", "mla_fp8_longmix_verify")
+HEADLINE = "mla_fp8_longmix_verify"
+# sources behind each timed call (a stored counter figure is used only while they are unchanged)
+CALL_SOURCES = {"reshard_kernel": ["reshard.hip", "common.h"],
+                "reshard_tokens_kernel": ["reshard.hip", "common.h"],
+                "dcp_decode_partial": ["attention.hip", "attn_common.h", "attn_kernels.h", "dispatch.hip",
+                                       "gqa_bf16.hip", "mla_fp8.hip"]}
+# kernels of each timed call, as rocprofv3 names them; the first one that appears counts launches
+CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",), "reshard_tokens_kernel": ("reshard_tokens_kernel",),
+                "dcp_decode_partial": ("gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
+                                       "plan_kernel", "chunk_reduce_kernel")}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="gqa_bf16_16x4k-32k")
+    ap.add_argument("--workload", default="all", help="'all' (the four full-size workloads) or one name")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="budget of the CPU oracle sample per workload (half reshard, half attention)")
     ap.add_argument("--own", choices=["page", "token"], default="page",
                     help="DCP ownership: page p on shard p mod N (default) or token t on shard t mod N")
     ap.add_argument("--pack-cap-mib", type=int, default=64,
@@ -48,10 +62,10 @@ def parse():
                          "known-size kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--pmc-summarize", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_JSON"),
                     help="no GPU run: turn the counter_collection.csv files of a FETCH_SIZE pass and a "
-                         "WRITE_SIZE pass of this bench (run with --calib-copy-mib) plus the JSON line that "
-                         "run printed into HBM bytes per launch of the dominant kernel, stored in "
+                         "WRITE_SIZE pass of this bench (one workload, run with --calib-copy-mib) plus the JSON "
+                         "line that run printed into HBM bytes per launch of each timed call, stored in "
                          "profiles/pmc_traffic.json")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def kernel_source_hash(files):
@@ -65,7 +79,7 @@ def kernel_source_hash(files):
 TRAFFIC_DB = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 
 
-def load_traffic(kernel_key: str, src_hash: str, launches_bytes: float, path: str = TRAFFIC_DB):
+def load_traffic(kernel_key: str, src_hash: str, launches_bytes: float = 0.0, path: str = TRAFFIC_DB):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
     try:
@@ -77,6 +91,51 @@ def load_traffic(kernel_key: str, src_hash: str, launches_bytes: float, path: st
         return float(e["hbm_bytes_per_launch"])
     except Exception:
         return None
+
+
+def device_telemetry():
+    """What distinguishes one box from another: memory clock, partition modes and a hash of the
+    device's unique id, read from sysfs (nothing is changed; missing entries are left out)."""
+    out = {}
+    try:
+        import glob
+        cards = sorted(glob.glob("/sys/class/drm/card*/device/current_compute_partition"))
+        base = os.path.dirname(cards[0]) if cards else None
+        if base is None:
+            for c in sorted(glob.glob("/sys/class/drm/card*/device")):
+                if os.path.exists(os.path.join(c, "pp_dpm_mclk")):
+                    base = c
+                    break
+        if base is None:
+            return out
+
+        def rd(name):
+            try:
+                with open(os.path.join(base, name)) as f:
+                    return f.read().strip()
+            except OSError:
+                return None
+
+        for key, name in (("compute_partition", "current_compute_partition"),
+                          ("memory_partition", "current_memory_partition")):
+            v = rd(name)
+            if v:
+                out[key] = v
+        mclk = rd("pp_dpm_mclk")
+        if mclk:
+            cur = [ln for ln in mclk.splitlines() if ln.strip().endswith("*")]
+            out["memory_clock"] = (cur[0] if cur else mclk.splitlines()[-1]).split(":", 1)[-1].strip(" *")
+        sclk = rd("pp_dpm_sclk")
+        if sclk:
+            cur = [ln for ln in sclk.splitlines() if ln.strip().endswith("*")]
+            if cur:
+                out["shader_clock"] = cur[0].split(":", 1)[-1].strip(" *")
+        uid = rd("unique_id")
+        if uid:
+            out["unique_id_hash"] = hashlib.sha256(uid.encode()).hexdigest()[:12]
+    except Exception:
+        pass
+    return out
 
 
 class Step:
@@ -116,7 +175,7 @@ class Step:
             if sc is not None:
                 sc[-1].fill_(gen.SCALE_SENTINEL)
                 self.src_scales.append(sc)
-            print(f"[bench] source {r} of {w.num_sources} filled", file=sys.stderr, flush=True)
+            print(f"[bench] {w.name}: source {r + 1} of {w.num_sources} filled", file=sys.stderr, flush=True)
         # pools: random pages where requests are not transferred in the step, else a sentinel
         fill_random = self.has_attention and len(self.reshard_reqs) < w.num_requests
         self.pools, self.scales = [], ([] if w.has_scales else None)
@@ -132,7 +191,7 @@ class Step:
             self.pools.append(t)
             if sc is not None:
                 self.scales.append(sc)
-            print(f"[bench] pool {d} of {N} filled", file=sys.stderr, flush=True)
+            print(f"[bench] {w.name}: pool {d + 1} of {N} filled", file=sys.stderr, flush=True)
         self.src_ids = torch.from_numpy(gen.draw_src_order(w, S)[: self.num_pages].astype(np.int32)).to(dev)
         self.dst_ids = torch.from_numpy(np.concatenate([self.pages[b] for b in self.reshard_reqs] or [np.zeros(0)])
                                         .astype(np.int64)).to(dev)
@@ -263,6 +322,13 @@ class Step:
             scales = 0
         return self.total_tokens * per_tok + scales
 
+    def bytes_partial_call(self):
+        """Algorithmic HBM bytes of one dcp_decode_partial call: the KV, the query and the
+        partials written once."""
+        if not self.has_attention:
+            return 0
+        return self.bytes_kv() + self.q.numel() * self.q.element_size() + (self.po.numel() + self.pl.numel()) * 4
+
     def bytes_attn_other(self):
         w = self.w
         if not self.has_attention:
@@ -284,55 +350,58 @@ def _cpu_model() -> str:
     return "unknown CPU"
 
 
+def cpu_workers() -> int:
+    """Worker processes of the CPU baseline: every core this process may run on, capped at 16,
+    the host-core share one GPU of the bench box is given."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
 def cpu_baseline(st, budget_s: float):
     """The float64 oracle on the host, timed on a bounded sample of the same workload and
-    scaled linearly to the step's GB/s.  Independent units (reshard passes over a page
-    sample; requests of the attention, decoded and merged head by head) run on a pool of
-    worker processes, one per host core up to 16, each with one BLAS thread.  Page bytes
-    are copied from the GPU by this process; the workers never touch it."""
+    scaled to the full step.  Units of work run on a pool of worker processes, each with one
+    BLAS thread: reshard passes over each worker's own page set (distinct memory, 128 MiB of
+    source pages per worker, so the sample streams from DRAM rather than cache), and requests
+    of the attention, whose pages are decoded once and whose heads then run one at a time.
+    Page bytes are copied from the GPU by this process; the workers never touch it."""
     import multiprocessing as mp
-    import torch
     import oracle as O
     from tests import harness as Hn  # oracle-side page gathering shared with the tests
     from tests import oracle_workers as OW
 
     w = st.w
-    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    workers = cpu_workers()
     budget = budget_s / (2 if (st.has_reshard and st.has_attention) else 1)
-    notes = []
-    rs_time_full = at_time_full = 0.0
+    notes, extra = [], {}
+    rs_wall_full = at_wall_full = None
     saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
     for k in saved:
         os.environ[k] = "1"
     try:
         with mp.get_context("spawn").Pool(workers) as pool:
             pool.map(OW.warm, range(workers))  # processes up before anything is timed
-            if st.has_reshard:
-                # the real source bytes of the first uncached pages, one layer per source,
-                # re-addressed into compact host pools (same per-page work as the full geometry)
-                n = min(len(st.dst_ids) - st.first_uncached, 16 if w.page_bytes > 65536 else 64)
-                sel = slice(st.first_uncached, st.first_uncached + n)
-                sids = st.src_ids[sel]
-                src_h = []
-                for r in range(w.num_sources):
-                    t = np.full((2, n, w.page_bytes), 0x5A, np.uint8)
-                    t[0] = st.src[r][0].index_select(0, sids.long()).cpu().numpy()
-                    src_h.append(t)
-                g = st.dst_ids[sel].cpu().numpy()
-                g2 = np.arange(n) * w.dcp_size + (g % w.dcp_size)
+            if st.has_reshard and st.num_pages > st.first_uncached:
+                # real source bytes of up to 16 uncached pages (one layer per source); each worker
+                # tiles them into its own 128 MiB source set
+                n = min(len(st.dst_ids) - st.first_uncached, 16)
+                sids = st.src_ids[st.first_uncached:st.first_uncached + n]
+                sample = [st.src[r][0].index_select(0, sids.long()).cpu().numpy() for r in range(w.num_sources)]
                 rows, row_bytes = ((1, 576) if w.layout == "mla" else
                                    (2 * w.num_kv_heads, w.head_dim_qk * w.elem_bytes))
+                target = 128 << 20
                 deadline = time.time() + budget
                 t0 = time.perf_counter()
-                task = (src_h, w.dcp_size, (w.num_sources, n, w.page_bytes), w.num_sources, w.dcp_size, st.own,
-                        w.page_size, rows, row_bytes, g2, deadline)
-                reps = sum(pool.map(OW.reshard_passes, [task] * workers))
+                task = (sample, w.page_bytes, w.dcp_size, st.own, w.page_size, rows, row_bytes, target, deadline)
+                res = pool.map(OW.reshard_sample, [task] * workers)
                 t_rs = time.perf_counter() - t0
-                rate = 2.0 * reps * n * w.num_sources * w.page_bytes / t_rs
-                rs_time_full = st.bytes_reshard() / rate
+                moved = sum(m for m, _ in res)
+                pages = res[0][1]
+                rate = moved / t_rs  # bytes read + written per second over all workers
+                rs_wall_full = st.bytes_reshard() / rate
+                extra["reshard_GBps"] = round(rate / 1e9, 4)
                 kind = "token scatter" if st.own else "page"
-                notes.append(f"scalar {kind} reshard of {n} pages x {w.num_sources} layer(s), {reps} passes on "
-                             f"{workers} processes in {t_rs:.1f}s")
+                notes.append(f"scalar {kind} reshard passes over {pages} distinct pages x {w.num_sources} source(s) "
+                             f"({pages * w.page_bytes * w.num_sources >> 20} MiB of source per worker) on {workers} "
+                             f"processes, {moved / 1e9:.2f} GB moved in {t_rs:.1f}s")
             if st.has_attention:
                 geo = {"layout": w.layout, "kv_dtype": w.kv_dtype, "num_kv_heads": w.num_kv_heads,
                        "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v, "page_size": w.page_size,
@@ -341,13 +410,17 @@ def cpu_baseline(st, budget_s: float):
                 n_sh, lay = w.dcp_size, w.attn_layer
                 deadline = time.time() + budget
                 t0 = time.perf_counter()
+                # the requests the sample reaches, shortest first within a bounded set: one task per
+                # worker at a time (the longest requests take the oracle tens of seconds to decode)
+                order = sorted(range(w.num_requests), key=lambda b: int(st.seq_lens[b]))
                 pending, results = [], []
-                for b in range(w.num_requests):
+                for b in order[: 2 * workers]:
                     if time.time() >= deadline:
                         break
                     pages = st.pages[b]
                     pages_h = scales_h = by_slot = None
-                    if st.own:  # every shard's pages at the request's virtual slots
+                    if st.own:
+                        import torch
                         vslots = [O.dcp_local_slot(int(pages[j]), n_sh) for j in range(0, len(pages), n_sh)]
                         sl = torch.tensor(vslots, dtype=torch.int64, device=st.pools[0].device)
                         by_slot = {}
@@ -362,42 +435,62 @@ def cpu_baseline(st, budget_s: float):
                     q = st.q[b].float().cpu().numpy().astype(np.float64)
                     pending.append(pool.apply_async(OW.request_rows, ((geo, pages_h, scales_h, by_slot, pages,
                                                                        int(st.seq_lens[b]), q, deadline),)))
-                    while len(pending) > workers + 1:  # bounded host memory: one spare task
+                    while len(pending) > workers:
                         results.append(pending.pop(0).get())
                 results += [r.get() for r in pending]
                 t_at = time.perf_counter() - t0
-                rows, done = sum(r for r, _ in results), sum(d for _, d in results)
-                at_time_full = t_at * (st.total_tokens * w.q_len * w.num_q_heads) / max(done, 1)
-                notes.append(f"partials + merge for {rows} of {w.num_requests * w.num_q_heads} (request, head) "
-                             f"rows on {workers} processes in {t_at:.1f}s (page gather and decode included)")
+                dec_s = sum(r[0] for r in results)
+                dec_tok = sum(r[1] for r in results)
+                head_s = sum(r[2] for r in results)
+                head_units = sum(r[3] for r in results)  # (token, query, head) triples
+                heads = sum(r[4] for r in results)
+                if dec_tok and head_units:
+                    cpu_s = (st.total_tokens / (dec_tok / dec_s) +
+                             st.total_tokens * w.q_len * w.num_q_heads / (head_units / head_s))
+                    at_wall_full = cpu_s / workers
+                notes.append(f"attention of {len(results)} requests ({dec_tok} tokens decoded, {heads} (request, head) "
+                             f"rows of partials + merge) on {workers} processes in {t_at:.1f}s; page decode and "
+                             f"per-head work extrapolated separately to all {st.total_tokens} tokens x "
+                             f"{w.num_q_heads} heads")
     finally:
         for k, v in saved.items():
             if v is None:
                 os.environ.pop(k, None)
             else:
                 os.environ[k] = v
-    step_bytes = st.bytes_reshard() + st.bytes_kv() + st.bytes_attn_other()
-    value = step_bytes / (rs_time_full + at_time_full) / 1e9
-    return {"value": round(value, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
-            "sample": f"float64 numpy oracle on {workers} worker processes ({_cpu_model()}), one BLAS thread "
-                      "each: " + "; ".join(notes) + "; scaled linearly to the full step"}
+    if st.has_attention:
+        if at_wall_full is None:
+            return None
+        value = st.bytes_kv() / at_wall_full / 1e9
+        unit_note = "attention KV GB/s (partials + merge)"
+    else:
+        if rs_wall_full is None:
+            return None
+        value = st.bytes_reshard() / rs_wall_full / 1e9
+        unit_note = "reshard GB/s (read + write)"
+    out = {"value": round(value, 6), "unit": "GB/s", "cores": workers, "kind": "oracle",
+           "sample": f"float64 numpy oracle, {unit_note}, on {workers} worker processes ({_cpu_model()}), one BLAS "
+                     "thread each: " + "; ".join(notes) + "; scaled linearly to the full step"}
+    out.update(extra)
+    return out
 
 
-def plain_copy_gbps(torch, dev, nbytes: int, reps: int = 5) -> float:
-    """Read + write GB/s of one contiguous device-to-device copy of about `nbytes` (capped at 2 GiB),
-    timed with events: the practical copy ceiling of this GPU, next to which the reshard is read."""
-    n = max(1 << 20, min(int(nbytes), 2 << 30)) // 16 * 16
+def copy_ceiling_gbps(torch, K, dev, nbytes: int, reps: int = 5) -> float:
+    """Read + write GB/s of the library's streaming copy (the reshard's own copy loop over one
+    contiguous range) over about `nbytes` (capped at 4 GiB), timed with events."""
+    n = max(1 << 20, min(int(nbytes), 4 << 30)) // 16 * 16
     a = torch.empty(n, dtype=torch.uint8, device=dev)
     b = torch.empty_like(a)
     a.fill_(1)
-    b.copy_(a)
+    stream = torch.cuda.current_stream()
+    K.dcpkv_probe_copy(a, b)
     torch.cuda.synchronize()
     ts = []
     for _ in range(reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
+        e0.record(stream)
+        K.dcpkv_probe_copy(a, b)
+        e1.record(stream)
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e-3)
     del a, b
@@ -420,15 +513,9 @@ def mfma_probe_tflops(torch, K, dev, kind: int, iters: int = 4000, reps: int = 3
     return float(np.median(rates))
 
 
-# kernels of each timed call, as rocprofv3 names them
-CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",), "reshard_tokens_kernel": ("reshard_tokens_kernel",),
-                "dcp_decode_partial": ("plan_kernel", "gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
-                                       "chunk_reduce_kernel")}
-
-
 def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: int, path: str = TRAFFIC_DB) -> dict:
-    """Scale the FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) of the dominant call's kernels by
-    what the same counters read for the calibration copy, and store HBM bytes per launch."""
+    """Scale the FETCH_SIZE / WRITE_SIZE readings (KiB per dispatch) of each timed call's kernels by
+    what the same counters read for the calibration copy, and store HBM bytes per launch per call."""
     import csv
     import re
 
@@ -440,77 +527,67 @@ def pmc_summarize(fetch_csv: str, write_csv: str, bench_json: str, calib_mib: in
                 line = json.loads(ln)
     if line is None:
         sys.exit(f"no bench JSON line in {bench_json}")
-    wl, roof = line["config"]["workload"], line["roofline"]
-    call = roof["kernel"].split()[0]
-    names = CALL_KERNELS[call]
+    wl = line["config"]["workload"]
+    calls = line["parts"]["workloads"][wl]["calls"]
+    own = ":token" if line["config"].get("ownership") == "token" else ""
 
-    def per_dispatch(path, counter):
+    def per_dispatch(path_, counter):
         rows = {}
-        with open(path) as f:
+        with open(path_) as f:
             for r in csv.DictReader(f):
                 if r["Counter_Name"] != counter:
                     continue
                 rows.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])[1] += float(r["Counter_Value"])
         return [rows[k] for k in sorted(rows)]
 
-    out = {}
-    for counter, csv_path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        ds = per_dispatch(csv_path, counter)
-        calib = [v for k, v in ds if "bitwise_not" in k]
+    ds = {c: per_dispatch(p, c) for c, p in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv))}
+    scale = {}
+    for counter, rows in ds.items():
+        calib = [v for k, v in rows if "bitwise_not" in k]
         if len(calib) != 1:
-            sys.exit(f"{csv_path}: expected one calibration copy dispatch, found {len(calib)}")
-        scale = calib_mib * (1 << 20) / (calib[0] * 1024.0)  # true bytes per counted byte
-        # the timed call's kernels, grouped per launch of the call: one group per launch of its main kernel
-        mine = [(k, v) for k, v in ds if any(re.search(r"\b" + n + r"\b", k) for n in names)]
-        main_name = [n for n in names if n not in ("plan_kernel", "chunk_reduce_kernel")]
-        launches = sum(1 for k, _ in mine if any(n in k for n in main_name))
-        if launches == 0:
-            sys.exit(f"{csv_path}: no dispatch of {names}")
-        out[counter] = {"kib_per_launch": sum(v for _, v in mine) / launches, "scale": scale,
-                        "calib_kib": calib[0], "launches": launches}
-    hbm = sum(out[c]["kib_per_launch"] * 1024.0 * out[c]["scale"] for c in out)
-    key = f"{wl}:{call}" + (":token" if line["config"].get("ownership") == "token" else "")
+            sys.exit(f"{counter}: expected one calibration copy dispatch, found {len(calib)}")
+        scale[counter] = calib_mib * (1 << 20) / (calib[0] * 1024.0)  # true bytes per counted byte
     try:
         with open(path) as f:
             db = json.load(f)
     except FileNotFoundError:
         db = {}
-    db[key] = {"source_hash": roof["source_hash"], "hbm_bytes_per_launch": round(hbm),
-               "fetch_kib_per_launch": round(out["FETCH_SIZE"]["kib_per_launch"], 1),
-               "write_kib_per_launch": round(out["WRITE_SIZE"]["kib_per_launch"], 1),
-               "scale_fetch": round(out["FETCH_SIZE"]["scale"], 4), "scale_write": round(out["WRITE_SIZE"]["scale"], 4),
-               "calib_copy_mib": calib_mib, "launches": out["FETCH_SIZE"]["launches"],
-               "algorithmic_bytes_per_launch": roof.get("algorithmic_bytes")}
+    stored = {}
+    for call, info in calls.items():
+        names = CALL_KERNELS[call]
+        out = {}
+        for counter, rows in ds.items():
+            mine = [(k, v) for k, v in rows if any(re.search(r"\b" + n + r"\b", k) for n in names)]
+            main = [n for n in names if any(re.search(r"\b" + n + r"\b", k) for k, _ in mine)]
+            if not main:
+                break
+            launches = sum(1 for k, _ in mine if re.search(r"\b" + main[0] + r"\b", k))
+            out[counter] = {"kib_per_launch": sum(v for _, v in mine) / launches, "launches": launches}
+        if len(out) != 2:
+            continue
+        hbm = sum(out[c]["kib_per_launch"] * 1024.0 * scale[c] for c in out)
+        key = f"{wl}:{call}{own}"
+        db[key] = {"source_hash": info["source_hash"], "hbm_bytes_per_launch": round(hbm),
+                   "fetch_kib_per_launch": round(out["FETCH_SIZE"]["kib_per_launch"], 1),
+                   "write_kib_per_launch": round(out["WRITE_SIZE"]["kib_per_launch"], 1),
+                   "scale_fetch": round(scale["FETCH_SIZE"], 4), "scale_write": round(scale["WRITE_SIZE"], 4),
+                   "calib_copy_mib": calib_mib, "launches": out["FETCH_SIZE"]["launches"],
+                   "algorithmic_bytes_per_launch": info.get("algorithmic_bytes")}
+        stored[key] = db[key]
+    if not stored:
+        sys.exit("no timed call's kernels in the counter files")
     with open(path, "w") as f:
         json.dump(db, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps({key: db[key]}))
-    return db[key]
+    print(json.dumps(stored))
+    return stored
 
 
-def main():
-    a = parse()
-    if a.pmc_summarize:
-        pmc_summarize(*a.pmc_summarize, a.calib_copy_mib or sys.exit("--pmc-summarize needs --calib-copy-mib"))
-        return
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the multi-GPU design "
-              "is described in the design notes but not built", file=sys.stderr)
-        sys.exit(2)
+def measure(w, dev, a, probes):
+    """Inputs of workload w in HBM, W warm-up steps, K timed steps; returns its part of the line."""
     import torch
-    from workloads.configs import get_workload
-
-    if not torch.cuda.is_available():
-        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
-        sys.exit(1)
-    w = get_workload(a.workload)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    K = probes["K"]
     print(f"[bench] building inputs for {w.name}", file=sys.stderr, flush=True)
-    if a.own == "token" and w.has_scales and w.num_sources > 0:
-        print(f"{w.name}: its pools carry per-page fp8 scales, which the token reshard does not move",
-              file=sys.stderr)
-        sys.exit(2)
     st = Step(w, dev, a.own)
     torch.cuda.synchronize()
     if a.calib_copy_mib:  # one elementwise kernel reading and writing exactly this many bytes
@@ -527,7 +604,7 @@ def main():
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(a.steps)]
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {w.name}: timing {a.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(a.steps):
@@ -547,19 +624,26 @@ def main():
     t_step = np.array([e[0].elapsed_time(e[3]) for e in evs]) * 1e-3
     if st.has_attention:
         assert torch.isfinite(st.out).all() and torch.isfinite(st.lse).all(), "non-finite attention output"
-    ms_per_step = wall / a.steps * 1e3
     b_rs, b_kv, b_other = st.bytes_reshard(), st.bytes_kv(), st.bytes_attn_other()
-    step_bytes = b_rs + b_kv + b_other
-    value = step_bytes / (wall / a.steps) / 1e9
-    parts = {"step_event_us": round(t_step.mean() * 1e6, 2),
-             "bytes": {"reshard_rw": b_rs, "kv": b_kv, "attn_other": b_other}}
+    part = {"requests": w.num_requests, "total_tokens": st.total_tokens, "q_heads": w.num_q_heads,
+            "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_qk, "page_size": w.page_size, "dcp_size": w.dcp_size,
+            "q_len": w.q_len, "layers": w.num_layers, "dtype": w.kv_dtype,
+            "step": " + ".join(x for x, on in (("reshard", st.has_reshard), ("partial attention", st.has_attention),
+                                               ("LSE merge", st.has_attention)) if on),
+            "ms_per_step": round(wall / a.steps * 1e3, 4), "step_event_us": round(t_step.mean() * 1e6, 2),
+            "bytes": {"reshard_rw": b_rs, "kv": b_kv, "attn_other": b_other}, "calls": {}}
+    calls = part["calls"]
+    own = ":token" if st.own else ""
     if st.has_reshard:
         rs_gbps = b_rs / t_rs.mean() / 1e9
-        copy_gbps = plain_copy_gbps(torch, dev, b_rs // 2)
-        parts.update({"reshard_GBps": round(rs_gbps, 1), "reshard_frac_hbm": round(rs_gbps / HBM_PEAK_GBPS, 4),
-                      "reshard_us": round(t_rs.mean() * 1e6, 2),
-                      "plain_copy_GBps": round(copy_gbps, 1),
-                      "reshard_frac_of_plain_copy": round(rs_gbps / copy_gbps, 4)})
+        name = "reshard_tokens_kernel" if st.own else "reshard_kernel"
+        h = kernel_source_hash(CALL_SOURCES[name])
+        ceil = copy_ceiling_gbps(torch, K, dev, b_rs // 2)
+        calls[name] = {"us": round(t_rs.mean() * 1e6, 2), "algorithmic_bytes": int(b_rs), "source_hash": h,
+                       "traffic": load_traffic(f"{w.name}:{name}{own}", h)}
+        part.update({"reshard_GBps": round(rs_gbps, 1), "reshard_frac_hbm": round(rs_gbps / HBM_PEAK_GBPS, 4),
+                     "reshard_us": round(t_rs.mean() * 1e6, 2), "copy_ceiling_GBps": round(ceil, 1),
+                     "reshard_frac_of_copy_ceiling": round(rs_gbps / ceil, 4)})
         if a.pack_cap_mib > 0 and not st.own and st.num_pages > st.first_uncached:
             # the same pages path by path through a fixed staging buffer: every page is read and
             # written twice (source -> staging -> pool)
@@ -576,72 +660,124 @@ def main():
                 ts.append(e0.elapsed_time(e1) * 1e-3)
             t_pk = float(np.median(ts))
             pk_gbps = 2 * b_rs / t_pk / 1e9
-            parts.update({"pack_cap_pages": cap, "pack_windows": st.windows, "pack_unpack_us": round(t_pk * 1e6, 2),
-                          "pack_unpack_GBps": round(pk_gbps, 1), "pack_unpack_frac_hbm": round(pk_gbps / HBM_PEAK_GBPS, 4),
-                          "pack_unpack_time_vs_reshard": round(t_pk / t_rs.mean(), 3)})
+            part.update({"pack_cap_pages": cap, "pack_windows": st.windows, "pack_unpack_us": round(t_pk * 1e6, 2),
+                         "pack_unpack_GBps": round(pk_gbps, 1), "pack_unpack_frac_hbm": round(pk_gbps / HBM_PEAK_GBPS, 4),
+                         "pack_unpack_time_vs_reshard": round(t_pk / t_rs.mean(), 3)})
     if st.has_attention:
         t_attn = t_pa.mean() + t_mg.mean()
         kv_gbps = b_kv / t_attn / 1e9
-        parts.update({"attn_kv_GBps": round(kv_gbps, 1), "attn_kv_frac_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
-                      "attn_all_bytes_GBps": round((b_kv + b_other) / t_attn / 1e9, 1),
-                      "attn_TFLOPs": round(st.flops_attn() / t_pa.mean() / 1e12, 1),
-                      "partial_us": round(t_pa.mean() * 1e6, 2), "merge_us": round(t_mg.mean() * 1e6, 2),
-                      "decode_tokens_per_s": round(w.num_requests * w.q_len / t_attn, 1)})
+        h = kernel_source_hash(CALL_SOURCES["dcp_decode_partial"])
+        calls["dcp_decode_partial"] = {"us": round(t_pa.mean() * 1e6, 2), "algorithmic_bytes": int(st.bytes_partial_call()),
+                                       "source_hash": h,
+                                       "traffic": load_traffic(f"{w.name}:dcp_decode_partial{own}", h)}
+        part.update({"attn_kv_GBps": round(kv_gbps, 1), "attn_kv_frac_hbm": round(kv_gbps / HBM_PEAK_GBPS, 4),
+                     "attn_all_bytes_GBps": round((b_kv + b_other) / t_attn / 1e9, 1),
+                     "attn_TFLOPs": round(st.flops_attn() / t_pa.mean() / 1e12, 1),
+                     "partial_us": round(t_pa.mean() * 1e6, 2), "merge_us": round(t_mg.mean() * 1e6, 2),
+                     "decode_tokens_per_s": round(w.num_requests * w.q_len / t_attn, 1)})
         if w.layout == "mla":
             # what this device's matrix cores deliver on back-to-back MFMAs of the two kinds the
             # kernel issues, and the MFMA time of its instructions at those rates (latent scores:
             # two fp8 products per score, the query's hi and lo terms; rope and PV: fp16)
-            r16, r8 = mfma_probe_tflops(torch, st.K, dev, 0), mfma_probe_tflops(torch, st.K, dev, 1)
+            r16, r8 = probes["mfma_f16"], probes["mfma_fp8"]
             pairs = st.flops_attn() / (2.0 * w.num_q_heads * (w.head_dim_qk + w.head_dim_v))
             f8 = 2.0 * pairs * w.num_q_heads * w.head_dim_v * 2
             f16 = 2.0 * pairs * w.num_q_heads * ((w.head_dim_qk - w.head_dim_v) + w.head_dim_v)
             t_mfma = f8 / (r8 * 1e12) + f16 / (r16 * 1e12)
-            parts.update({"mfma_probe_f16_TFLOPs": round(r16, 1), "mfma_probe_fp8_TFLOPs": round(r8, 1),
-                          "partial_mfma_us_at_probe_rates": round(t_mfma * 1e6, 2),
-                          "partial_frac_of_probe_rates": round(t_mfma / t_pa.mean(), 4)})
+            part.update({"attn_frac_mfma_peak": round(st.flops_attn() / t_pa.mean() / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                         "partial_mfma_us_at_probe_rates": round(t_mfma * 1e6, 2),
+                         "partial_frac_of_probe_rates": round(t_mfma / t_pa.mean(), 4)})
     # roofline of the dominant call of the step
     if st.has_reshard and (not st.has_attention or t_rs.mean() >= t_pa.mean()):
-        dom = "reshard_tokens_kernel" if st.own else "reshard_kernel"
-        src_files = ["reshard.hip", "common.h"]
+        name = "reshard_tokens_kernel" if st.own else "reshard_kernel"
         achieved = b_rs / t_rs.mean() / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4)}
-        dom_bytes = b_rs
     else:
-        dom = "dcp_decode_partial (plan + partial + chunk-reduce kernels)"
-        src_files = ["attention.hip", "attn_common.h", "attn_kernels.h", "dispatch.hip", "gqa_bf16.hip",
-                     "mla_fp8.hip"]
-        dom_bytes = b_kv + b_other - (st.out.numel() + st.lse.numel()) * 4
+        name = "dcp_decode_partial"
         if w.layout == "mla":  # 128 heads share one latent: the matrix cores bind, fp16 MFMA peak
             achieved = st.flops_attn() / t_pa.mean() / 1e12
             roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4)}
         else:
-            achieved = dom_bytes / t_pa.mean() / 1e9
+            achieved = st.bytes_partial_call() / t_pa.mean() / 1e9
             roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBPS, 4)}
-    src_hash = kernel_source_hash(src_files)
-    tkey = f"{w.name}:{dom.split()[0]}" + (":token" if st.own else "")
-    roof.update({"traffic": load_traffic(tkey, src_hash, dom_bytes), "kernel": dom,
-                 "algorithmic_bytes": int(dom_bytes), "source_hash": src_hash})
-    cpu = None
+    c = calls[name]
+    roof.update({"traffic": c["traffic"], "kernel": name + (" (plan + partial + chunk-reduce kernels)"
+                                                            if name == "dcp_decode_partial" else ""),
+                 "algorithmic_bytes": c["algorithmic_bytes"], "launch_us": c["us"], "source_hash": c["source_hash"]})
+    part["roofline"] = roof
+    # the workload's own rate of the metric: attention KV GB/s where there is attention, else the
+    # reshard's read + write GB/s
+    part["value"] = part["attn_kv_GBps"] if st.has_attention else part["reshard_GBps"]
+    part["value_is"] = ("attention KV GB/s (partial + merge)" if st.has_attention
+                        else "reshard GB/s (read + write)")
+    part["cpu_baseline"] = None
     if not a.no_cpu_baseline:
-        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(st, a.cpu_seconds)
-    steps_desc = " + ".join(x for x, on in (("reshard", st.has_reshard), ("partial attention", st.has_attention),
-                                           ("LSE merge", st.has_attention)) if on)
+        print(f"[bench] {w.name}: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        part["cpu_baseline"] = cpu_baseline(st, a.cpu_seconds)
+    del st
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return part
+
+
+def main():
+    a = parse()
+    if a.pmc_summarize:
+        pmc_summarize(*a.pmc_summarize, a.calib_copy_mib or sys.exit("--pmc-summarize needs --calib-copy-mib"))
+        return
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the multi-GPU design "
+              "is described in the design notes but not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from workloads.configs import get_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X (no GPU visible)", file=sys.stderr)
+        sys.exit(1)
+    names = list(WORKLOADS) if a.workload == "all" else [a.workload]
+    ws = [get_workload(n) for n in names]
+    if a.own == "token":
+        bad = [w.name for w in ws if w.has_scales and w.num_sources > 0]
+        if bad:
+            print(f"{bad}: their pools carry per-page fp8 scales, which the token reshard does not move",
+                  file=sys.stderr)
+            sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    import context_paged_kv_amd as K
+
+    probes = {"K": K}
+    if any(w.layout == "mla" and w.has_attention for w in ws):
+        probes["mfma_f16"] = mfma_probe_tflops(torch, K, dev, 0)
+        probes["mfma_fp8"] = mfma_probe_tflops(torch, K, dev, 1)
+    parts = {}
+    for w in ws:
+        parts[w.name] = measure(w, dev, a, probes)
+    head_name = HEADLINE if HEADLINE in parts else names[-1]
+    head = parts[head_name]
+    hw = get_workload(head_name)
     line = {
         "metric": "DCP decode attention KV GB/s (% HBM peak) + reshard GB/s, 1 MI355X",
-        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.kv_dtype, "data": "synthetic (seeded N(0,1) KV, random page maps)",
-        "config": {"workload": w.name, "requests": w.num_requests, "total_tokens": st.total_tokens,
-                   "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim_qk,
-                   "page_size": w.page_size, "dcp_size": w.dcp_size, "q_len": w.q_len,
-                   "layers": w.num_layers, "ownership": a.own, "step": steps_desc},
-        "parts": parts,
-        "roofline": roof,
-        "cpu_baseline": cpu,
+        "value": head["value"], "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": hw.kv_dtype, "data": "synthetic (seeded N(0,1) KV, random page maps)",
+        "config": {"workload": head_name, "requests": head["requests"], "total_tokens": head["total_tokens"],
+                   "q_heads": head["q_heads"], "kv_heads": head["kv_heads"], "head_dim": head["head_dim"],
+                   "page_size": head["page_size"], "dcp_size": head["dcp_size"], "q_len": head["q_len"],
+                   "layers": head["layers"], "ownership": a.own, "step": head["step"]},
+        "parts": {"value_is": head["value_is"] + " of the headline workload",
+                  "headline_reshard_GBps": head.get("reshard_GBps"),
+                  "headline_reshard_frac_hbm": head.get("reshard_frac_hbm"),
+                  "device": device_telemetry(),
+                  "mfma_probe_f16_TFLOPs": round(probes["mfma_f16"], 1) if "mfma_f16" in probes else None,
+                  "mfma_probe_fp8_TFLOPs": round(probes["mfma_fp8"], 1) if "mfma_fp8" in probes else None,
+                  "workloads": parts},
+        "roofline": head["roofline"],
+        "cpu_baseline": head["cpu_baseline"],
     }
     print(json.dumps(line), flush=True)
 

@@ -62,7 +62,7 @@ EXPORTED = (
     "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_check_unique_pages",
     "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
     "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_decode_partial_noalloc", "dcp_lse_merge",
-    "dcpkv_probe_mfma",
+    "dcpkv_probe_mfma", "dcpkv_probe_copy",
 )
 NOALLOC_SCRATCH_BYTES = 64 << 20  # DCPKV_NOALLOC_SCRATCH_BYTES
 
@@ -127,6 +127,7 @@ _SIGS = {
                                     C.c_int32, C.c_int32, _P, _P, _P], C.c_int),
     "dcp_lse_merge": ([C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P], C.c_int),
     "dcpkv_probe_mfma": ([C.c_int32, C.c_int32, _P, C.c_int64, _I64P, _P], C.c_int),
+    "dcpkv_probe_copy": ([_P, _P, C.c_int64, _P], C.c_int),
 }
 HOST_SYMBOLS = ("dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
                 "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
@@ -406,3 +407,8 @@ def dcpkv_probe_mfma(kind: int, iters: int, sink, stream=None) -> int:
     _check(_lib.dcpkv_probe_mfma(kind, iters, _dptr(sink), sink.numel(), C.byref(flops), _stream(stream)))
     return flops.value
 
+
+def dcpkv_probe_copy(src, dst, nbytes: Optional[int] = None, stream=None) -> None:
+    """Enqueue the streaming copy the reshard is read against (see include/dcpkv.h)."""
+    n = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(_lib.dcpkv_probe_copy(_dptr(src), _dptr(dst), n, _stream(stream)))

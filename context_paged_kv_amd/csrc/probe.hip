@@ -89,3 +89,62 @@ extern "C" int dcpkv_probe_mfma(int32_t kind, int32_t iters, float* sink, int64_
   return DCPKV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Streaming copy: the copy ceiling the reshard is read against
+// ---------------------------------------------------------------------------
+
+namespace dcpkv {
+
+typedef uint32_t u32x4p __attribute__((ext_vector_type(4)));
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;  // 16-byte loads in flight per thread
+constexpr int kCopyBlocksPerCU = 2;
+
+// A persistent grid over segments of kCopyThreads * kCopyUnroll chunks: every thread issues
+// all of its non-temporal 16-byte loads before its stores (the reshard's segment loop over one
+// contiguous range instead of a page list, in the geometry that streamed fastest in a sweep of
+// loads per thread, threads per workgroup, workgroups per CU and cache hints).
+__global__ __launch_bounds__(kCopyThreads) void stream_copy_kernel(const u32x4p* __restrict__ src,
+                                                                   u32x4p* __restrict__ dst, int64_t chunks) {
+  constexpr int64_t seg = (int64_t)kCopyThreads * kCopyUnroll;
+  const int64_t items = (chunks + seg - 1) / seg;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t base = it * seg;
+    const int64_t n = chunks - base < seg ? chunks - base : seg;
+    if (n == seg) {  // straight-line: every load in flight before the first store
+      u32x4p v[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        v[u] = __builtin_nontemporal_load(src + base + u * kCopyThreads + threadIdx.x);
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        __builtin_nontemporal_store(v[u], dst + base + u * kCopyThreads + threadIdx.x);
+    } else {
+      for (int64_t c = threadIdx.x; c < n; c += kCopyThreads)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(src + base + c), dst + base + c);
+    }
+  }
+}
+
+}  // namespace dcpkv
+
+extern "C" int dcpkv_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (!src || !dst || bytes < 16 || bytes % 16 || !aligned16(src) || !aligned16(dst))
+    return set_error(DCPKV_EINVAL, "probe_copy: bad arguments (%lld bytes; 16-byte multiples and alignment)",
+                     (long long)bytes);
+  const char* s = static_cast<const char*>(src);
+  char* d = static_cast<char*>(dst);
+  if (s < d + bytes && d < s + bytes) return set_error(DCPKV_EINVAL, "probe_copy: source and destination overlap");
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return set_error(DCPKV_EDEVICE, "probe_copy: no device");
+  const int64_t chunks = bytes / 16;
+  const int64_t items = (chunks + (int64_t)kCopyThreads * kCopyUnroll - 1) / ((int64_t)kCopyThreads * kCopyUnroll);
+  const int64_t grid = std::min<int64_t>(items, (int64_t)cus * kCopyBlocksPerCU);
+  hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4p*>(src), static_cast<u32x4p*>(dst), chunks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "probe_copy: launch failed: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}

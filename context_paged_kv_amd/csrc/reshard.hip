@@ -8,12 +8,14 @@
 // position (section 6.3).
 //
 // Work is split into items (layer, entry, segment): each page is cut into
-// near-equal segments of at most 36 KB (a whole 576-byte x 64-token fp8 page
-// is one segment).  A persistent grid strides over the items; every thread
-// issues all of its 16-byte non-temporal loads for the segment (up to nine)
-// before its stores, and the page ids of the workgroup's next item are read
-// while the current one is in flight, so neither the id lookup nor the data
-// latency is exposed per item.
+// segments of 12-24 KB (a 256 KB bf16 GQA page into 16 of 16 KB, a 576-byte x
+// 64-token fp8 page into 3 of 12 KB).  A persistent grid of two workgroups per
+// CU strides over the items; every thread issues all of its 16-byte
+// non-temporal loads for the segment (three to six) before its stores, in
+// straight-line code, and the page ids of the workgroup's next item are read
+// while the current one is in flight.  The side work per (layer, entry) --
+// page scales, counts of bad entries and of pages per destination -- runs
+// before the copy loop, spread over all threads.
 
 #include <hip/hip_runtime.h>
 
@@ -26,6 +28,23 @@
 namespace dcpkv {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Division of a 32-bit n < 2^31 by a launch constant d >= 1 without a divide: with
+// s = ceil(log2 d) and m = ceil(2^(32+s) / d), floor(n / d) = (n * m) >> (32 + s) exactly (the
+// rounding error of m times n stays below 2^(31+s)).
+struct FastDiv {
+  uint64_t m;
+  uint32_t s, d;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const unsigned __int128 num = (unsigned __int128)1 << (32 + s);
+  return FastDiv{(uint64_t)((num + d - 1) / d), s, d};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((unsigned __int128)n * f.m) >> (32 + f.s));
+}
 
 struct ReshardArgs {
   const uint8_t* src[kMaxSources];
@@ -49,15 +68,65 @@ struct ReshardArgs {
   int32_t n;           // DCP size
   int32_t dst_filter;
   int32_t has_scales;
+  FastDiv div_layer;   // by work * segs: item -> layer
+  FastDiv div_seg;     // by segs: item within a layer -> entry
+  FastDiv div_n;       // by n: global page -> slot
 };
 
+// Copy geometry, measured on MI355X over page-permuted copies and both page sizes of the
+// workloads: two 256-thread workgroups per CU with three to five 16-byte loads per thread in
+// flight (segments of 12-20 KB) stream better than deeper queues (nine loads, three or four
+// workgroups: 2-5% slower) or one workgroup per CU (25% slower).
 constexpr int kReshardThreads = 256;
-constexpr int kReshardUnroll = 9;                                          // 16-byte loads per thread
-constexpr int64_t kReshardSegMax = 16 * kReshardThreads * kReshardUnroll;  // 36864 bytes
-#ifndef RESHARD_BLOCKS_PER_CU
-#define RESHARD_BLOCKS_PER_CU 4
-#endif
-constexpr int kReshardBlocksPerCU = RESHARD_BLOCKS_PER_CU;
+constexpr int kReshardBlocksPerCU = 2;
+constexpr int kReshardMaxUnroll = 6;
+
+// Loads per thread for pages of page_bytes: four when 16 KB segments cut the page exactly (the
+// fastest in the sweep; 256 KB pages), else the first of 6, 5 and 3 that does (36 KB pages: three
+// segments of 12 KB, 5% faster than two of 18 KB with a partial round), else of 4, 5 and 6 the one
+// whose near-equal segments leave the fewest lanes idle (ties to the smaller).
+static int reshard_unroll(int64_t page_bytes) {
+  for (int u : {4, 6, 5, 3})
+    if (page_bytes % (16LL * kReshardThreads * u) == 0) return u;
+  int best = 4;
+  double best_fill = 0.0;
+  for (int u = 4; u <= kReshardMaxUnroll; ++u) {
+    const int64_t cap = 16LL * kReshardThreads * u;
+    const int64_t nseg = (page_bytes + cap - 1) / cap;
+    const double fill = (double)page_bytes / (double)(nseg * cap);
+    if (fill > best_fill + 1e-9) {
+      best_fill = fill;
+      best = u;
+    }
+  }
+  return best;
+}
+
+// One segment of `chunks` 16-byte chunks, every load issued before the first store.  A segment
+// of the launch's full size (UF rounds of all threads, plus one round of the first `chunks mod
+// 256` threads when PART) runs as straight-line code, so the compiler counts the loads in flight
+// exactly instead of waiting for every earlier access before each store; the partial round's
+// load is clamped into the segment and only its store is predicated.  A shorter segment (the
+// last of a page) copies one chunk per thread at a time.  store(c, v) writes chunk c.
+template <int UF, bool PART, typename Store, typename Between>
+__device__ __forceinline__ void copy_segment(const u32x4* __restrict__ src, int chunks, int full_chunks,
+                                             Store store, Between between) {
+  const int t = threadIdx.x;
+  if (chunks == full_chunks) {
+    u32x4 v[UF > 0 ? UF : 1], x;
+#pragma unroll
+    for (int u = 0; u < UF; ++u) v[u] = __builtin_nontemporal_load(src + u * kReshardThreads + t);
+    const int cx = UF * kReshardThreads + t;
+    if (PART) x = __builtin_nontemporal_load(src + (cx < chunks ? cx : chunks - 1));
+    between();  // while the loads are in flight
+#pragma unroll
+    for (int u = 0; u < UF; ++u) store(u * kReshardThreads + t, v[u]);
+    if (PART && cx < chunks) store(cx, x);
+  } else {
+    between();
+    for (int c = t; c < chunks; c += kReshardThreads) store(c, __builtin_nontemporal_load(src + c));
+  }
+}
 
 // Owner of `layer` under the section 4.1 split, and the first layer it owns.
 __device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_sources, int& r,
@@ -73,73 +142,90 @@ __device__ __forceinline__ void layer_owner(int layer, int num_layers, int num_s
   }
 }
 
-// Entry e of the list: source page id and destination global page (plain loads; the
-// compiler turns them into scalar loads since every lane reads the same word).
+// Entry e of the list: source page id and destination global page.
 struct ReshardEntry {
   int64_t g;
   int32_t sp;
 };
-__device__ __forceinline__ ReshardEntry reshard_entry(const ReshardArgs& a, int64_t it) {
-  ReshardEntry en{-1, -1};
-  if (it < a.items) {
-    const int64_t e = (it % (a.work * a.segs)) / a.segs;
-    en.g = a.dst_ids[a.first + e];
-    en.sp = a.src_ids[a.first + e];
-  }
-  return en;
+
+// The entry of item `it`, clamped into range instead of branched on, and with divisions by
+// launch constants, so the loop around it has no data-dependent branch.  (Reading the entries
+// with scalar loads instead, so that the next segment's loads need not wait for the previous
+// segment's stores, measured 1-3% slower: the wait keeps fewer bytes in flight per CU, which
+// this memory system prefers.)
+__device__ __forceinline__ ReshardEntry reshard_entry(const ReshardArgs& a, uint32_t it) {
+  const uint32_t itc = it < (uint32_t)a.items ? it : (uint32_t)a.items - 1;
+  const uint32_t layer = fdiv(itc, a.div_layer);
+  const uint32_t e = fdiv(itc - layer * a.div_layer.d, a.div_seg);
+  const int64_t* gp = a.dst_ids + a.first + e;
+  const int32_t* sp = a.src_ids + a.first + e;
+  return ReshardEntry{*gp, *sp};
 }
 
+// Destination shard and slot of global page g, and whether the entry is copied at all (page ids
+// are below 2^31: the host limits M * N).
+__device__ __forceinline__ bool reshard_target(const ReshardArgs& a, int64_t g, int32_t sp, int& d, int64_t& s) {
+  const bool in = g >= 0 && g < (int64_t)a.dst_pages * a.n && sp >= 0 && sp < a.src_pages;
+  const uint32_t g32 = in ? (uint32_t)g : 0u;
+  const uint32_t q = a.n > 1 ? fdiv(g32, a.div_n) : g32;
+  d = (int)(g32 - q * (uint32_t)a.n);
+  s = q;
+  return in;
+}
+
+template <int UF, bool PART>
 __global__ __launch_bounds__(kReshardThreads) void reshard_kernel(ReshardArgs a) {
-  const int64_t per_layer = a.work * a.segs;
+  // The per-(layer, entry) side work first, spread over all threads: the page scales, the count
+  // of entries out of range and the per-destination page counts.  The copy loop below then
+  // holds no per-lane memory access, so the compiler keeps its loads and stores overlapped.
+  if (a.has_scales || a.bad || a.per_dst) {
+    const int64_t pairs = (int64_t)a.num_layers * a.work;
+    for (int64_t q = (int64_t)blockIdx.x * kReshardThreads + threadIdx.x; q < pairs;
+         q += (int64_t)gridDim.x * kReshardThreads) {
+      const int layer = (int)(q / a.work);
+      const int64_t e = q - (int64_t)layer * a.work;
+      const int64_t g = a.dst_ids[a.first + e];
+      const int32_t sp = a.src_ids[a.first + e];
+      int d;
+      int64_t s;
+      if (!reshard_target(a, g, sp, d, s)) {
+        if (a.bad) atomicAdd(a.bad, 1);
+        continue;
+      }
+      if (a.dst_filter >= 0 && d != a.dst_filter) continue;
+      if (a.per_dst && layer == 0) atomicAdd((unsigned long long*)&a.per_dst[d], 1ull);
+      if (a.has_scales) {
+        int r, begin;
+        layer_owner(layer, a.num_layers, a.num_sources, r, begin);
+        a.dst_scale[d][(int64_t)layer * a.dst_pages + s] = a.src_scale[r][(int64_t)(layer - begin) * a.src_pages + sp];
+      }
+    }
+  }
   ReshardEntry en = reshard_entry(a, blockIdx.x);
-  for (int64_t it = blockIdx.x; it < a.items; it += gridDim.x) {
-    const ReshardEntry nx = reshard_entry(a, it + gridDim.x);  // in flight during this copy
-    const int layer = (int)(it / per_layer);
-    const int64_t rest = it - (int64_t)layer * per_layer;
-    const int sg = (int)(rest % a.segs);
-    const int64_t g = en.g;
-    const int32_t sp = en.sp;
-    en = nx;
+  for (uint32_t it = blockIdx.x; it < (uint32_t)a.items; it += gridDim.x) {
+    const uint32_t layer = fdiv(it, a.div_layer);
+    const uint32_t rest = it - layer * a.div_layer.d;
+    const uint32_t e = fdiv(rest, a.div_seg);
+    const int sg = (int)(rest - e * (uint32_t)a.segs);
+    const ReshardEntry cur = en;
     int d;
     int64_t s;
-    if (a.n > 1) {
-      d = (int)(g % a.n);
-      s = g / a.n;
-    } else {
-      d = 0;
-      s = g;
-    }
-    const bool ok = g >= 0 && s < a.dst_pages && sp >= 0 && sp < a.src_pages;
-    if (!ok) {
-      if (sg == 0 && threadIdx.x == 0 && a.bad) atomicAdd(a.bad, 1);
+    const uint32_t nxt = it + gridDim.x;
+    if (!reshard_target(a, cur.g, cur.sp, d, s) || (a.dst_filter >= 0 && d != a.dst_filter)) {
+      en = reshard_entry(a, nxt);
       continue;
     }
-    if (a.dst_filter >= 0 && d != a.dst_filter) continue;
-    if (a.per_dst && layer == 0 && sg == 0 && threadIdx.x == 0) atomicAdd((unsigned long long*)&a.per_dst[d], 1ull);
     int r, begin;
-    layer_owner(layer, a.num_layers, a.num_sources, r, begin);
+    layer_owner((int)layer, a.num_layers, a.num_sources, r, begin);
     const int64_t off = (int64_t)sg * a.seg_bytes;
-    const int64_t src_off = ((int64_t)(layer - begin) * a.src_pages + sp) * a.page_bytes + off;
+    const int64_t src_off = ((int64_t)((int)layer - begin) * a.src_pages + cur.sp) * a.page_bytes + off;
     const int64_t dst_off = ((int64_t)layer * a.dst_pages + s) * a.page_bytes + off;
     const u32x4* __restrict__ src = reinterpret_cast<const u32x4*>(a.src[r] + src_off);
     u32x4* __restrict__ dst = reinterpret_cast<u32x4*>(a.dst[d] + dst_off);
     const int64_t len = (a.page_bytes - off) < a.seg_bytes ? (a.page_bytes - off) : a.seg_bytes;
-    const int chunks = (int)(len >> 4);  // <= kReshardThreads * kReshardUnroll
-    u32x4 v[kReshardUnroll];
-#pragma unroll
-    for (int u = 0; u < kReshardUnroll; ++u) {
-      const int c = u * kReshardThreads + threadIdx.x;
-      if (c < chunks) v[u] = __builtin_nontemporal_load(src + c);
-    }
-#pragma unroll
-    for (int u = 0; u < kReshardUnroll; ++u) {
-      const int c = u * kReshardThreads + threadIdx.x;
-      if (c < chunks) __builtin_nontemporal_store(v[u], dst + c);
-    }
-    if (a.has_scales && sg == 0 && threadIdx.x == 0) {
-      a.dst_scale[d][(int64_t)layer * a.dst_pages + s] =
-          a.src_scale[r][(int64_t)(layer - begin) * a.src_pages + sp];
-    }
+    copy_segment<UF, PART>(src, (int)(len >> 4), (int)(a.seg_bytes >> 4),
+                           [dst](int c, const u32x4& v) { __builtin_nontemporal_store(v, dst + c); },
+                           [&]() { en = reshard_entry(a, nxt); });
   }
 }
 
@@ -190,6 +276,7 @@ __device__ __forceinline__ int64_t token_request_base(const TokenReshardArgs& a,
 // u = (k*P + x) div N, row u mod P of the request's virtual page k div N, whose slot is
 // g_{o + (k div N) N} div N on every shard.  A page is token_rows blocks of P rows of row_bytes;
 // token x is row x of each block, and so is its destination row.
+template <int UF, bool PART>
 __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenReshardArgs a) {
   // the destination pools' base addresses, indexed per lane below, from LDS
   __shared__ uint8_t* s_dst[kMaxShards];
@@ -224,26 +311,18 @@ __global__ __launch_bounds__(kReshardThreads) void reshard_tokens_kernel(TokenRe
     const int d0 = (int)(t0 % a.n);
     const int y0 = (int)((t0 / a.n) % a.page_size);
     const int c0 = (int)(off0 >> 4);  // first 16-byte chunk of the segment in the page
-    u32x4 v[kReshardUnroll];
-#pragma unroll
-    for (int q = 0; q < kReshardUnroll; ++q) {
-      const int c = q * kReshardThreads + threadIdx.x;
-      if (c < chunks) v[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off0) + c);
-    }
-#pragma unroll
-    for (int q = 0; q < kReshardUnroll; ++q) {
-      const int c = q * kReshardThreads + threadIdx.x;
-      if (c < chunks) {
-        const int ci = c0 + c;  // chunk in the page: block, token row, chunk within the row
-        const int blk = small_div(ci, a.block16, a.r_block16), rem = ci - blk * a.block16;
-        const int x = small_div(rem, a.row16, a.r_row16), cr = rem - x * a.row16;
-        const int sx = d0 + x, dq = small_div(sx, a.n, a.r_n);
-        const int d = sx - dq * a.n;
-        const int y = y0 + dq >= a.page_size ? y0 + dq - a.page_size : y0 + dq;
-        __builtin_nontemporal_store(
-            v[q], reinterpret_cast<u32x4*>(s_dst[d] + dst_page) + ((int64_t)blk * a.page_size + y) * a.row16 + cr);
-      }
-    }
+    uint8_t* const* dsts = s_dst;
+    copy_segment<UF, PART>(reinterpret_cast<const u32x4*>(src + off0), chunks, (int)(a.seg_bytes >> 4),
+                           [&a, dsts, dst_page, c0, d0, y0](int c, const u32x4& v) {
+      const int ci = c0 + c;  // chunk in the page: block, token row, chunk within the row
+      const int blk = small_div(ci, a.block16, a.r_block16), rem = ci - blk * a.block16;
+      const int x = small_div(rem, a.row16, a.r_row16), cr = rem - x * a.row16;
+      const int sx = d0 + x, dq = small_div(sx, a.n, a.r_n);
+      const int d = sx - dq * a.n;
+      const int y = y0 + dq >= a.page_size ? y0 + dq - a.page_size : y0 + dq;
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(dsts[d] + dst_page) + ((int64_t)blk * a.page_size + y) * a.row16 + cr);
+    }, []() {});
   }
 }
 
@@ -268,6 +347,29 @@ static int check_unique_on_device(const int64_t* dst_ids, int64_t num_pages, int
                      (long long)h[(size_t)dup], (long long)dup);
   return DCPKV_OK;
 }
+
+// Launch KERNEL<UF, PART> for full segments of SEG_CHUNKS chunks: UF = SEG_CHUNKS / 256 whole
+// rounds (at most kReshardMaxUnroll) and PART when a partial round is left.
+#define DCPKV_SEGMENT_DISPATCH(KERNEL, SEG_CHUNKS, GRID, ST, ARGS)                                     \
+  do {                                                                                              \
+    const int uf_ = (int)((SEG_CHUNKS) / kReshardThreads);                                          \
+    const bool part_ = ((SEG_CHUNKS) % kReshardThreads) != 0;                                       \
+    const dim3 g_((unsigned)(GRID)), b_(kReshardThreads);                                           \
+    switch (uf_ * 2 + (part_ ? 1 : 0)) {                                                            \
+      case 1: hipLaunchKernelGGL((KERNEL<0, true>), g_, b_, 0, ST, ARGS); break;                    \
+      case 2: hipLaunchKernelGGL((KERNEL<1, false>), g_, b_, 0, ST, ARGS); break;                   \
+      case 3: hipLaunchKernelGGL((KERNEL<1, true>), g_, b_, 0, ST, ARGS); break;                    \
+      case 4: hipLaunchKernelGGL((KERNEL<2, false>), g_, b_, 0, ST, ARGS); break;                   \
+      case 5: hipLaunchKernelGGL((KERNEL<2, true>), g_, b_, 0, ST, ARGS); break;                    \
+      case 6: hipLaunchKernelGGL((KERNEL<3, false>), g_, b_, 0, ST, ARGS); break;                   \
+      case 7: hipLaunchKernelGGL((KERNEL<3, true>), g_, b_, 0, ST, ARGS); break;                    \
+      case 8: hipLaunchKernelGGL((KERNEL<4, false>), g_, b_, 0, ST, ARGS); break;                   \
+      case 9: hipLaunchKernelGGL((KERNEL<4, true>), g_, b_, 0, ST, ARGS); break;                    \
+      case 10: hipLaunchKernelGGL((KERNEL<5, false>), g_, b_, 0, ST, ARGS); break;                  \
+      case 11: hipLaunchKernelGGL((KERNEL<5, true>), g_, b_, 0, ST, ARGS); break;                   \
+      default: hipLaunchKernelGGL((KERNEL<6, false>), g_, b_, 0, ST, ARGS); break;                  \
+    }                                                                                               \
+  } while (0)
 
 static int device_cus_reshard() {
   int dev = 0, cus = 0;
@@ -338,8 +440,10 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   a.bad = bad_entries;
   a.per_dst = pages_per_dst;
   a.page_bytes = D.page_bytes;
-  {  // near-equal segments of at most 36 KB, 16-byte multiples, covering the page exactly
-    const int64_t nseg = (D.page_bytes + kReshardSegMax - 1) / kReshardSegMax;
+  const int unroll = reshard_unroll(D.page_bytes);
+  {  // near-equal segments of at most 16 * 256 * unroll bytes, 16-byte multiples, covering the page
+    const int64_t seg_max = 16LL * kReshardThreads * unroll;
+    const int64_t nseg = (D.page_bytes + seg_max - 1) / seg_max;
     a.seg_bytes = (((D.page_bytes + nseg - 1) / nseg + 15) / 16) * 16;
     a.segs = (int32_t)((D.page_bytes + a.seg_bytes - 1) / a.seg_bytes);
   }
@@ -348,14 +452,21 @@ extern "C" int kv_reshard_pages(const kv_reshard_desc* desc, const void* const* 
   a.first = first_uncached;
   a.work = work;
   a.items = (int64_t)D.num_layers * work * a.segs;
+  if (a.items + (int64_t)device_cus_reshard() * kReshardBlocksPerCU >= (1LL << 31) ||
+      D.dst_pages * D.dcp_size >= (1LL << 31) || D.src_pages >= (1LL << 31))
+    return set_error(DCPKV_EINVAL, "reshard: %lld (layer, page, segment) items or %lld destination pages per layer "
+                     "(limit 2^31)", (long long)a.items, (long long)(D.dst_pages * D.dcp_size));
+  a.div_layer = make_fastdiv((uint32_t)(work * a.segs));
+  a.div_seg = make_fastdiv((uint32_t)a.segs);
+  a.div_n = make_fastdiv((uint32_t)D.dcp_size);
   a.num_layers = D.num_layers;
   a.num_sources = D.num_sources;
   a.n = D.dcp_size;
   a.dst_filter = D.dst_filter;
   a.has_scales = src_scales != nullptr;
   const int64_t grid = std::min<int64_t>(a.items, (int64_t)device_cus_reshard() * kReshardBlocksPerCU);
-  hipLaunchKernelGGL(reshard_kernel, dim3((unsigned)grid), dim3(kReshardThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DCPKV_SEGMENT_DISPATCH(reshard_kernel, a.seg_bytes >> 4, grid, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "reshard: launch failed: %s", hipGetErrorString(e));
   return DCPKV_OK;
@@ -408,8 +519,10 @@ extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* 
   a.dst_ids = dst_global_pages;
   a.bad = bad_entries;
   a.page_bytes = page_bytes;
+  const int unroll = reshard_unroll(page_bytes);
   {
-    const int64_t nseg = (page_bytes + kReshardSegMax - 1) / kReshardSegMax;
+    const int64_t seg_max = 16LL * kReshardThreads * unroll;
+    const int64_t nseg = (page_bytes + seg_max - 1) / seg_max;
     a.seg_bytes = (((page_bytes + nseg - 1) / nseg + 15) / 16) * 16;
     a.segs = (int32_t)((page_bytes + a.seg_bytes - 1) / a.seg_bytes);
   }
@@ -429,8 +542,8 @@ extern "C" int kv_reshard_tokens(const kv_token_reshard_desc* desc, const void* 
   a.r_block16 = 1.0f / (float)a.block16;
   a.r_n = 1.0f / (float)D.dcp_size;
   const int64_t grid = std::min<int64_t>(a.items, (int64_t)device_cus_reshard() * kReshardBlocksPerCU);
-  hipLaunchKernelGGL(reshard_tokens_kernel, dim3((unsigned)grid), dim3(kReshardThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DCPKV_SEGMENT_DISPATCH(reshard_tokens_kernel, a.seg_bytes >> 4, grid, st, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "token reshard: launch failed: %s", hipGetErrorString(e));
   return DCPKV_OK;

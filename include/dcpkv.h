@@ -437,6 +437,14 @@ DCPKV_API int dcp_lse_merge(int32_t dcp_size, int64_t rows, int32_t head_dim_v, 
 DCPKV_API int dcpkv_probe_mfma(int32_t kind, int32_t iters, float* sink, int64_t sink_floats, int64_t* out_flops,
                      void* stream);
 
+/* The copy ceiling the reshard is read against: `bytes` (a multiple of 16)
+ * from src to dst (device, 16-byte aligned, not overlapping) with the
+ * reshard's own copy loop (a persistent grid of 256-thread workgroups, two per
+ * CU, each thread issuing four non-temporal 16-byte loads before its stores)
+ * over one contiguous range instead of a page list.  Time it with events on
+ * `stream`.  EINVAL on bad arguments, EDEVICE if the launch fails. */
+DCPKV_API int dcpkv_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

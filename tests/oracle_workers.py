@@ -11,20 +11,30 @@ import numpy as np
 import oracle as O
 
 
-def reshard_passes(args) -> int:
-    """Scalar reshard passes over a host sample until the deadline; returns the pass count."""
-    src_h, n_dst, shape, num_layers, dcp_size, own, page_size, rows, row_bytes, g2, deadline = args
-    dst_h = [np.zeros(shape, np.uint8) for _ in range(n_dst)]
-    n = shape[1]
-    reps = 0
+def reshard_sample(args):
+    """Scalar reshard passes until the deadline over this worker's own page set: the sample pages
+    (one layer per source) tiled into about target_bytes of distinct source pages per source, moved
+    into N pools of their own.  Returns (bytes read + written, pages per source)."""
+    sample, page_bytes, dcp_size, own, page_size, rows, row_bytes, target_bytes, deadline = args
+    n_src = len(sample)
+    pages = max(1, int(target_bytes // (page_bytes * n_src)))
+    src_h = []
+    for r in range(n_src):
+        t = np.empty((2, pages, page_bytes), np.uint8)  # one layer + the transient slot
+        t[0] = np.resize(sample[r], (pages, page_bytes))
+        t[1] = 0x5A
+        src_h.append(t)
+    m = -(-pages // dcp_size)
+    dst_h = [np.zeros((n_src, m, page_bytes), np.uint8) for _ in range(dcp_size)]
+    ids = np.arange(pages)
+    moved = 0
     while time.time() < deadline:
         if own:
-            O.reshard_tokens(src_h, dst_h, num_layers, dcp_size, page_size, rows, row_bytes, np.arange(n),
-                             np.arange(n), 0)
+            O.reshard_tokens(src_h, dst_h, n_src, dcp_size, page_size, rows, row_bytes, ids, ids, 0)
         else:
-            O.reshard(src_h, dst_h, num_layers, dcp_size, np.arange(n), g2, 0)
-        reps += 1
-    return reps
+            O.reshard(src_h, dst_h, n_src, dcp_size, ids, ids, 0)
+        moved += 2 * pages * n_src * page_bytes
+    return moved, pages
 
 
 def _logical_kv(geo: dict, pages_h, scales_h, host_by_slot, global_pages, seq_len: int):
@@ -47,22 +57,25 @@ def _logical_kv(geo: dict, pages_h, scales_h, host_by_slot, global_pages, seq_le
 
 
 def request_rows(args):
-    """Decode one request's pages, then its per-shard partials and their merge head by head
-    until the deadline; returns (rows done, query-token pairs done)."""
+    """Decode one request's pages, then its per-shard partials and their merge head by head until
+    the deadline.  Returns (decode seconds, tokens decoded, head seconds, (token, query, head)
+    triples done, heads done)."""
     geo, pages_h, scales_h, host_by_slot, global_pages, seq_len, q, deadline = args
     if time.time() >= deadline:
-        return 0, 0
+        return 0.0, 0, 0.0, 0, 0
+    t0 = time.perf_counter()
     k, v = _logical_kv(geo, pages_h, scales_h, host_by_slot, global_pages, seq_len)
-    rows = done = 0
+    t1 = time.perf_counter()
+    heads = 0
     for h in range(geo["num_q_heads"]):
         po, pl = O.request_partials(q, k, v, seq_len, geo["softmax_scale"], global_pages, geo["page_size"],
                                     geo["dcp_size"], heads=[h], own=geo["own"])
         O.lse_merge(po[:, :, [h]], pl[:, :, [h]])
-        rows += 1
-        done += seq_len * geo["q_len"]
+        heads += 1
         if time.time() >= deadline:
             break
-    return rows, done
+    t2 = time.perf_counter()
+    return t1 - t0, seq_len, t2 - t1, heads * seq_len * geo["q_len"], heads
 
 
 def oracle_request_rows(args):

@@ -19,9 +19,12 @@ def _counter_csv(path, counter, rows):
                         "Counter_Value": value})
 
 
-def _bench_line(path, workload, kernel, own="page", src_hash="h0", algorithmic=1):
+def _bench_line(path, workload, calls, own="page"):
+    """A bench line of one workload whose timed calls are {name: (source hash, algorithmic bytes)}."""
     line = {"metric": "m", "config": {"workload": workload, "ownership": own},
-            "roofline": {"kernel": kernel, "source_hash": src_hash, "algorithmic_bytes": algorithmic}}
+            "parts": {"workloads": {workload: {"calls": {c: {"source_hash": h, "algorithmic_bytes": b}
+                                                          for c, (h, b) in calls.items()}}}},
+            "roofline": {"kernel": next(iter(calls))}}
     with open(path, "w") as f:
         f.write("[bench] some progress line\n" + json.dumps(line) + "\n")
 
@@ -40,21 +43,24 @@ def test_traffic_scaled_by_calibration_copy_and_grouped_per_launch(tmp_path):
     _counter_csv(write, "WRITE_SIZE", [(1, CALIB, 1048576)] + [(d, rs, 2000) for d in (2, 3, 4)] +
                  [(5, other, 99999)])
     line = tmp_path / "b.json"
-    _bench_line(line, "wl", "reshard_kernel", src_hash="abc", algorithmic=4_000_000)
+    _bench_line(line, "wl", {"reshard_kernel": ("abc", 4_000_000)})
     db = tmp_path / "traffic.json"
-    e = bench.pmc_summarize(str(fetch), str(write), str(line), 1024, path=str(db))
-    assert e["launches"] == 3
+    stored = bench.pmc_summarize(str(fetch), str(write), str(line), 1024, path=str(db))
+    assert set(stored) == {"wl:reshard_kernel"}
+    e = stored["wl:reshard_kernel"]
+    assert e["launches"] == 3 and e["algorithmic_bytes_per_launch"] == 4_000_000
     assert e["scale_fetch"] == 2.0 and e["scale_write"] == 1.0
     assert e["fetch_kib_per_launch"] == 1000.0 and e["write_kib_per_launch"] == 2000.0
     assert e["hbm_bytes_per_launch"] == 1000 * 1024 * 2 + 2000 * 1024
-    assert bench.load_traffic("wl:reshard_kernel", "abc", 0, path=str(db)) == 4_096_000
-    assert bench.load_traffic("wl:reshard_kernel", "changed", 0, path=str(db)) is None
-    assert bench.load_traffic("other:reshard_kernel", "abc", 0, path=str(db)) is None
+    assert bench.load_traffic("wl:reshard_kernel", "abc", path=str(db)) == 4_096_000
+    assert bench.load_traffic("wl:reshard_kernel", "changed", path=str(db)) is None
+    assert bench.load_traffic("other:reshard_kernel", "abc", path=str(db)) is None
 
 
 def test_traffic_of_the_decode_call_sums_its_kernels_per_launch(tmp_path):
     # one launch of the call = planner + partial kernel + chunk reduction; launches are counted
-    # by the partial kernel; token ownership gets its own key
+    # by the partial kernel; token ownership gets its own key; a call whose kernels are not in
+    # the counter files (the reshard here) is left out
     fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
     ks = ["dcpkv::plan_kernel(dcpkv::AttnParams)", "dcpkv::mla_fp8_kernel(dcpkv::AttnParams)",
           "dcpkv::chunk_reduce_kernel(dcpkv::AttnParams)"]
@@ -68,9 +74,10 @@ def test_traffic_of_the_decode_call_sums_its_kernels_per_launch(tmp_path):
     _counter_csv(fetch, "FETCH_SIZE", rows_f)
     _counter_csv(write, "WRITE_SIZE", rows_w)
     line = tmp_path / "b.json"
-    _bench_line(line, "mla", "dcp_decode_partial (plan + partial + chunk-reduce kernels)", own="token")
+    _bench_line(line, "mla", {"dcp_decode_partial": ("h1", 10), "reshard_kernel": ("h2", 20)}, own="token")
     db = tmp_path / "traffic.json"
-    e = bench.pmc_summarize(str(fetch), str(write), str(line), 1024, path=str(db))
+    stored = bench.pmc_summarize(str(fetch), str(write), str(line), 1024, path=str(db))
+    e = stored["mla:dcp_decode_partial:token"]
     assert e["launches"] == 2
     assert e["fetch_kib_per_launch"] == 530.0 and e["write_kib_per_launch"] == 110.0
     assert e["hbm_bytes_per_launch"] == 530 * 1024 * 2 + 110 * 1024
@@ -81,3 +88,17 @@ def test_kernel_source_hash_follows_the_sources():
     a = bench.kernel_source_hash(["reshard.hip"])
     assert a == bench.kernel_source_hash(["reshard.hip"]) and len(a) == 16
     assert a != bench.kernel_source_hash(["reshard.hip", "common.h"])
+
+
+def test_default_run_covers_the_four_full_size_workloads_with_the_long_mix_as_headline():
+    a = bench.parse([])
+    assert a.workload == "all" and a.gpus == 1
+    assert bench.WORKLOADS == ("gqa_bf16_16x4k-32k", "reshard_mla_128k", "mla_fp8_48x100k",
+                               "mla_fp8_longmix_verify")
+    assert bench.HEADLINE == "mla_fp8_longmix_verify"
+    assert 1 <= bench.cpu_workers() <= 16
+
+
+def test_device_telemetry_never_raises():
+    t = bench.device_telemetry()
+    assert isinstance(t, dict)

@@ -302,3 +302,7 @@ def test_probe_rejects_bad_arguments_on_host():
     assert L._lib.dcpkv_probe_mfma(0, 10, v, L.PROBE_SINK_FLOATS - 1, C.byref(flops), None) == E
     assert L._lib.dcpkv_probe_mfma(0, 10, None, L.PROBE_SINK_FLOATS, C.byref(flops), None) == E
     assert L._lib.dcpkv_probe_mfma(1, 10, v, L.PROBE_SINK_FLOATS, None, None) == E
+    assert L._lib.dcpkv_probe_copy(v, C.c_void_p(1 << 20), 100, None) == E          # not a multiple of 16
+    assert L._lib.dcpkv_probe_copy(C.c_void_p(264), C.c_void_p(1 << 20), 64, None) == E  # misaligned
+    assert L._lib.dcpkv_probe_copy(v, C.c_void_p(512), 1024, None) == E            # overlapping
+    assert L._lib.dcpkv_probe_copy(None, v, 64, None) == E

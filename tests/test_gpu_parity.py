@@ -836,3 +836,15 @@ def test_probe_mfma_counts_its_work(kind, per_mfma):
     rate = flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
     H.log(f"  probe kind {kind}: {rate:.0f} TFLOP/s")
     assert 0 < rate < (2600 if kind == 0 else 5200)
+
+
+def test_probe_copy_copies_every_byte():
+    """The streaming copy the reshard is read against moves its bytes exactly (odd sizes leave a
+    short last segment; bytes past the end stay untouched)."""
+    for nbytes in (16, 36864 * 3 + 48, (5 << 20) + 160):
+        g = torch.Generator(device=DEV).manual_seed(nbytes)
+        src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device=DEV, generator=g)
+        dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device=DEV)
+        K.dcpkv_probe_copy(src, dst, nbytes)
+        _sync()
+        assert torch.equal(dst[:nbytes], src[:nbytes]) and (dst[nbytes:] == 0).all()
