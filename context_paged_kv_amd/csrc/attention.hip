@@ -156,6 +156,100 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Even split plan (GQA kernel): page prefix sums and where each wave starts
+// ---------------------------------------------------------------------------
+
+constexpr int kEvenPlanThreads = 256;
+
+__global__ __launch_bounds__(kEvenPlanThreads) void plan_even_kernel(AttnParams p) {
+  __shared__ int64_t s_pfx[kEvenMaxPairs + 1];
+  __shared__ int64_t s_wsum[kEvenPlanThreads / 64];
+  __shared__ int32_t s_first[kEvenPlanThreads];
+  __shared__ int32_t s_next[kEvenMaxPairs];
+  const int tid = threadIdx.x;
+  const int num_pairs = p.shard_count * p.batch;  // <= kEvenMaxPairs (the host checks)
+  for (int i = tid; i < num_pairs; i += kEvenPlanThreads) {
+    const int d = p.shard_begin + i / p.batch, b = i % p.batch;
+    s_pfx[i + 1] = local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local, p.tok_il);
+  }
+  if (tid == 0) s_pfx[0] = 0;
+  __syncthreads();
+  // inclusive prefix sums over s_pfx[1 .. num_pairs]: each thread a block of pairs, then a
+  // scan of the block sums
+  const int per = (num_pairs + kEvenPlanThreads - 1) / kEvenPlanThreads;
+  const int lo = min(num_pairs, tid * per), hi = min(num_pairs, lo + per);
+  int64_t sum = 0;
+  int first = num_pairs;  // first pair with local pages in this thread's block
+  for (int i = hi - 1; i >= lo; --i) {
+    sum += s_pfx[i + 1];
+    if (s_pfx[i + 1] > 0) first = i;
+  }
+  int64_t incl = sum;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t u = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) s_wsum[tid >> 6] = incl;
+  s_first[tid] = first;
+  __syncthreads();
+  int64_t run = incl - sum;
+  for (int k = 0; k < (tid >> 6); ++k) run += s_wsum[k];
+  // the next pair with pages after this block: the first later block that has one
+  int after = num_pairs;
+  for (int t = tid + 1; t < kEvenPlanThreads; ++t)
+    if (s_first[t] < num_pairs) {
+      after = s_first[t];
+      break;
+    }
+  // pair entries (k = next pair with pages), written back to front within the block
+  for (int i = hi - 1; i >= lo; --i) {
+    const int nl = (int)s_pfx[i + 1];
+    p.pairs[i] = PairPlan{0, -1, after, nl};
+    s_next[i] = after;
+    if (nl > 0) after = i;
+  }
+  for (int i = lo; i < hi; ++i) {
+    run += s_pfx[i + 1];
+    s_pfx[i + 1] = run;
+  }
+  __syncthreads();
+  for (int i = tid; i <= num_pairs; i += kEvenPlanThreads) p.pair_pfx[i] = s_pfx[i];
+  const int64_t P = s_pfx[num_pairs] * p.hkv;
+  const int G = (int)min<int64_t>(p.slots, P);
+  for (int w = tid; w < p.slots; w += kEvenPlanThreads) {
+    WaveStart ws = {0, 0, 0, 0, 0, num_pairs, 0, 0};
+    if (w < G) {
+      const int64_t x0 = (int64_t)w * P / G, x1 = (int64_t)(w + 1) * P / G;
+      // the pair holding item x0: the last one whose first item is <= x0 (it has pages)
+      int a = 0, z = num_pairs - 1;
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (s_pfx[mid] * p.hkv <= x0) a = mid; else z = mid - 1;
+      }
+      const int64_t nl = s_pfx[a + 1] - s_pfx[a];
+      const int64_t off = x0 - s_pfx[a] * p.hkv;
+      ws.pair = a;
+      ws.hb = (int)(off / nl);
+      ws.j0 = (int)(off % nl);
+      ws.count = (int)(x1 - x0);
+      ws.n_local = (int)nl;
+      ws.next_pair = s_next[a];
+      ws.seq_len = p.seq_lens[a % p.batch];
+    }
+    p.wstarts[w] = ws;
+  }
+  if (tid == 0) {
+    p.hdr->total_chunks = 0;
+    p.hdr->ws_chunks = 0;
+    p.hdr->fallback = 0;
+    p.hdr->waves = G;
+    p.hdr->total_work = P;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Generic VALU partial kernel
 // ---------------------------------------------------------------------------
 
@@ -388,6 +482,76 @@ __global__ __launch_bounds__(256) void chunk_reduce_kernel(AttnParams p) {
                  p.dv, p.partial_out + out_row * p.dv, p.partial_lse + out_row);
 }
 
+// Even split: merge the parts of every segment that spans several waves (the same LSE
+// algebra as the cross-shard merge, accumulated part by part), and write the rows of
+// pairs without local pages (O = 0, LSE = -inf).  One workgroup per (pair, KV head):
+// thread (row r, dims 8 (tid mod 16) .. + 8).
+__global__ __launch_bounds__(256) void even_reduce_kernel(AttnParams p) {
+  const int pair = blockIdx.x, hb = blockIdx.y;
+  const int tid = threadIdx.x, r = tid >> 4, c8 = (tid & 15) * 8;
+  const int rows = p.group * p.q_len;
+  if (r >= rows || c8 >= p.dv) return;
+  const int d = p.shard_begin + pair / p.batch, b = pair % p.batch;
+  const int t = r / p.group, h = hb * p.group + r % p.group;
+  const int64_t out_row = ((int64_t)d * p.batch + b) * p.rows + (int64_t)t * p.hq + h;
+  float* out = p.partial_out + out_row * p.dv + c8;
+  const int nl = p.pairs[pair].n_local;
+  if (nl == 0) {
+    *reinterpret_cast<float4*>(out) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(out + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+    if ((tid & 15) == 0) p.partial_lse[out_row] = kNegInf;
+    return;
+  }
+  const int64_t P = p.hdr->total_work;
+  const int G = p.hdr->waves;
+  const int64_t X = p.pair_pfx[pair] * p.hkv + (int64_t)hb * nl;
+  const int w0 = even_wave_of(X, P, G), w1 = even_wave_of(X + nl - 1, P, G);
+  if (w0 == w1) return;  // one wave held the whole segment and wrote it
+  // wave w0's part is its first segment's (slot 2 w0) when its range starts here, else its
+  // last one's (2 w0 + 1); the waves after it start inside the segment (slot 2 w)
+  const int64_t first_slot = ((int64_t)w0 * P / G == X) ? 2 * (int64_t)w0 : 2 * (int64_t)w0 + 1;
+  const int K = w1 - w0 + 1;
+  float m = kNegInf, sum = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < K; i0 += 4) {
+    float lv[4];
+    float4 xa[4], xb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // all loads of four parts at once
+      const int i = min(i0 + u, K - 1);
+      const int64_t row = (i == 0 ? first_slot : 2 * ((int64_t)w0 + i)) * kEvenRows + r;
+      lv[u] = p.ws_lse[row];
+      xa[u] = *reinterpret_cast<const float4*>(p.ws_o + row * p.dv + c8);
+      xb[u] = *reinterpret_cast<const float4*>(p.ws_o + row * p.dv + c8 + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u >= K || lv[u] == kNegInf) continue;  // an empty part's O may hold anything
+      if (lv[u] > m) {
+        const float sc = m == kNegInf ? 0.f : expf(m - lv[u]);
+        sum *= sc;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] *= sc;
+        m = lv[u];
+      }
+      const float wgt = expf(lv[u] - m);
+      sum += wgt;
+      acc[0] += wgt * xa[u].x;
+      acc[1] += wgt * xa[u].y;
+      acc[2] += wgt * xa[u].z;
+      acc[3] += wgt * xa[u].w;
+      acc[4] += wgt * xb[u].x;
+      acc[5] += wgt * xb[u].y;
+      acc[6] += wgt * xb[u].z;
+      acc[7] += wgt * xb[u].w;
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  *reinterpret_cast<float4*>(out) = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<float4*>(out + 4) = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if ((tid & 15) == 0) p.partial_lse[out_row] = sum > 0.f ? m + logf(sum) : kNegInf;
+}
+
 // ---------------------------------------------------------------------------
 // Cross-shard merge (dcp_lse_merge)
 // ---------------------------------------------------------------------------
@@ -431,6 +595,13 @@ static int mla_score_mode() {
   return !std::strcmp(e, "fp8") ? 1 : (!std::strcmp(e, "exact") ? 2 : 0);
 }
 
+// DCPKV_GQA_SPLIT=chunks gives the GQA kernel the chunk plan (the one it takes beyond
+// kEvenMaxPairs pairs) at any batch; the default is the even split.
+static bool gqa_force_chunks() {
+  const char* e = std::getenv("DCPKV_GQA_SPLIT");
+  return e && !std::strcmp(e, "chunks");
+}
+
 static int validate(const dcp_attn_desc& D) {
   const bool split = D.kv_layout == DCPKV_LAYOUT_SPLIT, mla = D.kv_layout == DCPKV_LAYOUT_MLA;
   if (!split && !mla) return set_error(DCPKV_EINVAL, "attn: unknown kv_layout %d", D.kv_layout);
@@ -472,13 +643,16 @@ static int64_t page_bytes_of(const dcp_attn_desc& D) {
 struct Geometry {
   int kind;          // KernelKind
   int rb_rows, rb_per_head, hb_count, rows, chunk_pages;
+  bool even;         // even split plan (GQA kernel) instead of chunks
+  int slots;         // even split: waves launched
   int64_t ws_cap;
-  size_t hdr_off, pairs_off, chunks_off, o_off, lse_off, bytes;
+  size_t hdr_off, pairs_off, chunks_off, pfx_off, wst_off, o_off, lse_off, bytes;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus, Geometry& g) {
+  g = Geometry{};
   g.kind = choose_kernel(D);
   g.rb_rows = kernel_rows_per_block(g.kind, D);
   const int rg_rows = (D.num_q_heads / D.num_kv_heads) * D.q_len;
@@ -504,6 +678,20 @@ static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus,
   g.o_off = align256(g.chunks_off + (size_t)(pairs + est_pages / c + 1) * sizeof(ChunkPlan));
   g.lse_off = align256(g.o_off + (size_t)g.ws_cap * g.rows * D.head_dim_v * sizeof(float));
   g.bytes = align256(g.lse_off + (size_t)g.ws_cap * g.rows * sizeof(float));
+  // The GQA kernel splits evenly when the plan's pairs fit the planner's LDS and the
+  // page-items of one wave fit 32 bits: pair prefix sums, one start per wave and two
+  // part slots of kEvenRows rows per wave.
+  g.slots = (int)std::min<int64_t>((int64_t)cus * kernel_resident_per_cu(g.kind), 1 << 20);
+  if (g.kind == KK_GQA_BF16 && pairs <= kEvenMaxPairs && est_pages * D.num_kv_heads < (1LL << 31) &&
+      !gqa_force_chunks()) {
+    g.even = true;
+    g.pfx_off = align256(g.pairs_off + (size_t)pairs * sizeof(PairPlan));
+    g.wst_off = align256(g.pfx_off + (size_t)(pairs + 1) * sizeof(int64_t));
+    g.o_off = align256(g.wst_off + (size_t)g.slots * sizeof(WaveStart));
+    g.ws_cap = 2 * (int64_t)g.slots;
+    g.lse_off = align256(g.o_off + (size_t)g.ws_cap * kEvenRows * D.head_dim_v * sizeof(float));
+    g.bytes = align256(g.lse_off + (size_t)g.ws_cap * kEvenRows * sizeof(float));
+  }
 }
 
 // Fit the geometry into `cap` bytes by holding fewer chunk partials (a coarser split: the
@@ -511,6 +699,7 @@ static void plan_geometry(const dcp_attn_desc& D, int64_t total_tokens, int cus,
 // plan without chunk partials does not fit.
 static bool cap_geometry(const dcp_attn_desc& D, size_t cap, Geometry& g) {
   if (g.bytes <= cap) return true;
+  if (g.even) return false;  // its size is fixed by the device (two part slots per wave)
   if (g.o_off + 512 > cap) return false;
   const size_t per_slot = (size_t)g.rows * (D.head_dim_v + 1) * sizeof(float);
   const int64_t fit = (int64_t)((cap - g.o_off - 512) / per_slot);
@@ -604,6 +793,10 @@ static int decode_partial(const dcp_attn_desc* desc, const void* q, const void* 
   p.hdr = reinterpret_cast<PlanHeader*>(ws + g.hdr_off);
   p.pairs = reinterpret_cast<PairPlan*>(ws + g.pairs_off);
   p.chunks = reinterpret_cast<ChunkPlan*>(ws + g.chunks_off);
+  p.pair_pfx = g.even ? reinterpret_cast<int64_t*>(ws + g.pfx_off) : nullptr;
+  p.wstarts = g.even ? reinterpret_cast<WaveStart*>(ws + g.wst_off) : nullptr;
+  // even split: up to 64 x 4 pairs every wave plans its own range (no planner launch)
+  p.even = g.even ? ((int64_t)shard_count * D.batch <= 256 ? 2 : 1) : 0;
   p.ws_o = reinterpret_cast<float*>(ws + g.o_off);
   p.ws_lse = reinterpret_cast<float*>(ws + g.lse_off);
   p.ws_cap = g.ws_cap;
@@ -625,7 +818,8 @@ static int decode_partial(const dcp_attn_desc* desc, const void* q, const void* 
   p.shard_begin = shard_begin;
   p.shard_count = shard_count;
   p.chunk_pages = g.chunk_pages;
-  p.slots = (int32_t)std::min<int64_t>((int64_t)device_cus() * kernel_resident_per_cu(g.kind), INT32_MAX);
+  p.slots = g.even ? g.slots
+                   : (int32_t)std::min<int64_t>((int64_t)device_cus() * kernel_resident_per_cu(g.kind), INT32_MAX);
   p.group = D.num_q_heads / D.num_kv_heads;
   p.rows = g.rows;
   p.hb_count = g.hb_count;
@@ -645,15 +839,21 @@ static int decode_partial(const dcp_attn_desc* desc, const void* q, const void* 
                             (int64_t)D.batch * (D.token_interleave ? D.dcp_size : 1);
   p.max_chunks = pairs + est_pages / g.chunk_pages + 1;
   const int64_t item_bound = p.max_chunks * g.hb_count;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
+  if (p.even == 1)
+    hipLaunchKernelGGL(plan_even_kernel, dim3(1), dim3(kEvenPlanThreads), 0, st, p);
+  else if (!p.even)
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: plan launch: %s", hipGetErrorString(e));
   rc = launch_partial(g.kind, p, D, cus, item_bound, st);
   if (rc) return rc;
 
-  hipLaunchKernelGGL(chunk_reduce_kernel,
-                     dim3((unsigned)pairs, (unsigned)((g.rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock)),
-                     dim3(256), 0, st, p);
+  if (g.even)
+    hipLaunchKernelGGL(even_reduce_kernel, dim3((unsigned)pairs, (unsigned)D.num_kv_heads), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL(chunk_reduce_kernel,
+                       dim3((unsigned)pairs, (unsigned)((g.rows + kRowsPerMergeBlock - 1) / kRowsPerMergeBlock)),
+                       dim3(256), 0, st, p);
   e = hipGetLastError();
   if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "attn: reduce launch: %s", hipGetErrorString(e));
   return DCPKV_OK;

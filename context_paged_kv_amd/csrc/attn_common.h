@@ -27,7 +27,7 @@ constexpr float kNegInf = -INFINITY;
 struct PairPlan {
   int32_t chunk_begin;  // exclusive prefix sum of k over pairs
   int32_t ws_begin;     // first workspace chunk slot (k >= 2), else -1
-  int32_t k;            // chunks of this pair
+  int32_t k;            // chunks of this pair; even split: the next pair with local pages (pairs if none)
   int32_t n_local;      // local pages of this pair
 };
 
@@ -43,9 +43,38 @@ struct alignas(16) ChunkPlan {
 struct PlanHeader {
   int32_t total_chunks;
   int32_t ws_chunks;
-  int32_t fallback;  // 1 when the workspace could not hold the split and k = 1 was used
-  int32_t pad[13];
+  int32_t fallback;     // 1 when the workspace could not hold the split and k = 1 was used
+  int32_t waves;        // even split: waves with work (G)
+  int64_t total_work;   // even split: page-items over all (pair, KV head) segments (P)
+  int32_t pad[10];
 };
+
+// Even split (the GQA kernel's plan).  The work is the sequence of page-items
+// (pair, KV head, local page) in that order, split into P pages of segments
+// (pair, KV head) of n_local pages each.  Wave w of the grid takes items
+// [floor(w P / G), floor((w + 1) P / G)), so every wave streams the same number
+// of pages (to one) and no wave waits on another.  A segment inside one wave's
+// range is written straight to partial_out; the parts of a segment that spans
+// several waves go to workspace slots (a wave's first segment to slot 2w, its
+// last to 2w + 1) and the reduction merges them.  This is where wave w starts.
+struct alignas(16) WaveStart {
+  int32_t pair;       // pair of the first segment
+  int32_t hb;         // KV head of the first segment
+  int32_t j0;         // first local page
+  int32_t count;      // page-items of the wave (0: no work)
+  int32_t n_local;    // local pages of the pair
+  int32_t next_pair;  // the next pair with local pages (pairs if none)
+  int32_t seq_len;    // the pair's request length
+  int32_t pad;
+};
+
+constexpr int kEvenRows = 16;        // query rows of one segment (group x q_len <= 16)
+constexpr int kEvenMaxPairs = 4096;  // pairs the even planner holds in LDS
+
+// Wave whose range holds page-item x of the even split (G waves over P items).
+__device__ __forceinline__ int even_wave_of(int64_t x, int64_t P, int G) {
+  return (int)(((x + 1) * G - 1) / P);
+}
 
 struct AttnParams {
   const void* q;
@@ -58,6 +87,8 @@ struct AttnParams {
   PlanHeader* hdr;
   PairPlan* pairs;
   ChunkPlan* chunks;        // [max_chunks]
+  int64_t* pair_pfx;        // even split: local pages of pairs before each pair, [pairs + 1]
+  WaveStart* wstarts;       // even split: [slots]
   float* ws_o;
   float* ws_lse;
   int64_t ws_cap;           // chunk partial slots in the workspace
@@ -77,6 +108,7 @@ struct AttnParams {
   float scale;
   int32_t tok_il;       // 1: token t on shard t mod N; 0: page ownership
   int32_t mla_scores;   // fp8 MLA kernel: 0 exact scores for rows with outliers, 1 fp8 always, 2 exact always
+  int32_t even;         // 0: chunk plan; even split (GQA kernel): 1 from the planner, 2 planned by every wave
 };
 
 // Tokens of (request with seq_len tokens) held by shard d, and its local pages.

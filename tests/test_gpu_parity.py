@@ -37,12 +37,17 @@ def test_decode_tiny_fp32_full():
     H.log("  " + H.fmt_worst(worst))
 
 
-@pytest.mark.parametrize("seed_shift,q_len", [(0, 1), (1, 1), (2, 2), (3, 4)])
-def test_decode_gqa_bf16_small(seed_shift, q_len):
+@pytest.mark.parametrize("seed_shift,q_len,split", [(0, 1, "even"), (1, 1, "even"), (2, 2, "even"), (3, 4, "even"),
+                                                   (0, 1, "chunks"), (3, 4, "chunks")])
+def test_decode_gqa_bf16_small(seed_shift, q_len, split, monkeypatch):
+    # the GQA kernel under its even split (the default) and under the chunk plan it takes for
+    # batches beyond the even planner's pairs
     base = get_workload("gqa_bf16_16x4k-32k")
     w = scaled(base, seed=base.seed + 100 + seed_shift, seq_segments=((5, 70, 3000),), pool_pages=256,
                q_len=q_len)
-    H.log(f"decode gqa bf16 small seed {w.seed} q_len {q_len}")
+    H.log(f"decode gqa bf16 small seed {w.seed} q_len {q_len} split {split}")
+    if split == "chunks":
+        monkeypatch.setenv("DCPKV_GQA_SPLIT", "chunks")
     case = H.make_decode_case(w, DEV)
     outs = H.run_decode(case)
     _sync()
@@ -246,30 +251,7 @@ def test_decode_out_of_range_table_entries(name, force_generic, monkeypatch):
         monkeypatch.setenv("DCPKV_FORCE_GENERIC", "1")
     outs = H.run_decode(case)
     _sync()
-    tol_o, tol_l = H.tolerance(w)
-    heads = list(range(min(w.num_q_heads, 8)))
-    for b in range(w.num_requests):
-        T = int(case.seq_lens[b])
-        pb, psc = H.gather_request_pages(case.pools, case.scales, case.pages[b], n, case.layer)
-        k, v = H.oracle_logical_kv(w, pb, psc, T)
-        q = H.q_host(case, b)
-        po, pl = [], []
-        for d in range(n):
-            mask = O.shard_token_mask(case.pages[b], ps, T, n, d)
-            for dd, j, _ in holes.get(b, []):
-                if dd == d:  # local page j of shard d is sequence page j*N + d
-                    mask[(j * n + d) * ps:min(T, (j * n + d + 1) * ps)] = False
-            o_, l_ = O.request_attention(q, k, v, T, w.softmax_scale, mask, heads)
-            po.append(o_)
-            pl.append(l_)
-        po, pl = np.stack(po), np.stack(pl)
-        uo, ul = O.lse_merge(po, pl)
-        for d in range(n):
-            H.check_rows(f"partial d={d} b={b}", outs.partial_out[d, b][:, heads].cpu().numpy(),
-                         outs.partial_lse[d, b][:, heads].cpu().numpy(), po[d][:, heads], pl[d][:, heads],
-                         tol_o, tol_l)
-        H.check_rows(f"merged b={b}", outs.out[b][:, heads].cpu().numpy(), outs.lse[b][:, heads].cpu().numpy(),
-                     uo[:, heads], ul[:, heads], tol_o, tol_l)
+    _check_with_holes(case, outs, holes, heads=list(range(min(w.num_q_heads, 8))))
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "gqa_bf16_16x4k-32k", "mla_fp8_48x100k"])
@@ -342,8 +324,10 @@ def _local_pages(seq_lens, page_size, n):
     return out
 
 
-def test_decode_plan_splits_mixed_lengths_longest_first():
-    """Unequal pairs are split into chunks of at most C pages, emitted longest first."""
+def test_decode_plan_splits_mixed_lengths_longest_first(monkeypatch):
+    """Unequal pairs are split into chunks of at most C pages, emitted longest first (the
+    GQA kernel under its chunk plan)."""
+    monkeypatch.setenv("DCPKV_GQA_SPLIT", "chunks")
     base = get_workload("gqa_bf16_16x4k-32k")
     ps, n = base.page_size, base.dcp_size
     w = scaled(base, seed=base.seed + 240, seq_segments=((12, ps * n * 4, ps * n * 40), (2, 5, ps)),
@@ -361,10 +345,12 @@ def test_decode_plan_splits_mixed_lengths_longest_first():
     H.check_decode(case, outs, heads=list(range(8)))
 
 
-def test_decode_plan_keeps_equal_pairs_whole_when_they_fill_the_device():
+def test_decode_plan_keeps_equal_pairs_whole_when_they_fill_the_device(monkeypatch):
     """Equal-length pairs whose work items fill every workgroup slot in whole rounds keep one
-    chunk each (GQA kernel: four resident workgroups per compute unit, one per KV head and
-    chunk); one pair shorter than the rest breaks the rule and the long pairs split again."""
+    chunk each (GQA kernel under its chunk plan: four resident workgroups per compute unit,
+    one per KV head and chunk); one pair shorter than the rest breaks the rule and the long
+    pairs split again."""
+    monkeypatch.setenv("DCPKV_GQA_SPLIT", "chunks")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     base = get_workload("gqa_bf16_16x4k-32k")
     ps, n = base.page_size, base.dcp_size
@@ -386,6 +372,141 @@ def test_decode_plan_keeps_equal_pairs_whole_when_they_fill_the_device():
         else:
             assert total == pairs and (pp[:, 2] == 1).all()
         H.check_decode(case, outs, requests=[0, b - 1], heads=list(range(4)))
+
+
+def _read_even_plan(ws: torch.Tensor, pairs: int, slots: int):
+    """The even planner's output in the workspace: waves with work and page-items (header
+    words 3 and 4-5), the pair entries from byte 256 (16 bytes: -, -, next pair with pages,
+    local pages), the pairs' page prefix sums (int64) and the wave starts (32 bytes: pair,
+    KV head, first page, count, local pages, next pair, request length, -), each from the
+    next 256-byte boundary."""
+    raw = ws.cpu().numpy()
+    i32 = raw.view(np.int32)
+    waves, total = int(i32[3]), int(raw[16:24].view(np.int64)[0])
+    al = lambda x: (x + 255) // 256 * 256
+    pp = i32[64:64 + 4 * pairs].reshape(pairs, 4)
+    pfx_off = al(256 + 16 * pairs)
+    pfx = raw[pfx_off:pfx_off + 8 * (pairs + 1)].view(np.int64)
+    wst_off = al(pfx_off + 8 * (pairs + 1))
+    wst = i32[wst_off // 4:wst_off // 4 + 8 * slots].reshape(slots, 8)
+    return waves, total, pp, pfx, wst
+
+
+@pytest.mark.parametrize("segs", [((14, 64 * 4 * 4, 64 * 4 * 40), (2, 5, 64)),  # mixed lengths
+                                  ((3, 70, 300), (2, 10, 10), (2, 64 * 9, 64 * 9)),  # shards without pages
+                                  ((60, 64 * 4 * 2, 64 * 4 * 6), (10, 10, 60), (10, 64 * 9, 64 * 9))])  # 320 pairs
+def test_decode_gqa_even_plan_covers_every_page_item(segs):
+    """The even split: the pairs' local pages, their prefix sums, the next pair with pages and
+    the header (waves with work, page-items) the reduction reads.  Beyond 256 pairs, where the
+    planner writes the wave starts: the waves' ranges tile the page-items of the (pair, KV
+    head) segments in order, with counts that differ by at most one, and every start names
+    the segment and page of its first item and carries that pair's length and the next pair
+    with pages.  (Up to 256 pairs every wave plans its own range; the oracle comparison below
+    covers it.)"""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slots = cus * 4
+    base = get_workload("gqa_bf16_16x4k-32k")
+    ps, n, hkv = base.page_size, base.dcp_size, base.num_kv_heads
+    w = scaled(base, seed=base.seed + 260, seq_segments=segs, pool_pages=512, num_layers=1, attn_layer=0)
+    case = H.make_decode_case(w, DEV, seq_lens=np.concatenate(
+        [np.linspace(lo, hi, k).astype(np.int64) for k, lo, hi in segs]))
+    outs, ws = H.alloc_outputs(case)
+    H.run_decode(case, outs, ws)
+    _sync()
+    pairs = n * w.num_requests
+    waves, total, pp, pfx, wst = _read_even_plan(ws, pairs, slots)
+    nl = np.array(_local_pages(case.seq_lens, ps, n), dtype=np.int64)
+    assert (pp[:, 3] == nl).all()
+    assert (pfx == np.concatenate([[0], np.cumsum(nl)])).all()
+    P = int(nl.sum()) * hkv
+    assert total == P and waves == min(slots, P)
+    nxt = [next((j for j in range(i + 1, pairs) if nl[j] > 0), pairs) for i in range(pairs)]
+    assert (pp[:, 2] == np.array(nxt)).all()
+    if pairs <= 256:
+        H.check_decode(case, outs, heads=list(range(8)))
+        return
+    x = 0
+    for wv in range(slots):
+        pair, hb, j0, cnt, nlw, nxw, slw, _ = (int(v) for v in wst[wv])
+        if wv >= waves:
+            assert cnt == 0
+            continue
+        assert x == wv * P // waves and cnt == (wv + 1) * P // waves - x
+        assert pfx[pair] * hkv + hb * nl[pair] + j0 == x and 0 <= j0 < nl[pair] and 0 <= hb < hkv
+        assert nlw == nl[pair] and nxw == nxt[pair] and slw == int(case.seq_lens[pair % w.num_requests])
+        x += cnt
+    assert x == P
+    H.check_decode(case, outs, heads=list(range(8)))
+
+
+def _check_with_holes(case, outs, holes, heads):
+    """Partials and merge against the oracle with the table entries of `holes` ({request:
+    [(shard, local page, value)]}) out of range: those pages' tokens take no part."""
+    w = case.w
+    n, ps = w.dcp_size, w.page_size
+    tol_o, tol_l = H.tolerance(w)
+    for b in range(w.num_requests):
+        T = int(case.seq_lens[b])
+        pb, psc = H.gather_request_pages(case.pools, case.scales, case.pages[b], n, case.layer)
+        k, v = H.oracle_logical_kv(w, pb, psc, T)
+        q = H.q_host(case, b)
+        po, pl = [], []
+        for d in range(n):
+            mask = O.shard_token_mask(case.pages[b], ps, T, n, d)
+            for dd, j, _ in holes.get(b, []):
+                if dd == d:  # local page j of shard d is sequence page j*N + d
+                    mask[(j * n + d) * ps:min(T, (j * n + d + 1) * ps)] = False
+            o_, l_ = O.request_attention(q, k, v, T, w.softmax_scale, mask, heads)
+            po.append(o_)
+            pl.append(l_)
+        po, pl = np.stack(po), np.stack(pl)
+        uo, ul = O.lse_merge(po, pl)
+        for d in range(n):
+            H.check_rows(f"partial d={d} b={b}", outs.partial_out[d, b][:, heads].cpu().numpy(),
+                         outs.partial_lse[d, b][:, heads].cpu().numpy(), po[d][:, heads], pl[d][:, heads],
+                         tol_o, tol_l)
+        H.check_rows(f"merged b={b}", outs.out[b][:, heads].cpu().numpy(), outs.lse[b][:, heads].cpu().numpy(),
+                     uo[:, heads], ul[:, heads], tol_o, tol_l)
+
+
+def test_decode_gqa_even_segments_without_valid_pages():
+    """Even split, segments that span many waves (a few page-items per wave): a shard whose
+    first 66 local pages are out of range (its first page with a slot lies past the first
+    64-entry window), a shard with no page in range at all (its part is empty: O = 0,
+    LSE = -inf), and out-of-range pages at the ends of wave ranges."""
+    base = get_workload("gqa_bf16_16x4k-32k")
+    ps, n = base.page_size, base.dcp_size
+    long_t = ps * n * 70 + 17  # 71 local pages on shard 0, 70 on the others
+    w = scaled(base, seed=base.seed + 270, seq_segments=((1, long_t, long_t), (1, ps * n * 12, ps * n * 12),
+                                                        (1, 300, 300)), pool_pages=1024, q_len=2,
+               num_layers=1, attn_layer=0)
+    case = H.make_decode_case(w, DEV)
+    tables = case.tables.copy()
+    holes = {0: [(0, j, -1) for j in range(66)] + [(2, 30, w.pool_pages)],
+             1: [(1, j, -3) for j in range(12)] + [(3, 11, 1 << 28)]}
+    for b, hs in holes.items():
+        for d, j, v in hs:
+            tables[d, b, j] = v
+    case.bt_dev.copy_(torch.from_numpy(tables))
+    H.log("decode gqa even split: 71-page shard with 66 holes, an all-hole shard, B=3, N=4, q_len 2")
+    outs = H.run_decode(case)
+    _sync()
+    assert torch.isneginf(outs.partial_lse[1, 1]).all() and (outs.partial_out[1, 1] == 0).all()
+    _check_with_holes(case, outs, holes, heads=list(range(w.num_q_heads)))
+
+
+def test_decode_gqa_many_pairs_take_the_chunk_plan():
+    """More (shard, request) pairs than the even planner holds: the GQA kernel runs under the
+    chunk plan; sampled requests against the oracle."""
+    base = get_workload("gqa_bf16_16x4k-32k")
+    B = 1100  # x 4 shards = 4400 pairs > 4096
+    w = scaled(base, seed=base.seed + 280, seq_segments=((B, 20, 700),), pool_pages=4096, num_layers=1,
+               attn_layer=0)
+    case = H.make_decode_case(w, DEV)
+    H.log(f"decode gqa bf16, B={B} x N={w.dcp_size} pairs: chunk plan")
+    outs = H.run_decode(case)
+    _sync()
+    H.check_decode(case, outs, requests=[0, 1, 549, 1098, 1099], heads=list(range(8)))
 
 
 def test_decode_shard_subset_calls():
