@@ -497,6 +497,33 @@ def copy_ceiling_gbps(torch, K, dev, nbytes: int, reps: int = 5) -> float:
     return 2 * n / float(np.median(ts)) / 1e9
 
 
+def scatter_ceiling_gbps(torch, K, dev, page_bytes: int, nbytes: int, reps: int = 5, seed: int = 7) -> float:
+    """Read + write GB/s of the library's page-list copy (the same loop over a page list) moving
+    about `nbytes` (capped at 4 GiB) in pages of page_bytes between two buffers, source and
+    destination pages each in an independent seeded random order: the copy rate this memory
+    system gives a page scatter like the reshard's (random page maps on both sides)."""
+    pages = max(1, min(int(nbytes), 4 << 30) // page_bytes)
+    a = torch.empty(pages * page_bytes, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    rng = np.random.default_rng(seed)
+    sp = torch.from_numpy(rng.permutation(pages).astype(np.int32)).to(dev)
+    dp = torch.from_numpy(rng.permutation(pages).astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    K.dcpkv_probe_copy_pages(a, b, sp, dp, page_bytes)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        K.dcpkv_probe_copy_pages(a, b, sp, dp, page_bytes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    del a, b
+    return 2 * pages * page_bytes / float(np.median(ts)) / 1e9
+
+
 def mfma_probe_tflops(torch, K, dev, kind: int, iters: int = 4000, reps: int = 3) -> float:
     """Median TFLOP/s of the library's MFMA rate probe (kind 0: fp16 16x16x32, 1: fp8 16x16x128)."""
     sink = torch.empty(K.PROBE_SINK_FLOATS, dtype=torch.float32, device=dev)
@@ -639,11 +666,14 @@ def measure(w, dev, a, probes):
         name = "reshard_tokens_kernel" if st.own else "reshard_kernel"
         h = kernel_source_hash(CALL_SOURCES[name])
         ceil = copy_ceiling_gbps(torch, K, dev, b_rs // 2)
+        sceil = scatter_ceiling_gbps(torch, K, dev, w.page_bytes, b_rs // 2)
         calls[name] = {"us": round(t_rs.mean() * 1e6, 2), "algorithmic_bytes": int(b_rs), "source_hash": h,
                        "traffic": load_traffic(f"{w.name}:{name}{own}", h)}
         part.update({"reshard_GBps": round(rs_gbps, 1), "reshard_frac_hbm": round(rs_gbps / HBM_PEAK_GBPS, 4),
                      "reshard_us": round(t_rs.mean() * 1e6, 2), "copy_ceiling_GBps": round(ceil, 1),
-                     "reshard_frac_of_copy_ceiling": round(rs_gbps / ceil, 4)})
+                     "reshard_frac_of_copy_ceiling": round(rs_gbps / ceil, 4),
+                     "scatter_copy_ceiling_GBps": round(sceil, 1),
+                     "reshard_frac_of_scatter_ceiling": round(rs_gbps / sceil, 4)})
         if a.pack_cap_mib > 0 and not st.own and st.num_pages > st.first_uncached:
             # the same pages path by path through a fixed staging buffer: every page is read and
             # written twice (source -> staging -> pool)

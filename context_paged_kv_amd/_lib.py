@@ -39,7 +39,7 @@ if not HOST_ONLY:
 _lib = C.CDLL(LIB_PATH)
 
 # the include/dcpkv.h revision these signatures follow; a library of another revision is refused
-ABI_VERSION = 6
+ABI_VERSION = 7
 _lib.dcpkv_abi_version.restype = C.c_int
 if _lib.dcpkv_abi_version() != ABI_VERSION:
     raise ImportError(f"{LIB_PATH} has ABI version {_lib.dcpkv_abi_version()}, this binding needs {ABI_VERSION}: "
@@ -62,7 +62,7 @@ EXPORTED = (
     "dcp_pagemap_release", "dcp_build_block_tables", "kv_reshard_pages", "kv_check_unique_pages",
     "kv_path_entries", "kv_pack_pages", "kv_unpack_pages", "kv_reshard_tokens",
     "dcp_decode_partial_workspace", "dcp_decode_partial", "dcp_decode_partial_noalloc", "dcp_lse_merge",
-    "dcpkv_probe_mfma", "dcpkv_probe_copy",
+    "dcpkv_probe_mfma", "dcpkv_probe_copy", "dcpkv_probe_copy_pages",
 )
 NOALLOC_SCRATCH_BYTES = 64 << 20  # DCPKV_NOALLOC_SCRATCH_BYTES
 
@@ -128,6 +128,7 @@ _SIGS = {
     "dcp_lse_merge": ([C.c_int32, C.c_int64, C.c_int32, _P, _P, _P, _P, _P], C.c_int),
     "dcpkv_probe_mfma": ([C.c_int32, C.c_int32, _P, C.c_int64, _I64P, _P], C.c_int),
     "dcpkv_probe_copy": ([_P, _P, C.c_int64, _P], C.c_int),
+    "dcpkv_probe_copy_pages": ([_P, _P, _P, _P, C.c_int64, C.c_int64, C.c_int64, C.c_int64, _P], C.c_int),
 }
 HOST_SYMBOLS = ("dcpkv_last_error", "dcpkv_abi_version", "cp_layersplit_layer_range", "dcp_filter_kv_indices",
                 "dcp_pagemap_create", "dcp_pagemap_destroy", "dcp_pagemap_num_free", "dcp_pagemap_alloc",
@@ -412,3 +413,11 @@ def dcpkv_probe_copy(src, dst, nbytes: Optional[int] = None, stream=None) -> Non
     """Enqueue the streaming copy the reshard is read against (see include/dcpkv.h)."""
     n = src.numel() * src.element_size() if nbytes is None else nbytes
     _check(_lib.dcpkv_probe_copy(_dptr(src), _dptr(dst), n, _stream(stream)))
+
+
+def dcpkv_probe_copy_pages(src, dst, src_pages, dst_pages, page_bytes: int, stream=None) -> None:
+    """Enqueue the page-list copy (see include/dcpkv.h): page src_pages[i] of src to page
+    dst_pages[i] of dst; the capacities are the buffers' sizes in pages."""
+    sb, db = src.numel() * src.element_size(), dst.numel() * dst.element_size()
+    _check(_lib.dcpkv_probe_copy_pages(_dptr(src), _dptr(dst), _dptr(src_pages), _dptr(dst_pages), src_pages.numel(),
+                                       sb // page_bytes, db // page_bytes, page_bytes, _stream(stream)))

@@ -32,7 +32,7 @@ using namespace dcpkv;
 
 extern "C" const char* dcpkv_last_error(void) { return g_err; }
 
-extern "C" int dcpkv_abi_version(void) { return 6; }
+extern "C" int dcpkv_abi_version(void) { return 7; }
 
 // [2DR] section 4.1: start_r = r*floor(L/N) + min(r, L mod N), end_r = start_{r+1}.
 extern "C" int cp_layersplit_layer_range(int32_t num_layers, int32_t num_sources, int32_t r,

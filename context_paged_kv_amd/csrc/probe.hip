@@ -126,7 +126,77 @@ __global__ __launch_bounds__(kCopyThreads) void stream_copy_kernel(const u32x4p*
   }
 }
 
+// The same segment loop over a page list: page src_pages[i] of src to page dst_pages[i] of dst,
+// entries outside the buffers skipped.
+__global__ __launch_bounds__(kCopyThreads) void page_copy_kernel(const u32x4p* __restrict__ src,
+                                                                 u32x4p* __restrict__ dst,
+                                                                 const int32_t* __restrict__ src_pages,
+                                                                 const int32_t* __restrict__ dst_pages,
+                                                                 int64_t num_pages, int64_t src_cap, int64_t dst_cap,
+                                                                 int64_t page_chunks) {
+  constexpr int64_t seg = (int64_t)kCopyThreads * kCopyUnroll;
+  const int64_t per_page = (page_chunks + seg - 1) / seg;
+  const int64_t items = num_pages * per_page;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t pg = it / per_page, off = (it - pg * per_page) * seg;
+    const int64_t sp = src_pages[pg], dp = dst_pages[pg];
+    if (sp < 0 || sp >= src_cap || dp < 0 || dp >= dst_cap) continue;
+    const u32x4p* s = src + sp * page_chunks + off;
+    u32x4p* d = dst + dp * page_chunks + off;
+    const int64_t n = page_chunks - off < seg ? page_chunks - off : seg;
+    if (n == seg) {
+      u32x4p v[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) v[u] = __builtin_nontemporal_load(s + u * kCopyThreads + threadIdx.x);
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) __builtin_nontemporal_store(v[u], d + u * kCopyThreads + threadIdx.x);
+    } else {
+      for (int64_t c = threadIdx.x; c < n; c += kCopyThreads)
+        __builtin_nontemporal_store(__builtin_nontemporal_load(s + c), d + c);
+    }
+  }
+}
+
+static int probe_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || *cus <= 0)
+    return set_error(DCPKV_EDEVICE, "probe: no device");
+  return DCPKV_OK;
+}
+
 }  // namespace dcpkv
+
+extern "C" int dcpkv_probe_copy_pages(const void* src, void* dst, const int32_t* src_pages, const int32_t* dst_pages,
+                                      int64_t num_pages, int64_t src_capacity, int64_t dst_capacity,
+                                      int64_t page_bytes, void* stream) {
+  if (num_pages < 0 || page_bytes < 16 || page_bytes % 16 || src_capacity < 1 || dst_capacity < 1)
+    return set_error(DCPKV_EINVAL, "probe_copy_pages: bad sizes (%lld pages of %lld bytes)", (long long)num_pages,
+                     (long long)page_bytes);
+  if (num_pages == 0) return DCPKV_OK;
+  if (!src || !dst || !src_pages || !dst_pages || !aligned16(src) || !aligned16(dst) ||
+      (reinterpret_cast<uintptr_t>(src_pages) & 3u) || (reinterpret_cast<uintptr_t>(dst_pages) & 3u))
+    return set_error(DCPKV_EINVAL, "probe_copy_pages: NULL or misaligned pointer");
+  if (src_capacity > INT64_MAX / page_bytes || dst_capacity > INT64_MAX / page_bytes)
+    return set_error(DCPKV_EINVAL, "probe_copy_pages: buffers too large");
+  const char* s = static_cast<const char*>(src);
+  char* d = static_cast<char*>(dst);
+  if (s < d + dst_capacity * page_bytes && d < s + src_capacity * page_bytes)
+    return set_error(DCPKV_EINVAL, "probe_copy_pages: source and destination overlap");
+  int cus = 0;
+  int rc = probe_cus(&cus);
+  if (rc) return rc;
+  const int64_t seg = (int64_t)kCopyThreads * kCopyUnroll, chunks = page_bytes / 16;
+  const int64_t per_page = (chunks + seg - 1) / seg;
+  if (num_pages > INT64_MAX / per_page) return set_error(DCPKV_EINVAL, "probe_copy_pages: too many pages");
+  const int64_t grid = std::min<int64_t>(num_pages * per_page, (int64_t)cus * kCopyBlocksPerCU);
+  hipLaunchKernelGGL(page_copy_kernel, dim3((unsigned)grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4p*>(src), static_cast<u32x4p*>(dst), src_pages, dst_pages, num_pages,
+                     src_capacity, dst_capacity, chunks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(DCPKV_EDEVICE, "probe_copy_pages: launch failed: %s", hipGetErrorString(e));
+  return DCPKV_OK;
+}
 
 extern "C" int dcpkv_probe_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (!src || !dst || bytes < 16 || bytes % 16 || !aligned16(src) || !aligned16(dst))

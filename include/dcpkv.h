@@ -445,6 +445,17 @@ DCPKV_API int dcpkv_probe_mfma(int32_t kind, int32_t iters, float* sink, int64_t
  * `stream`.  EINVAL on bad arguments, EDEVICE if the launch fails. */
 DCPKV_API int dcpkv_probe_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
+/* The same copy loop over a page list, the ceiling of a scattered page copy:
+ * page src_pages[i] of src (src_capacity pages of page_bytes) to page
+ * dst_pages[i] of dst (dst_capacity pages), i < num_pages, 16 KB segments per
+ * workgroup step.  Entries outside [0, capacity) are skipped.  src, dst:
+ * device, 16-byte aligned, not overlapping; the page lists: device int32,
+ * caller-owned.  page_bytes a positive multiple of 16.  Time it with events on
+ * `stream`.  EINVAL on bad arguments, EDEVICE if the launch fails. */
+DCPKV_API int dcpkv_probe_copy_pages(const void* src, void* dst, const int32_t* src_pages, const int32_t* dst_pages,
+                                     int64_t num_pages, int64_t src_capacity, int64_t dst_capacity,
+                                     int64_t page_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTED)
     assert set(L.HOST_SYMBOLS) <= set(names)
-    assert K.dcpkv_abi_version() == 6 == L.ABI_VERSION
+    assert K.dcpkv_abi_version() == 7 == L.ABI_VERSION
 
 
 @device_symbols
@@ -306,3 +306,14 @@ def test_probe_rejects_bad_arguments_on_host():
     assert L._lib.dcpkv_probe_copy(C.c_void_p(264), C.c_void_p(1 << 20), 64, None) == E  # misaligned
     assert L._lib.dcpkv_probe_copy(v, C.c_void_p(512), 1024, None) == E            # overlapping
     assert L._lib.dcpkv_probe_copy(None, v, 64, None) == E
+    P = C.c_void_p
+    a, b, ids = P(1 << 20), P(1 << 30), P(4096)
+    cp = L._lib.dcpkv_probe_copy_pages
+    assert cp(a, b, ids, ids, 4, 8, 8, 100, None) == E                    # page not a multiple of 16
+    assert cp(a, b, ids, ids, -1, 8, 8, 4096, None) == E                  # negative count
+    assert cp(a, b, ids, ids, 4, 0, 8, 4096, None) == E                   # no source pages
+    assert cp(a, P((1 << 20) + 4096), ids, ids, 4, 8, 8, 4096, None) == E  # overlapping buffers
+    assert cp(P((1 << 20) + 8), b, ids, ids, 4, 8, 8, 4096, None) == E    # misaligned
+    assert cp(a, b, None, ids, 4, 8, 8, 4096, None) == E
+    assert cp(a, b, ids, P(4098), 4, 8, 8, 4096, None) == E               # misaligned list
+    assert cp(None, None, None, None, 0, 8, 8, 4096, None) == L.DCPKV_OK  # nothing to copy

@@ -959,6 +959,31 @@ def test_probe_mfma_counts_its_work(kind, per_mfma):
     assert 0 < rate < (2600 if kind == 0 else 5200)
 
 
+def test_probe_copy_pages_moves_listed_pages():
+    """The page-list copy (the scattered-copy ceiling) moves page src_pages[i] to page
+    dst_pages[i], skips entries outside either buffer, and touches nothing else."""
+    for page_bytes, n_src, n_dst in ((256 * 1024, 40, 48), (36864, 70, 64), (48, 9, 9)):
+        g = torch.Generator(device=DEV).manual_seed(page_bytes)
+        src = torch.randint(0, 256, (n_src * page_bytes,), dtype=torch.uint8, device=DEV, generator=g)
+        dst = torch.zeros(n_dst * page_bytes, dtype=torch.uint8, device=DEV)
+        rng = np.random.default_rng(page_bytes)
+        k = min(n_src, n_dst) - 2
+        sp = rng.permutation(n_src)[:k].astype(np.int32)
+        dp = rng.permutation(n_dst)[:k].astype(np.int32)
+        sp[1], dp[2] = -1, n_dst  # skipped entries
+        K.dcpkv_probe_copy_pages(src, dst, torch.from_numpy(sp).to(DEV), torch.from_numpy(dp).to(DEV), page_bytes)
+        _sync()
+        s2, d2 = src.view(n_src, page_bytes).cpu(), dst.view(n_dst, page_bytes).cpu()
+        written = set()
+        for i in range(k):
+            if 0 <= sp[i] < n_src and 0 <= dp[i] < n_dst:
+                assert torch.equal(d2[dp[i]], s2[sp[i]])
+                written.add(int(dp[i]))
+        for j in range(n_dst):
+            if j not in written:
+                assert (d2[j] == 0).all()
+
+
 def test_probe_copy_copies_every_byte():
     """The streaming copy the reshard is read against moves its bytes exactly (odd sizes leave a
     short last segment; bytes past the end stay untouched)."""
