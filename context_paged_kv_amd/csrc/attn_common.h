@@ -159,12 +159,45 @@ __device__ __forceinline__ float wave_sum(float v) {
 // ([2DR] section 5.2 for LSE; the O rule is the exact recombination of [SGL]).
 // Partial i's LSE is at lse[i * lse_stride], its output at o + i * o_stride.
 // Partials with LSE = -inf (no visible token) take no part, whatever their O holds.
-// Up to 64 partials, lane i holds L_i and its weight, and the O loads of four
-// partials are in flight together, so a row costs two memory round trips.
+// Up to eight partials of at most 256 dims (a multiple of four), every load is
+// issued before the first use: one memory round trip.  Up to 64 partials, lane
+// i holds L_i and its weight, and the O loads of four partials are in flight
+// together, so a row costs two memory round trips.
 __device__ inline void wave_merge_row(int count, const float* __restrict__ lse, int64_t lse_stride,
                                       const float* __restrict__ o, int64_t o_stride, int dv,
                                       float* __restrict__ out, float* __restrict__ out_lse) {
   const int lane = threadIdx.x & 63;
+  if (count <= 8 && (dv & 3) == 0 && dv <= 256 && (o_stride & 3) == 0) {
+    // up to eight partials of up to 256 dims: every load (clamped into range, so none is
+    // predicated) goes out before the first use, one memory round trip in all
+    const int c = min(lane * 4, dv - 4);
+    float4 x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = *reinterpret_cast<const float4*>(o + min(i, count - 1) * o_stride + c);
+    const float lraw = lse[min(lane, count - 1) * lse_stride];
+    const float l = lane < count ? lraw : kNegInf;
+    const float m = wave_max(l);
+    if (m == kNegInf) {
+      if (lane * 4 < dv) *reinterpret_cast<float4*>(out + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (lane == 0 && out_lse) *out_lse = kNegInf;
+      return;
+    }
+    const float tot = m + logf(wave_sum(l == kNegInf ? 0.f : expf(l - m)));
+    if (lane == 0 && out_lse) *out_lse = tot;
+    const float w = l == kNegInf ? 0.f : expf(l - tot);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float wi = __shfl(w, i, 64);
+      if (i >= count || wi == 0.f) continue;  // an empty partial's O may hold anything
+      acc.x += wi * x[i].x;
+      acc.y += wi * x[i].y;
+      acc.z += wi * x[i].z;
+      acc.w += wi * x[i].w;
+    }
+    if (lane * 4 < dv) *reinterpret_cast<float4*>(out + c) = acc;
+    return;
+  }
   if (count <= 64) {
     const float l = lane < count ? lse[lane * lse_stride] : kNegInf;
     const float m = wave_max(l);

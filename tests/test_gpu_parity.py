@@ -526,7 +526,8 @@ def test_decode_shard_subset_calls():
 # --------------------------------------------------------------------------- merge
 
 
-@pytest.mark.parametrize("n,rows,dv", [(1, 7, 64), (2, 33, 128), (8, 100, 512), (5, 9, 10)])
+@pytest.mark.parametrize("n,rows,dv", [(1, 7, 64), (2, 33, 128), (8, 100, 512), (5, 9, 10), (8, 17, 256),
+                                      (3, 5, 4), (9, 6, 128)])
 def test_lse_merge_vs_oracle(n, rows, dv):
     g = torch.Generator().manual_seed(n * 1000 + rows)
     po = torch.randn((n, rows, dv), generator=g)
