@@ -39,8 +39,9 @@ CALL_SOURCES = {"reshard_kernel": ["reshard.hip", "common.h"],
                                        "gqa_bf16.hip", "mla_fp8.hip"]}
 # kernels of each timed call, as rocprofv3 names them; the first one that appears counts launches
 CALL_KERNELS = {"reshard_kernel": ("reshard_kernel",), "reshard_tokens_kernel": ("reshard_tokens_kernel",),
-                "dcp_decode_partial": ("gqa_bf16_kernel", "mla_fp8_kernel", "partial_generic_kernel",
-                                       "plan_kernel", "chunk_reduce_kernel")}
+                "dcp_decode_partial": ("gqa_bf16_even_kernel", "gqa_bf16_kernel", "mla_fp8_kernel",
+                                       "partial_generic_kernel", "plan_kernel", "plan_even_kernel",
+                                       "chunk_reduce_kernel", "even_reduce_kernel")}
 
 
 def parse(argv=None):
