@@ -31,13 +31,15 @@ namespace dcpkv {
 
 constexpr int kPlanThreads = 64;  // one wavefront: shuffles instead of barriers
 
-// Inclusive prefix sum over the wavefront.
-// Size class of a chunk of `size` pages, 0 for the longest (size >= range), 63 for empty ones.
-__device__ __forceinline__ int size_key(int size, int range) {
-  const long long k = ((long long)(range - min(size, range)) * 64) / ((long long)range + 1);
-  return (int)k;
+// Size class of a chunk of `size` pages, 0 for the longest (size >= range), up to 63 for empty
+// ones: 64 (range - size) / (range + 1), with rs = 64 / (range + 1) computed once (an ordering
+// key only, so the float product needs no exact division; clamped into the 64 classes).
+__device__ __forceinline__ int size_key(int size, int range, float rs) {
+  const int k = (int)((float)(range - min(size, range)) * rs);
+  return min(max(k, 0), 63);
 }
 
+// Inclusive prefix sum over the wavefront.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -48,18 +50,42 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
+constexpr int kPlanLdsPairs = 4096;  // pairs whose plan entries the planner keeps in LDS
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
   const int lane = threadIdx.x;
   const int num_pairs = p.shard_count * p.batch;
-  auto pair_pages = [&](int i) {
-    const int d = p.shard_begin + i / p.batch, b = i % p.batch;
-    return local_pages_of(p.seq_lens[b], p.page_size, p.n, d, p.max_local, p.tok_il);
+  // One wavefront runs the plan, so its time is the latency of its dependent steps (integer
+  // divisions, cross-lane shuffles): every pair's local pages are computed once into LDS
+  // (eight request lengths in flight per lane), up to kPlanLdsPairs pairs.
+  __shared__ int32_t s_nl[kPlanLdsPairs];
+  __shared__ int32_t s_wsb[kPlanLdsPairs];  // each pair's first workspace slot, for the last pass
+  auto pages_of = [&](int i, int32_t len) {
+    const int d = p.shard_begin + i / p.batch;
+    return local_pages_of(len, p.page_size, p.n, d, p.max_local, p.tok_il);
   };
+  const bool staged = num_pairs <= kPlanLdsPairs;
+  if (staged) {
+    for (int i0 = 0; i0 < num_pairs; i0 += 8 * 64) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = p.seq_lens[min(i0 + 64 * u + lane, num_pairs - 1) % p.batch];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 64 * u + lane < num_pairs) s_nl[i0 + 64 * u + lane] = pages_of(i0 + 64 * u + lane, v[u]);
+    }
+    __syncthreads();
+  }
+  auto pair_pages = [&](int i) { return staged ? s_nl[i] : pages_of(i, p.seq_lens[i % p.batch]); };
   // Pairs of (nearly) equal length whose work items fill the device's workgroup slots in
   // whole rounds are already balanced: splitting them would only add the chunk round trip
   // and its reduction, so they keep one chunk each.  Equal: longest <= 17/16 of the
   // shortest non-empty pair; whole rounds: at most 1/32 of the slots of the last round idle.
+  // In the same pass, the chunk totals of the split at C = chunk_pages: one chunk per pair
+  // when the split would not fit the workspace or the launched grid.
   int ne = 0, lo = INT32_MAX, hi = 0;
+  long long need = 0, need_all = 0;
+  const int Cs = p.chunk_pages;
   for (int i = lane; i < num_pairs; i += 64) {
     const int nl = pair_pages(i);
     if (nl > 0) {
@@ -67,31 +93,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
       lo = min(lo, nl);
       hi = max(hi, nl);
     }
+    const int k = nl > Cs ? (nl + Cs - 1) / Cs : 1;
+    if (k >= 2) need += k;
+    need_all += k;
   }
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    ne += __shfl_xor(ne, off, 64);
-    lo = min(lo, __shfl_xor(lo, off, 64));
-    hi = max(hi, __shfl_xor(hi, off, 64));
+  for (int off = 32; off > 0; off >>= 1) {  // five independent reductions, their latencies overlapped
+    const int ne2 = __shfl_xor(ne, off, 64), lo2 = __shfl_xor(lo, off, 64), hi2 = __shfl_xor(hi, off, 64);
+    const long long nd2 = __shfl_xor(need, off, 64), na2 = __shfl_xor(need_all, off, 64);
+    ne += ne2;
+    lo = min(lo, lo2);
+    hi = max(hi, hi2);
+    need += nd2;
+    need_all += na2;
   }
   const long long items1 = (long long)ne * p.hb_count, slots = p.slots;
   const long long rounds1 = slots > 0 ? (items1 + slots - 1) / slots : 0;
   const bool whole = ne > 0 && (long long)hi * 16 <= (long long)lo * 17 && items1 >= slots && slots > 0 &&
                      (rounds1 * slots - items1) * 32 <= rounds1 * slots;
-  const int C = whole ? INT32_MAX : p.chunk_pages;
-  // chunk totals first: one chunk per pair when the split would not fit the workspace or
-  // the launched grid
-  long long need = 0, need_all = 0;
-  for (int i = lane; i < num_pairs; i += 64) {
-    const int nl = pair_pages(i);
-    const int k = nl > C ? (nl + C - 1) / C : 1;
-    if (k >= 2) need += k;
-    need_all += k;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    need += __shfl_xor(need, off, 64);
-    need_all += __shfl_xor(need_all, off, 64);
+  const int C = whole ? INT32_MAX : Cs;
+  if (whole) {
+    need = 0;
+    need_all = num_pairs;
   }
   const int fallback = (need > (long long)p.ws_cap || need_all > (long long)p.max_chunks) ? 1 : 0;
   // size classes of the longest-first order: chunk sizes run up to C pages (a pair's whole
@@ -100,6 +123,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
   s_cnt[lane] = 0;
   __syncthreads();
   const int range = (C == INT32_MAX || fallback) ? max(hi, 1) : C;
+  const float rs = 64.f / ((float)range + 1.f);
   // then exclusive prefix sums of the chunks and of the workspace slots, 64 pairs at a time
   int carry_k = 0, carry_w = 0;
   for (int base = 0; base < num_pairs; base += 64) {
@@ -118,10 +142,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
       pp.k = k;
       pp.n_local = nl;
       p.pairs[i] = pp;
+      if (staged) s_wsb[i] = pp.ws_begin;
       // a pair's chunks have at most two sizes: `extra` of base + 1 pages, then k - extra of base
       const int base_sz = nl / k, extra = nl - base_sz * k;
-      if (extra) atomicAdd(&s_cnt[size_key(base_sz + 1, range)], extra);
-      if (k > extra) atomicAdd(&s_cnt[size_key(base_sz, range)], k - extra);
+      if (extra) atomicAdd(&s_cnt[size_key(base_sz + 1, range, rs)], extra);
+      if (k > extra) atomicAdd(&s_cnt[size_key(base_sz, range, rs)], k - extra);
     }
     carry_k += __shfl(sk, 63, 64);
     carry_w += __shfl(sw, 63, 64);
@@ -136,10 +161,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(AttnParams p) {
   }
   __syncthreads();
   for (int i = lane; i < num_pairs; i += 64) {
-    const PairPlan pp = p.pairs[i];
+    PairPlan pp;
+    if (staged) {  // from LDS (the entry of a pair is written by the same lane above)
+      pp.n_local = s_nl[i];
+      pp.k = (!fallback && pp.n_local > C) ? (pp.n_local + C - 1) / C : 1;
+      pp.ws_begin = s_wsb[i];
+    } else {
+      pp = p.pairs[i];
+    }
     const int base_sz = pp.n_local / pp.k, extra = pp.n_local - base_sz * pp.k;
-    const int at_hi = extra ? atomicAdd(&s_cnt[size_key(base_sz + 1, range)], extra) : 0;
-    const int at_lo = pp.k > extra ? atomicAdd(&s_cnt[size_key(base_sz, range)], pp.k - extra) : 0;
+    const int at_hi = extra ? atomicAdd(&s_cnt[size_key(base_sz + 1, range, rs)], extra) : 0;
+    const int at_lo = pp.k > extra ? atomicAdd(&s_cnt[size_key(base_sz, range, rs)], pp.k - extra) : 0;
     for (int c = 0; c < pp.k; ++c) {
       int jb, je;
       chunk_range(pp, c, jb, je);
